@@ -1,0 +1,59 @@
+"""Algorithmic work and MI355X peaks: the denominators of every reported fraction.
+
+Bytes count what the method itself must move (each input read once, each
+output written once); flops count 2 per multiply-add.  Nothing here depends
+on how a kernel is tiled.
+"""
+from __future__ import annotations
+
+# MI355X published peaks (dense, no sparsity).
+HBM_BYTES_PER_S = 8.0e12
+MFMA_BF16_FLOPS = 2.5e15
+FP32_VECTOR_FLOPS = 157.3e12
+CUS = 256
+CLOCK_HZ = 2.4e9
+
+
+def dtype_bytes(dtype) -> int:
+    s = str(dtype)
+    return 2 if ("bfloat16" in s or s in ("bf16", "1")) else 4
+
+
+def forward_bytes(B, H, N, Dk, Dv, in_bytes, out_bytes=None, *, gated=False,
+                  state_in=False, state_out=True) -> int:
+    """Q, K, V read once, O written once, final (S, z) written once (fp32)."""
+    out_bytes = in_bytes if out_bytes is None else out_bytes
+    per_token = (2 * Dk + Dv) * in_bytes + Dv * out_bytes + (4 if gated else 0)
+    state = (Dk * Dv + Dk) * 4
+    return B * H * (N * per_token + state * (int(state_in) + int(state_out)))
+
+
+def decode_bytes(B, H, Dk, Dv, in_bytes, out_bytes=None, *, gated=False) -> int:
+    """The fp32 (S, z) read and written once, q/k/v read once, o written once."""
+    out_bytes = in_bytes if out_bytes is None else out_bytes
+    state = (Dk * Dv + Dk) * 4
+    return B * H * (2 * state + (2 * Dk + Dv) * in_bytes + Dv * out_bytes + (4 if gated else 0))
+
+
+def method_flops(B, H, N, Dk, Dv) -> int:
+    """Write S += phi(k) v^T and read phi(q)^T S per token: 2 Dk Dv each."""
+    return 4 * B * H * N * Dk * Dv
+
+
+def chunked_flops(B, H, N, Dk, Dv, C) -> int:
+    """What a chunk-C kernel issues with full C x C score tiles (utilization check only)."""
+    return B * H * N * (4 * Dk * Dv + 2 * C * Dk + 2 * C * Dv)
+
+
+def quadratic_form_flops(N, D) -> int:
+    """Score matrix then weighted sum, one contraction counted per form: 2 N^2 D."""
+    return 2 * N * N * D
+
+
+def recurrence_flops(N, D) -> int:
+    """N state updates of D x D, one contraction counted: 2 N D^2."""
+    return 2 * N * D * D
+
+
+def hbm_time_s(nbytes) -> float:
+    return nbytes / HBM_BYTES_PER_S

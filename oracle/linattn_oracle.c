@@ -1,0 +1,234 @@
+/*
+ * linattn_oracle.c -- plain fp64 CPU oracle for causal linear attention with
+ * the feature map phi(x) = elu(x) + 1.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the checker, not the product: only
+ * the test suite, the smoke check and the benchmark's CPU-baseline leg load
+ * it.  It shares no code, header or constant with the HIP library and must
+ * never be called from the product path.
+ *
+ * Every routine is the plain definition, one token at a time, in double
+ * precision, with no blocking or reordering:
+ *
+ *   phi(x)  = elu(x) + 1, elu(x) = x for x >= 0 and exp(x) - 1 for x < 0
+ *            ("Transformers are RNNs" review, feature-map table: elu row and
+ *             the +1 offset row; "Linear Attention: accumulating KV into a
+ *             fixed-size state", section "Why replace softmax").
+ *   S_t     = a_t * S_{t-1} + phi(k_t) v_t^T     (a_t = 1 when ungated)
+ *   z_t     = a_t * z_{t-1} + phi(k_t)
+ *   o_t     = phi(q_t)^T S_t / (phi(q_t)^T z_t + eps)
+ *            (fixed-size-state page, section "State update and read as
+ *             equations"; review page, causal-masking and RNN-form tables,
+ *             which start from S_0 = 0, z_0 = 0; the scalar decay a_t on the
+ *             whole summary follows "Linear Attention: what happens when you
+ *             change the product order", section "The summary runs out of
+ *             room", and the h_t = a h_{t-1} + x_t recurrence of the
+ *             state-space-models page, section 3).
+ *
+ * The read uses the state *after* token t was added, so token t's own key and
+ * value take part in o_t (inclusive diagonal).  eps is added after the dot
+ * product.  parity pinned: see tests/test_oracle.py.
+ *
+ * Layout (row-major, contiguous, one (batch, head) pair after another):
+ *   q [BH][N][Dk], k [BH][N][Dk], v [BH][N][Dv], alpha [BH][N],
+ *   o [BH][N][Dv], s [BH][Dk][Dv] (row = key component, column = value
+ *   component), z [BH][Dk].
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define PHI_ELU1 0
+#define PHI_IDENTITY 1
+
+static double phi(double x, int mode)
+{
+    if (mode == PHI_IDENTITY)
+        return x;
+    /* elu(x) + 1: x + 1 on x >= 0; on x < 0, (exp(x) - 1) + 1, which is
+     * exp(x) exactly (written so, to keep the small values of exp(x)). */
+    return (x >= 0.0) ? x + 1.0 : exp(x);
+}
+
+/* One recurrence over N tokens for one (batch, head) pair.  s and z hold the
+ * running state on entry and on exit. */
+static void recur_one(const double *q, const double *k, const double *v,
+                      const double *alpha, double *o, double *s, double *z,
+                      int64_t N, int Dk, int Dv, int mode, double eps,
+                      double *fq, double *fk, double *num)
+{
+    for (int64_t t = 0; t < N; ++t) {
+        const double *qt = q + t * Dk;
+        const double *kt = k + t * Dk;
+        const double *vt = v + t * Dv;
+        for (int i = 0; i < Dk; ++i) {
+            fq[i] = phi(qt[i], mode);
+            fk[i] = phi(kt[i], mode);
+        }
+        if (alpha) {
+            double a = alpha[t];
+            for (int i = 0; i < Dk; ++i) {
+                z[i] *= a;
+                for (int j = 0; j < Dv; ++j)
+                    s[(int64_t)i * Dv + j] *= a;
+            }
+        }
+        /* write: S += phi(k) v^T, z += phi(k) */
+        for (int i = 0; i < Dk; ++i) {
+            z[i] += fk[i];
+            for (int j = 0; j < Dv; ++j)
+                s[(int64_t)i * Dv + j] += fk[i] * vt[j];
+        }
+        /* read the updated state with phi(q) */
+        double den = 0.0;
+        for (int j = 0; j < Dv; ++j)
+            num[j] = 0.0;
+        for (int i = 0; i < Dk; ++i) {
+            den += fq[i] * z[i];
+            for (int j = 0; j < Dv; ++j)
+                num[j] += fq[i] * s[(int64_t)i * Dv + j];
+        }
+        if (o) {
+            double *ot = o + t * Dv;
+            for (int j = 0; j < Dv; ++j)
+                ot[j] = num[j] / (den + eps);
+        }
+    }
+}
+
+/* Causal forward, optionally gated (alpha == NULL means a_t = 1).
+ * s_init / z_init may be NULL (zero state).  o, s_final, z_final may be NULL
+ * when not wanted.  Returns 0, or -1 on a bad argument / allocation failure. */
+int oracle_forward(const double *q, const double *k, const double *v,
+                   const double *alpha, const double *s_init,
+                   const double *z_init, double *o, double *s_final,
+                   double *z_final, int64_t BH, int64_t N, int Dk, int Dv,
+                   int mode, double eps, int nthreads)
+{
+    if (!q || !k || !v || BH < 0 || N < 0 || Dk < 1 || Dv < 1)
+        return -1;
+    int err = 0;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads > 0 ? nthreads : 1)
+    for (int64_t bh = 0; bh < BH; ++bh) {
+        double *s = calloc((size_t)Dk * Dv, sizeof(double));
+        double *z = calloc((size_t)Dk, sizeof(double));
+        double *fq = malloc(sizeof(double) * Dk);
+        double *fk = malloc(sizeof(double) * Dk);
+        double *num = malloc(sizeof(double) * Dv);
+        if (!s || !z || !fq || !fk || !num) {
+#pragma omp atomic write
+            err = 1;
+        } else {
+            if (s_init)
+                memcpy(s, s_init + bh * Dk * Dv, sizeof(double) * Dk * Dv);
+            if (z_init)
+                memcpy(z, z_init + bh * Dk, sizeof(double) * Dk);
+            recur_one(q + bh * N * Dk, k + bh * N * Dk, v + bh * N * Dv,
+                      alpha ? alpha + bh * N : NULL, o ? o + bh * N * Dv : NULL,
+                      s, z, N, Dk, Dv, mode, eps, fq, fk, num);
+            if (s_final)
+                memcpy(s_final + bh * Dk * Dv, s, sizeof(double) * Dk * Dv);
+            if (z_final)
+                memcpy(z_final + bh * Dk, z, sizeof(double) * Dk);
+        }
+        free(s); free(z); free(fq); free(fk); free(num);
+    }
+    return err ? -1 : 0;
+}
+
+/* Non-causal: S = sum_t phi(k_t) v_t^T and z = sum_t phi(k_t) over the whole
+ * sequence, computed once and read by every query ("Transformers are RNNs"
+ * review, discussion of the non-causal case that reuses the summed key-value
+ * matrix for all queries).  Zero initial state. */
+int oracle_noncausal(const double *q, const double *k, const double *v,
+                     double *o, double *s_out, double *z_out, int64_t BH,
+                     int64_t N, int Dk, int Dv, int mode, double eps,
+                     int nthreads)
+{
+    if (!q || !k || !v || BH < 0 || N < 0 || Dk < 1 || Dv < 1)
+        return -1;
+    int err = 0;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads > 0 ? nthreads : 1)
+    for (int64_t bh = 0; bh < BH; ++bh) {
+        double *s = calloc((size_t)Dk * Dv, sizeof(double));
+        double *z = calloc((size_t)Dk, sizeof(double));
+        double *fq = malloc(sizeof(double) * Dk);
+        double *num = malloc(sizeof(double) * Dv);
+        if (!s || !z || !fq || !num) {
+#pragma omp atomic write
+            err = 1;
+        } else {
+            const double *kb = k + bh * N * Dk, *vb = v + bh * N * Dv;
+            const double *qb = q + bh * N * Dk;
+            for (int64_t t = 0; t < N; ++t) {
+                for (int i = 0; i < Dk; ++i) {
+                    double f = phi(kb[t * Dk + i], mode);
+                    z[i] += f;
+                    for (int j = 0; j < Dv; ++j)
+                        s[(int64_t)i * Dv + j] += f * vb[t * Dv + j];
+                }
+            }
+            if (o) {
+                for (int64_t t = 0; t < N; ++t) {
+                    double den = 0.0;
+                    for (int i = 0; i < Dk; ++i)
+                        fq[i] = phi(qb[t * Dk + i], mode);
+                    for (int j = 0; j < Dv; ++j)
+                        num[j] = 0.0;
+                    for (int i = 0; i < Dk; ++i) {
+                        den += fq[i] * z[i];
+                        for (int j = 0; j < Dv; ++j)
+                            num[j] += fq[i] * s[(int64_t)i * Dv + j];
+                    }
+                    for (int j = 0; j < Dv; ++j)
+                        o[bh * N * Dv + t * Dv + j] = num[j] / (den + eps);
+                }
+            }
+            if (s_out)
+                memcpy(s_out + bh * Dk * Dv, s, sizeof(double) * Dk * Dv);
+            if (z_out)
+                memcpy(z_out + bh * Dk, z, sizeof(double) * Dk);
+        }
+        free(s); free(z); free(fq); free(num);
+    }
+    return err ? -1 : 0;
+}
+
+/* One decode step per (batch, head): the loop body of the recurrence applied
+ * once to the carried (S, z), which are updated in place ("Transformers are
+ * RNNs" review: the RNN mode keeps only (S, z) and takes one token at a
+ * time).  q, k: [BH][Dk]; v: [BH][Dv]; alpha: [BH] or NULL; o: [BH][Dv]. */
+int oracle_decode_step(const double *q, const double *k, const double *v,
+                       const double *alpha, double *s, double *z, double *o,
+                       int64_t BH, int Dk, int Dv, int mode, double eps,
+                       int nthreads)
+{
+    if (!q || !k || !v || !s || !z || BH < 0 || Dk < 1 || Dv < 1)
+        return -1;
+    int err = 0;
+#pragma omp parallel for schedule(static) num_threads(nthreads > 0 ? nthreads : 1)
+    for (int64_t bh = 0; bh < BH; ++bh) {
+        double *fq = malloc(sizeof(double) * Dk);
+        double *fk = malloc(sizeof(double) * Dk);
+        double *num = malloc(sizeof(double) * Dv);
+        if (!fq || !fk || !num) {
+#pragma omp atomic write
+            err = 1;
+        } else {
+            recur_one(q + bh * Dk, k + bh * Dk, v + bh * Dv,
+                      alpha ? alpha + bh : NULL, o ? o + bh * Dv : NULL,
+                      s + bh * Dk * Dv, z + bh * Dk, 1, Dk, Dv, mode, eps,
+                      fq, fk, num);
+        }
+        free(fq); free(fk); free(num);
+    }
+    return err ? -1 : 0;
+}
+
+/* The feature map alone, elementwise, for the closed-form pins. */
+void oracle_phi(const double *x, double *y, int64_t n, int mode)
+{
+    for (int64_t i = 0; i < n; ++i)
+        y[i] = phi(x[i], mode);
+}

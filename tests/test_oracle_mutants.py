@@ -1,0 +1,46 @@
+"""Planted mistakes in the oracle must fail its pins.
+
+Each mutant is a one-line edit of a copy of ``oracle/linattn_oracle.c``
+(a dropped term, a wrong sign, a wrong operand or index, a transposed state),
+compiled to a temporary library; ``tests/test_oracle.py`` is then run against it
+in a subprocess and must fail.  The real oracle source is never modified.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "linattn_oracle.c")
+
+MUTANTS = {
+    "phi_drops_plus_one": ("return (x >= 0.0) ? x + 1.0 : exp(x);", "return (x >= 0.0) ? x : exp(x);"),
+    "phi_wrong_sign": ("return (x >= 0.0) ? x + 1.0 : exp(x);", "return (x >= 0.0) ? x + 1.0 : exp(-x);"),
+    "read_with_key": ("num[j] += fq[i] * s[(int64_t)i * Dv + j];", "num[j] += fk[i] * s[(int64_t)i * Dv + j];"),
+    "state_transposed": ("s[(int64_t)i * Dv + j] += fk[i] * vt[j];", "s[(int64_t)j * Dk + i] += fk[i] * vt[j];"),
+    "z_not_decayed": ("z[i] *= a;", ";"),
+    "z_adds_query": ("z[i] += fk[i];", "z[i] += fq[i];"),
+    "den_counts_tokens": ("den += fq[i] * z[i];", "den += z[i];"),
+    "eps_dropped": ("ot[j] = num[j] / (den + eps);", "ot[j] = num[j] / den;"),
+    "gate_index_shifted": ("double a = alpha[t];", "double a = alpha[t > 0 ? t - 1 : 0];"),
+    "value_scaled_by_query": ("s[(int64_t)i * Dv + j] += fk[i] * vt[j];", "s[(int64_t)i * Dv + j] += fq[i] * vt[j];"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"mutation site for {name} not found"
+    mutated = src.replace(old, new, 1)
+    csrc = tmp_path / "mutant.c"
+    csrc.write_text(mutated)
+    lib = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", "-O1", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-o", str(lib),
+                    str(csrc), "-lm"], check=True)
+    env = dict(os.environ, LINATTN_ORACLE_LIB=str(lib))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0, f"mutant {name} passed every pin:\n{r.stdout[-2000:]}"
