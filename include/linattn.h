@@ -1,0 +1,181 @@
+/*
+ * linattn.h -- C ABI of the MI355X (gfx950) causal linear-attention library.
+ *
+ * The method (feature map phi(x) = elu(x) + 1 applied to queries and keys
+ * separately, never to values):
+ *
+ *     S_t = a_t S_{t-1} + phi(k_t) v_t^T          (a_t = 1 when ungated)
+ *     z_t = a_t z_{t-1} + phi(k_t)
+ *     o_t = phi(q_t)^T S_t / (phi(q_t)^T z_t + eps)
+ *
+ * Sources: "Linear Attention: accumulating KV into a fixed-size state",
+ * sections "Why replace softmax" (the feature map) and "State update and read
+ * as equations" (the update of S and z and the normalized read); the review
+ * of "Transformers are RNNs", feature-map table (elu + 1), causal-masking and
+ * RNN-form tables (S_0 = 0, z_0 = 0, one token at a time) and the discussion
+ * of the non-causal case; "Linear Attention: what happens when you change the
+ * product order", section "The summary runs out of room" (a scalar decay of
+ * the whole summary at every step); the state-space-models page, section 2
+ * (the output written with j <= t, i.e. token t reads its own key and value).
+ * No page adds eps; it is added after the dot product, here and in every path.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers to tensors are DEVICE pointers (hipMalloc'd or torch CUDA
+ *   memory), contiguous, row-major, owned by the caller.  The library
+ *   allocates and frees nothing and keeps no state between calls.
+ * - Shapes follow the pages' [batch, heads, tokens, head_dim] layout:
+ *   q, k [B][H][N][Dk], v [B][H][N][Dv], o [B][H][N][Dv]; the state
+ *   S [B][H][Dk][Dv] (row = key component, column = value component) and
+ *   z [B][H][Dk] are always fp32.
+ * - dtype (LINATTN_F32 or LINATTN_BF16) is the element type of q, k, v and o.
+ *   Arithmetic: bf16 inputs use bf16 matrix-core products with fp32
+ *   accumulation and an fp32 state; fp32 inputs use fp32 arithmetic
+ *   throughout.
+ * - Dk and Dv must each be one of 16, 32, 64, 128.
+ * - phi selects the feature map: LINATTN_PHI_ELU1 (the method) or
+ *   LINATTN_PHI_IDENTITY (checks against the pages' post-feature-map worked
+ *   examples; the caller then owns the sign of the denominator).
+ * - Work is enqueued on hip_stream (a hipStream_t; NULL = the null stream).
+ *   Calls return without synchronizing; results are valid once the stream
+ *   has reached that point.  Calls on different streams are independent as
+ *   long as their buffers are.
+ * - Every argument is validated on the host before anything is launched, so
+ *   an error return means nothing ran.  NaN or Inf inputs propagate; they
+ *   are not checked.
+ *
+ * Status codes: LINATTN_OK (0) or a negative LINATTN_E* value below.
+ */
+#ifndef LINATTN_H
+#define LINATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LINATTN_ABI_VERSION 1
+
+enum linattn_dtype { LINATTN_F32 = 0, LINATTN_BF16 = 1 };
+enum linattn_phi { LINATTN_PHI_ELU1 = 0, LINATTN_PHI_IDENTITY = 1 };
+enum linattn_kind { LINATTN_KIND_FORWARD = 0, LINATTN_KIND_GATED = 1, LINATTN_KIND_NONCAUSAL = 2 };
+
+enum linattn_status {
+    LINATTN_OK = 0,
+    LINATTN_EINVAL = -1,     /* NULL required pointer, B/H/N < 1, eps < 0 or not finite, aliasing */
+    LINATTN_ESHAPE = -2,     /* Dk or Dv not in {16, 32, 64, 128}, or sizes overflow 64-bit indexing */
+    LINATTN_EDTYPE = -3,     /* dtype or phi not one of the enumerated values */
+    LINATTN_EWORKSPACE = -4, /* workspace NULL or smaller than linattn_workspace_size() */
+    LINATTN_ELAUNCH = -5     /* a HIP launch failed (the HIP error is not cleared) */
+};
+
+/*
+ * Causal forward ("Transformer mode"): the whole sequence of each (b, h) in
+ * parallel, with the result of the one-token-at-a-time recurrence above.
+ *
+ *   q, k, v   inputs, dtype `dtype`.
+ *   o         output [B][H][N][Dv], dtype `dtype` (bf16: round-to-nearest-even).
+ *             Must not overlap q, k or v.
+ *   s_init,   initial state [B][H][Dk][Dv] and [B][H][Dk] fp32, or both NULL
+ *   z_init    for S_0 = 0, z_0 = 0 (the pages' start).  Passing the final
+ *             state of an earlier call resumes that sequence exactly.
+ *   s_final,  if non-NULL, receive the state after token N-1 (fp32).  They may
+ *   z_final   alias s_init / z_init (in-place resume); pass both or neither.
+ *   eps       added to the denominator; >= 0 and finite.
+ *   workspace device scratch of at least
+ *             linattn_workspace_size(LINATTN_KIND_FORWARD, B, H, N, Dk, Dv, dtype)
+ *             bytes (may be NULL when that size is 0).  Contents on entry do
+ *             not matter; the call overwrites it.
+ */
+int linattn_forward(const void *q, const void *k, const void *v, void *o,
+                    const float *s_init, const float *z_init,
+                    float *s_final, float *z_final,
+                    int B, int H, int N, int Dk, int Dv, int dtype, int phi,
+                    float eps, void *workspace, size_t workspace_bytes,
+                    void *hip_stream);
+
+/*
+ * Gated causal forward: as linattn_forward with the scalar decay a_t
+ * multiplying the whole summary (S and z) before token t is added, so token t
+ * itself is undecayed and a_0 multiplies s_init / z_init.
+ *
+ *   alpha     [B][H][N] fp32 per-token decay.  Values in [0, 1] are supported
+ *             (0 clears the summary exactly); values above 1 make the state
+ *             grow and may overflow, as the state-space-models page warns
+ *             (section 3).
+ * Other arguments as linattn_forward; workspace kind LINATTN_KIND_GATED.
+ */
+int linattn_forward_gated(const void *q, const void *k, const void *v,
+                          const float *alpha, void *o,
+                          const float *s_init, const float *z_init,
+                          float *s_final, float *z_final,
+                          int B, int H, int N, int Dk, int Dv, int dtype,
+                          int phi, float eps, void *workspace,
+                          size_t workspace_bytes, void *hip_stream);
+
+/*
+ * Non-causal form: S = sum_t phi(k_t) v_t^T and z = sum_t phi(k_t) over the
+ * whole sequence, computed once and read by every query:
+ * o_t = phi(q_t)^T S / (phi(q_t)^T z + eps).
+ *
+ *   s_out, z_out  if non-NULL, receive the global S [B][H][Dk][Dv] and
+ *                 z [B][H][Dk] (fp32); pass both or neither.
+ * Workspace kind LINATTN_KIND_NONCAUSAL.  The reduction order over the
+ * sequence is fixed, so results are bitwise reproducible.
+ */
+int linattn_forward_noncausal(const void *q, const void *k, const void *v,
+                              void *o, float *s_out, float *z_out,
+                              int B, int H, int N, int Dk, int Dv, int dtype,
+                              int phi, float eps, void *workspace,
+                              size_t workspace_bytes, void *hip_stream);
+
+/*
+ * One decode step ("RNN mode"): for every (b, h), update the carried state
+ * in place with one new token and read it with that token's query:
+ *   S <- a S + phi(k) v^T,  z <- a z + phi(k),  o = phi(q)^T S / (phi(q)^T z + eps)
+ * (the read uses the updated state).
+ *
+ *   q, k      [B][H][Dk], dtype `dtype`;  v [B][H][Dv], dtype `dtype`.
+ *   s, z      [B][H][Dk][Dv] and [B][H][Dk] fp32, read and overwritten.
+ *   alpha     [B][H] fp32 decay for this step, or NULL for a = 1.
+ *   o         [B][H][Dv], dtype `dtype`.  Must not overlap s or z.
+ * No workspace.
+ */
+int linattn_decode_step(const void *q, const void *k, const void *v,
+                        float *s, float *z, const float *alpha, void *o,
+                        int B, int H, int Dk, int Dv, int dtype, int phi,
+                        float eps, void *hip_stream);
+
+/*
+ * Workspace bytes a call of the given kind needs for these sizes (0 when the
+ * call needs none).  Pure host arithmetic; returns 0 for invalid arguments.
+ */
+size_t linattn_workspace_size(int kind, int B, int H, int N, int Dk, int Dv, int dtype);
+
+/* Static string naming a status code. */
+const char *linattn_status_string(int status);
+
+/* LINATTN_ABI_VERSION of the built library. */
+int linattn_abi_version(void);
+
+/*
+ * Kernel-level timing for measurement tools.  While enabled, every kernel the
+ * library launches is bracketed by a pair of hipEvents recorded on the
+ * caller's stream; linattn_profile_read() waits for them and reports, per
+ * kernel name, the number of launches and the summed device time since the
+ * last enable.  Not thread-safe: enable, run on one host thread, read.
+ *
+ *   linattn_profile_enable(1) clears the record and starts; (0) stops.
+ *   linattn_profile_read(names, ms, counts, max) fills up to max entries
+ *   (names point to static strings) and returns how many kernels were seen,
+ *   or LINATTN_ELAUNCH if an event failed.
+ */
+int linattn_profile_enable(int on);
+int linattn_profile_read(const char **names, double *total_ms, int *launches, int max);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LINATTN_H */

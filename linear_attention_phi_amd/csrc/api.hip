@@ -1,0 +1,453 @@
+// api.hip -- the C ABI of include/linattn.h: argument checks, the segment
+// plan, kernel dispatch and the optional per-kernel timing.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/linattn.h"
+#include "fwd_bf16.hpp"
+#include "recur.hpp"
+#include "scan_decode.hpp"
+
+using namespace linattn;
+
+namespace {
+
+// ------------------------------------------------------------------ plan
+// The sequence of each (b, h) is cut into P segments of seg_len tokens (a
+// multiple of the 64-token chunk).  Segments run in parallel; the state each
+// segment starts from is the prefix of the states of the segments before it.
+// P is chosen so that P * B * H workgroups cover the 256 compute units.
+constexpr int kTargetGroupsMfma = 256;
+constexpr int kTargetWavesRecur = 2048;
+
+struct Plan {
+    bool mfma = false;
+    int P = 1;        // segments per (b, h)
+    int seg_len = 0;  // tokens per segment
+    int nvb = 1;      // 64-column value blocks (recurrence path)
+    size_t E = 0;     // floats of one state (Dk * Dv + Dk)
+    size_t ws_states = 0, ws_gam = 0, ws_total = 0, ws_bytes = 0;
+};
+
+bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+Plan make_plan(int kind, int B, int H, int N, int Dk, int Dv, int dtype) {
+    Plan p;
+    p.mfma = dtype == LINATTN_BF16 && Dk >= 32 && Dv >= 32;
+    p.nvb = (Dv + 63) / 64;
+    const long long BH = (long long)B * H;
+    const int nch = (N + kChunk - 1) / kChunk;
+    long long want = p.mfma ? (kTargetGroupsMfma + BH - 1) / BH : (kTargetWavesRecur + BH * p.nvb - 1) / (BH * p.nvb);
+    if (want < 1) want = 1;
+    if (want > nch) want = nch;
+    const int cps = (int)((nch + want - 1) / want);
+    p.P = (nch + cps - 1) / cps;
+    p.seg_len = cps * kChunk;
+    p.E = (size_t)Dk * Dv + Dk;
+    const bool need_states = kind == LINATTN_KIND_NONCAUSAL || p.P > 1;
+    if (need_states) p.ws_states = align256((size_t)BH * p.P * p.E * sizeof(float));
+    if (kind == LINATTN_KIND_GATED && p.P > 1) p.ws_gam = align256((size_t)BH * p.P * sizeof(float));
+    if (kind == LINATTN_KIND_NONCAUSAL) p.ws_total = align256((size_t)BH * p.E * sizeof(float));
+    p.ws_bytes = p.ws_states + p.ws_gam + p.ws_total;
+    return p;
+}
+
+// ------------------------------------------------------------------ timing
+struct ProfRec {
+    const char *name;
+    hipEvent_t a, b;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof;      // recorded launches since enable
+std::vector<hipEvent_t> g_events; // event pool, reused across enables
+size_t g_event_next = 0;
+
+hipEvent_t prof_event() {
+    if (g_event_next == g_events.size()) {
+        hipEvent_t e;
+        if (hipEventCreate(&e) != hipSuccess) return nullptr;
+        g_events.push_back(e);
+    }
+    return g_events[g_event_next++];
+}
+
+// Launch helper: records an event pair around the launch while profiling.
+template <typename F> int launch(const char *name, hipStream_t st, F &&fn) {
+    ProfRec rec{name, nullptr, nullptr};
+    if (g_prof_on) {
+        rec.a = prof_event();
+        rec.b = prof_event();
+        if (rec.a) hipEventRecord(rec.a, st);
+    }
+    fn();
+    const hipError_t err = hipGetLastError();
+    if (g_prof_on && rec.a && rec.b) {
+        hipEventRecord(rec.b, st);
+        g_prof.push_back(rec);
+    }
+    return err == hipSuccess ? LINATTN_OK : LINATTN_ELAUNCH;
+}
+
+#define LA_TRY(x)                                                                                                      \
+    do {                                                                                                               \
+        const int rc_ = (x);                                                                                           \
+        if (rc_ != LINATTN_OK) return rc_;                                                                             \
+    } while (0)
+
+// ------------------------------------------------------------------ checks
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+    if (!a || !b || !na || !nb) return false;
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+int check_common(int B, int H, int N, int Dk, int Dv, int dtype, int phi, float eps) {
+    if (B < 1 || H < 1 || N < 1) return LINATTN_EINVAL;
+    if (!(eps >= 0.f) || !std::isfinite(eps)) return LINATTN_EINVAL;
+    if (dtype != LINATTN_F32 && dtype != LINATTN_BF16) return LINATTN_EDTYPE;
+    if (phi != LINATTN_PHI_ELU1 && phi != LINATTN_PHI_IDENTITY) return LINATTN_EDTYPE;
+    if (!dim_ok(Dk) || !dim_ok(Dv)) return LINATTN_ESHAPE;
+    // every index is formed in 64-bit; keep the element counts well inside it
+    const long double elems = (long double)B * H * (long double)N * (Dk > Dv ? Dk : Dv);
+    if (elems > 9.0e15L) return LINATTN_ESHAPE;
+    if ((long long)B * H > 0x7fffffffLL / 64) return LINATTN_ESHAPE;
+    return LINATTN_OK;
+}
+
+// ------------------------------------------------------------------ dispatch
+template <int DK, int DV, bool GATED>
+int run_mfma_causal(const Plan &pl, const void *q, const void *k, const void *v, const float *alpha, void *o,
+                    const float *s_init, const float *z_init, float *s_final, float *z_final, int BH, int N,
+                    int phi, float eps, char *ws, hipStream_t st) {
+    const float *start = s_init, *start_z = z_init;
+    size_t sbh = (size_t)DK * DV, sseg = 0, zbh = DK;
+    if (pl.P > 1) {
+        float *states = reinterpret_cast<float *>(ws);
+        float *gam = GATED ? reinterpret_cast<float *>(ws + pl.ws_states) : nullptr;
+        const int P_run = pl.P - 1;
+        LA_TRY(launch("seg_state_bf16", st, [&] {
+            seg_state_bf16<DK, DV, GATED><<<dim3(P_run * BH), dim3(kThreads), 0, st>>>(
+                (const uint16_t *)k, (const uint16_t *)v, alpha, states, gam, N, pl.P, P_run, pl.seg_len, phi);
+        }));
+        LA_TRY(launch("seg_prefix", st, [&] {
+            seg_prefix<<<dim3((unsigned)((pl.E + 255) / 256), BH), dim3(256), 0, st>>>(states, gam, s_init, z_init,
+                                                                                       pl.P, DK, DV);
+        }));
+        start = states;
+        start_z = states + (size_t)DK * DV;
+        sbh = (size_t)pl.P * pl.E;
+        sseg = pl.E;
+        zbh = (size_t)pl.P * pl.E;
+    }
+    return launch(GATED ? "fwd_out_bf16_gated" : "fwd_out_bf16", st, [&] {
+        fwd_out_bf16<DK, DV, GATED><<<dim3(pl.P * BH), dim3(kThreads), 0, st>>>(
+            (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, alpha, (uint16_t *)o, start, sbh, sseg,
+            start_z, zbh, s_final, z_final, N, pl.P, pl.seg_len, phi, eps);
+    });
+}
+
+template <int DK, int DV>
+int run_mfma_noncausal(const Plan &pl, const void *q, const void *k, const void *v, void *o, float *s_out,
+                       float *z_out, int BH, int N, int phi, float eps, char *ws, hipStream_t st) {
+    float *states = reinterpret_cast<float *>(ws);
+    float *total = reinterpret_cast<float *>(ws + pl.ws_states + pl.ws_gam);
+    LA_TRY(launch("seg_state_bf16", st, [&] {
+        seg_state_bf16<DK, DV, false><<<dim3(pl.P * BH), dim3(kThreads), 0, st>>>(
+            (const uint16_t *)k, (const uint16_t *)v, nullptr, states, nullptr, N, pl.P, pl.P, pl.seg_len, phi);
+    }));
+    LA_TRY(launch("seg_total", st, [&] {
+        seg_total<<<dim3((unsigned)((pl.E + 255) / 256), BH), dim3(256), 0, st>>>(states, total, s_out, z_out, pl.P,
+                                                                                  DK, DV);
+    }));
+    const int nch = (N + kChunk - 1) / kChunk;
+    const long long want_blocks = (2048 + BH - 1) / BH;
+    int cpb = (int)((nch + want_blocks - 1) / want_blocks);
+    if (cpb < 1) cpb = 1;
+    const int blocks = (nch + cpb - 1) / cpb;
+    return launch("noncausal_apply_bf16", st, [&] {
+        noncausal_apply_bf16<DK, DV><<<dim3(blocks * BH), dim3(kThreads), 0, st>>>(
+            (const uint16_t *)q, (uint16_t *)o, total, N, blocks, cpb, phi, eps);
+    });
+}
+
+template <typename T, int DK, bool GATED>
+int run_recur_causal(const Plan &pl, const void *q, const void *k, const void *v, const float *alpha, void *o,
+                     const float *s_init, const float *z_init, float *s_final, float *z_final, int BH, int N, int Dv,
+                     int phi, float eps, char *ws, hipStream_t st) {
+    const float *start = s_init, *start_z = z_init;
+    size_t sbh = (size_t)DK * Dv, sseg = 0, zbh = DK;
+    const size_t E = pl.E;
+    if (pl.P > 1) {
+        float *states = reinterpret_cast<float *>(ws);
+        float *gam = GATED ? reinterpret_cast<float *>(ws + pl.ws_states) : nullptr;
+        const int P_run = pl.P - 1;
+        LA_TRY(launch("recur_state", st, [&] {
+            recur_kernel<T, DK, GATED, RECUR_STATE><<<dim3(P_run * BH * pl.nvb), dim3(64), 0, st>>>(
+                (const T *)q, (const T *)k, (const T *)v, alpha, nullptr, nullptr, 0, 0, nullptr, 0, states,
+                states + (size_t)DK * Dv, (size_t)pl.P * E, E, (size_t)pl.P * E, gam, N, pl.P, P_run, pl.seg_len, Dv,
+                phi, eps);
+        }));
+        LA_TRY(launch("seg_prefix", st, [&] {
+            seg_prefix<<<dim3((unsigned)((E + 255) / 256), BH), dim3(256), 0, st>>>(states, gam, s_init, z_init, pl.P,
+                                                                                    DK, Dv);
+        }));
+        start = states;
+        start_z = states + (size_t)DK * Dv;
+        sbh = (size_t)pl.P * E;
+        sseg = E;
+        zbh = (size_t)pl.P * E;
+    }
+    return launch(GATED ? "recur_causal_gated" : "recur_causal", st, [&] {
+        recur_kernel<T, DK, GATED, RECUR_CAUSAL><<<dim3(pl.P * BH * pl.nvb), dim3(64), 0, st>>>(
+            (const T *)q, (const T *)k, (const T *)v, alpha, (T *)o, start, sbh, sseg, start_z, zbh, s_final, z_final,
+            (size_t)DK * Dv, 0, (size_t)DK, nullptr, N, pl.P, pl.P, pl.seg_len, Dv, phi, eps);
+    });
+}
+
+template <typename T, int DK>
+int run_recur_noncausal(const Plan &pl, const void *q, const void *k, const void *v, void *o, float *s_out,
+                        float *z_out, int BH, int N, int Dv, int phi, float eps, char *ws, hipStream_t st) {
+    const size_t E = pl.E;
+    float *states = reinterpret_cast<float *>(ws);
+    float *total = reinterpret_cast<float *>(ws + pl.ws_states + pl.ws_gam);
+    LA_TRY(launch("recur_state", st, [&] {
+        recur_kernel<T, DK, false, RECUR_STATE><<<dim3(pl.P * BH * pl.nvb), dim3(64), 0, st>>>(
+            (const T *)q, (const T *)k, (const T *)v, nullptr, nullptr, nullptr, 0, 0, nullptr, 0, states,
+            states + (size_t)DK * Dv, (size_t)pl.P * E, E, (size_t)pl.P * E, nullptr, N, pl.P, pl.P, pl.seg_len, Dv,
+            phi, eps);
+    }));
+    LA_TRY(launch("seg_total", st, [&] {
+        seg_total<<<dim3((unsigned)((E + 255) / 256), BH), dim3(256), 0, st>>>(states, total, s_out, z_out, pl.P, DK,
+                                                                              Dv);
+    }));
+    return launch("recur_apply", st, [&] {
+        recur_kernel<T, DK, false, RECUR_APPLY><<<dim3(pl.P * BH * pl.nvb), dim3(64), 0, st>>>(
+            (const T *)q, (const T *)k, (const T *)v, nullptr, (T *)o, total, E, 0, total + (size_t)DK * Dv, E,
+            nullptr, nullptr, 0, 0, 0, nullptr, N, pl.P, pl.P, pl.seg_len, Dv, phi, eps);
+    });
+}
+
+// Dispatch over the compiled (Dk, Dv) set.
+template <template <int, int> class F, typename... A> int by_dims_mfma(int Dk, int Dv, A &&...a) {
+#define LA_CASE(X, Y)                                                                                                  \
+    if (Dk == X && Dv == Y) return F<X, Y>::run(a...);
+    LA_CASE(32, 32) LA_CASE(32, 64) LA_CASE(32, 128)
+    LA_CASE(64, 32) LA_CASE(64, 64) LA_CASE(64, 128)
+    LA_CASE(128, 32) LA_CASE(128, 64) LA_CASE(128, 128)
+#undef LA_CASE
+    return LINATTN_ESHAPE;
+}
+
+template <bool GATED> struct MfmaCausal {
+    template <int DK, int DV> struct F {
+        template <typename... A> static int run(A &&...a) { return run_mfma_causal<DK, DV, GATED>(a...); }
+    };
+};
+template <int DK, int DV> struct MfmaNoncausal {
+    template <typename... A> static int run(A &&...a) { return run_mfma_noncausal<DK, DV>(a...); }
+};
+
+template <typename T, bool GATED, typename... A> int recur_causal_dk(int Dk, A &&...a) {
+    switch (Dk) {
+    case 16: return run_recur_causal<T, 16, GATED>(a...);
+    case 32: return run_recur_causal<T, 32, GATED>(a...);
+    case 64: return run_recur_causal<T, 64, GATED>(a...);
+    case 128: return run_recur_causal<T, 128, GATED>(a...);
+    }
+    return LINATTN_ESHAPE;
+}
+template <typename T, typename... A> int recur_noncausal_dk(int Dk, A &&...a) {
+    switch (Dk) {
+    case 16: return run_recur_noncausal<T, 16>(a...);
+    case 32: return run_recur_noncausal<T, 32>(a...);
+    case 64: return run_recur_noncausal<T, 64>(a...);
+    case 128: return run_recur_noncausal<T, 128>(a...);
+    }
+    return LINATTN_ESHAPE;
+}
+
+int forward_impl(bool gated, const void *q, const void *k, const void *v, const float *alpha, void *o,
+                 const float *s_init, const float *z_init, float *s_final, float *z_final, int B, int H, int N,
+                 int Dk, int Dv, int dtype, int phi, float eps, void *workspace, size_t workspace_bytes,
+                 void *hip_stream) {
+    LA_TRY(check_common(B, H, N, Dk, Dv, dtype, phi, eps));
+    if (!q || !k || !v || !o || (gated && !alpha)) return LINATTN_EINVAL;
+    if ((s_init == nullptr) != (z_init == nullptr)) return LINATTN_EINVAL;
+    if ((s_final == nullptr) != (z_final == nullptr)) return LINATTN_EINVAL;
+    const size_t es = dtype == LINATTN_BF16 ? 2 : 4;
+    const size_t nq = (size_t)B * H * N * Dk * es, nv = (size_t)B * H * N * Dv * es;
+    if (overlaps(o, nv, q, nq) || overlaps(o, nv, k, nq) || overlaps(o, nv, v, nv)) return LINATTN_EINVAL;
+    const Plan pl = make_plan(gated ? LINATTN_KIND_GATED : LINATTN_KIND_FORWARD, B, H, N, Dk, Dv, dtype);
+    if (pl.ws_bytes && (!workspace || workspace_bytes < pl.ws_bytes)) return LINATTN_EWORKSPACE;
+    hipStream_t st = (hipStream_t)hip_stream;
+    char *ws = (char *)workspace;
+    const int BH = B * H;
+    if (pl.mfma) {
+        if (gated)
+            return by_dims_mfma<MfmaCausal<true>::F>(Dk, Dv, pl, q, k, v, alpha, o, s_init, z_init, s_final, z_final,
+                                                    BH, N, phi, eps, ws, st);
+        return by_dims_mfma<MfmaCausal<false>::F>(Dk, Dv, pl, q, k, v, alpha, o, s_init, z_init, s_final, z_final, BH,
+                                                 N, phi, eps, ws, st);
+    }
+    if (dtype == LINATTN_BF16) {
+        if (gated)
+            return recur_causal_dk<uint16_t, true>(Dk, pl, q, k, v, alpha, o, s_init, z_init, s_final, z_final, BH, N,
+                                                   Dv, phi, eps, ws, st);
+        return recur_causal_dk<uint16_t, false>(Dk, pl, q, k, v, alpha, o, s_init, z_init, s_final, z_final, BH, N,
+                                                Dv, phi, eps, ws, st);
+    }
+    if (gated)
+        return recur_causal_dk<float, true>(Dk, pl, q, k, v, alpha, o, s_init, z_init, s_final, z_final, BH, N, Dv,
+                                            phi, eps, ws, st);
+    return recur_causal_dk<float, false>(Dk, pl, q, k, v, alpha, o, s_init, z_init, s_final, z_final, BH, N, Dv, phi,
+                                         eps, ws, st);
+}
+
+template <typename T, int DK, int DV>
+void launch_decode(const void *q, const void *k, const void *v, float *s, float *z, const float *alpha, void *o,
+                   int BH, int phi, float eps, hipStream_t st) {
+    decode_step_kernel<T, DK, DV><<<dim3(BH), dim3(256), 0, st>>>((const T *)q, (const T *)k, (const T *)v, s, z,
+                                                                    alpha, (T *)o, phi, eps);
+}
+
+template <typename T>
+bool decode_dims(int Dk, int Dv, const void *q, const void *k, const void *v, float *s, float *z, const float *alpha,
+                 void *o, int BH, int phi, float eps, hipStream_t st) {
+#define LA_D(X, Y)                                                                                                     \
+    if (Dk == X && Dv == Y) {                                                                                          \
+        launch_decode<T, X, Y>(q, k, v, s, z, alpha, o, BH, phi, eps, st);                                             \
+        return true;                                                                                                   \
+    }
+    LA_D(16, 16) LA_D(16, 32) LA_D(16, 64) LA_D(16, 128)
+    LA_D(32, 16) LA_D(32, 32) LA_D(32, 64) LA_D(32, 128)
+    LA_D(64, 16) LA_D(64, 32) LA_D(64, 64) LA_D(64, 128)
+    LA_D(128, 16) LA_D(128, 32) LA_D(128, 64) LA_D(128, 128)
+#undef LA_D
+    return false;
+}
+
+} // namespace
+
+// ====================================================================== C ABI
+extern "C" {
+
+int linattn_forward(const void *q, const void *k, const void *v, void *o, const float *s_init, const float *z_init,
+                    float *s_final, float *z_final, int B, int H, int N, int Dk, int Dv, int dtype, int phi,
+                    float eps, void *workspace, size_t workspace_bytes, void *hip_stream) {
+    return forward_impl(false, q, k, v, nullptr, o, s_init, z_init, s_final, z_final, B, H, N, Dk, Dv, dtype, phi,
+                        eps, workspace, workspace_bytes, hip_stream);
+}
+
+int linattn_forward_gated(const void *q, const void *k, const void *v, const float *alpha, void *o,
+                          const float *s_init, const float *z_init, float *s_final, float *z_final, int B, int H,
+                          int N, int Dk, int Dv, int dtype, int phi, float eps, void *workspace,
+                          size_t workspace_bytes, void *hip_stream) {
+    return forward_impl(true, q, k, v, alpha, o, s_init, z_init, s_final, z_final, B, H, N, Dk, Dv, dtype, phi, eps,
+                        workspace, workspace_bytes, hip_stream);
+}
+
+int linattn_forward_noncausal(const void *q, const void *k, const void *v, void *o, float *s_out, float *z_out,
+                              int B, int H, int N, int Dk, int Dv, int dtype, int phi, float eps, void *workspace,
+                              size_t workspace_bytes, void *hip_stream) {
+    LA_TRY(check_common(B, H, N, Dk, Dv, dtype, phi, eps));
+    if (!q || !k || !v || !o) return LINATTN_EINVAL;
+    if ((s_out == nullptr) != (z_out == nullptr)) return LINATTN_EINVAL;
+    const size_t es = dtype == LINATTN_BF16 ? 2 : 4;
+    const size_t nq = (size_t)B * H * N * Dk * es, nv = (size_t)B * H * N * Dv * es;
+    if (overlaps(o, nv, q, nq) || overlaps(o, nv, k, nq) || overlaps(o, nv, v, nv)) return LINATTN_EINVAL;
+    const Plan pl = make_plan(LINATTN_KIND_NONCAUSAL, B, H, N, Dk, Dv, dtype);
+    if (!workspace || workspace_bytes < pl.ws_bytes) return LINATTN_EWORKSPACE;
+    hipStream_t st = (hipStream_t)hip_stream;
+    char *ws = (char *)workspace;
+    const int BH = B * H;
+    if (pl.mfma) return by_dims_mfma<MfmaNoncausal>(Dk, Dv, pl, q, k, v, o, s_out, z_out, BH, N, phi, eps, ws, st);
+    if (dtype == LINATTN_BF16)
+        return recur_noncausal_dk<uint16_t>(Dk, pl, q, k, v, o, s_out, z_out, BH, N, Dv, phi, eps, ws, st);
+    return recur_noncausal_dk<float>(Dk, pl, q, k, v, o, s_out, z_out, BH, N, Dv, phi, eps, ws, st);
+}
+
+int linattn_decode_step(const void *q, const void *k, const void *v, float *s, float *z, const float *alpha,
+                        void *o, int B, int H, int Dk, int Dv, int dtype, int phi, float eps, void *hip_stream) {
+    LA_TRY(check_common(B, H, 1, Dk, Dv, dtype, phi, eps));
+    if (!q || !k || !v || !s || !z || !o) return LINATTN_EINVAL;
+    const size_t BH = (size_t)B * H;
+    const size_t es = dtype == LINATTN_BF16 ? 2 : 4;
+    if (overlaps(o, BH * Dv * es, s, BH * Dk * Dv * 4) || overlaps(o, BH * Dv * es, z, BH * Dk * 4) ||
+        overlaps(s, BH * Dk * Dv * 4, z, BH * Dk * 4))
+        return LINATTN_EINVAL;
+    hipStream_t st = (hipStream_t)hip_stream;
+    return launch("decode_step", st, [&] {
+        if (dtype == LINATTN_BF16)
+            decode_dims<uint16_t>(Dk, Dv, q, k, v, s, z, alpha, o, (int)BH, phi, eps, st);
+        else
+            decode_dims<float>(Dk, Dv, q, k, v, s, z, alpha, o, (int)BH, phi, eps, st);
+    });
+}
+
+size_t linattn_workspace_size(int kind, int B, int H, int N, int Dk, int Dv, int dtype) {
+    if (kind < LINATTN_KIND_FORWARD || kind > LINATTN_KIND_NONCAUSAL) return 0;
+    if (check_common(B, H, N, Dk, Dv, dtype, LINATTN_PHI_ELU1, 0.f) != LINATTN_OK) return 0;
+    return make_plan(kind, B, H, N, Dk, Dv, dtype).ws_bytes;
+}
+
+const char *linattn_status_string(int status) {
+    switch (status) {
+    case LINATTN_OK: return "ok";
+    case LINATTN_EINVAL: return "invalid argument";
+    case LINATTN_ESHAPE: return "unsupported shape";
+    case LINATTN_EDTYPE: return "unsupported dtype or feature map";
+    case LINATTN_EWORKSPACE: return "workspace too small";
+    case LINATTN_ELAUNCH: return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+int linattn_abi_version(void) { return LINATTN_ABI_VERSION; }
+
+int linattn_profile_enable(int on) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (on) {
+        g_prof.clear();
+        g_event_next = 0;
+    }
+    g_prof_on = on != 0;
+    return LINATTN_OK;
+}
+
+int linattn_profile_read(const char **names, double *total_ms, int *launches, int max) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    std::vector<const char *> nm;
+    std::vector<double> ms;
+    std::vector<int> cnt;
+    for (const ProfRec &r : g_prof) {
+        if (hipEventSynchronize(r.b) != hipSuccess) return LINATTN_ELAUNCH;
+        float t = 0.f;
+        if (hipEventElapsedTime(&t, r.a, r.b) != hipSuccess) return LINATTN_ELAUNCH;
+        size_t i = 0;
+        while (i < nm.size() && std::strcmp(nm[i], r.name) != 0) ++i;
+        if (i == nm.size()) {
+            nm.push_back(r.name);
+            ms.push_back(0.0);
+            cnt.push_back(0);
+        }
+        ms[i] += t;
+        cnt[i] += 1;
+    }
+    for (size_t i = 0; i < nm.size() && (int)i < max; ++i) {
+        if (names) names[i] = nm[i];
+        if (total_ms) total_ms[i] = ms[i];
+        if (launches) launches[i] = cnt[i];
+    }
+    return (int)nm.size();
+}
+
+} // extern "C"

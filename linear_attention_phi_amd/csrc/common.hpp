@@ -1,0 +1,97 @@
+// common.hpp -- device helpers shared by the linear-attention kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace linattn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kChunk = 64;    // tokens per chunk (one MFMA-tiled step of the chunked form)
+constexpr int kThreads = 256; // four 64-wide waves per workgroup
+
+// ---------------------------------------------------------------- feature map
+// phi(x) = elu(x) + 1: x + 1 for x >= 0 and exp(x) for x < 0 (elu's exp(x) - 1,
+// plus one).  Mode 1 is the identity map used for the post-feature-map worked
+// examples.
+__device__ __forceinline__ float phi_fast(float x, int mode) {
+    if (mode) return x;
+    // exp(x) = 2^(x log2 e) on the hardware exp2; relative error ~1e-7 for the
+    // |x| seen here, far below the bf16 rounding that follows.
+    return x >= 0.f ? x + 1.f : __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+}
+__device__ __forceinline__ float phi_exact(float x, int mode) {
+    if (mode) return x;
+    return x >= 0.f ? x + 1.f : expf(x);
+}
+
+// ---------------------------------------------------------------- bf16 helpers
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round-to-nearest-even float -> bf16, returned as raw bits.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    __bf16 b = static_cast<__bf16>(f);
+    return (uint32_t)__builtin_bit_cast(unsigned short, b);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// ---------------------------------------------------------------- MFMA
+// 16x16x32 bf16 -> fp32.  Lane l supplies A[l%16][8(l/16)+i], B[8(l/16)+i][l%16]
+// (i = 0..7) and receives D[4(l/16)+i][l%16] (i = 0..3).
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+__device__ __forceinline__ uint4 as_u4(bf16x8 v) { return __builtin_bit_cast(uint4, v); }
+
+// ---------------------------------------------------------------- cross-lane
+__device__ __forceinline__ float xor_shfl(float v, int mask) {
+    return __shfl_xor(v, mask, 64);
+}
+// Sum over the four 16-lane groups (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float sum_over_groups(float v) {
+    v += xor_shfl(v, 16);
+    v += xor_shfl(v, 32);
+    return v;
+}
+
+// ---------------------------------------------------------------- gating
+// In-chunk decay bookkeeping.  Within a chunk the decay between key j and
+// query t (j <= t) is prod_{m=j+1..t} a_m.  It is carried as a pair (count of
+// exactly-zero gates, sum of log of the nonzero gates) over the inclusive
+// prefix (log base 2), so that a zero gate clears exactly and no -inf - -inf
+// arises:
+//   decay(j -> t) = 0                       if zeros(t) > zeros(j)
+//                 = 2^(lsum(t) - lsum(j))   otherwise.
+// A gate below the smallest normal float counts as zero.
+__device__ __forceinline__ float decay_between(float to_lsum, int to_zeros, float from_lsum, int from_zeros) {
+    return to_zeros > from_zeros ? 0.f : __builtin_amdgcn_exp2f(to_lsum - from_lsum);
+}
+__device__ __forceinline__ bool gate_is_zero(float a) { return a < 1.17549435e-38f; }  // NaN stays NaN
+__device__ __forceinline__ float gate_log2(float a) { return gate_is_zero(a) ? 0.f : __builtin_amdgcn_logf(a); }
+
+// Inclusive scan over the 64 lanes of a wave (lane order = token order).
+__device__ __forceinline__ void wave_inclusive_scan(float &lsum, int &zeros) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        float ls = __shfl_up(lsum, d, 64);
+        int zs = __shfl_up(zeros, d, 64);
+        if (lane >= d) {
+            lsum += ls;
+            zeros += zs;
+        }
+    }
+}
+
+} // namespace linattn

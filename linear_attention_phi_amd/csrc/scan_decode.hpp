@@ -1,0 +1,146 @@
+// scan_decode.hpp -- segment-state prefix, non-causal total, and the
+// one-token decode step.
+#pragma once
+
+#include "common.hpp"
+
+namespace linattn {
+
+// Exclusive prefix over the segments of each (b, h), in place:
+//   ws[p] <- S_{<p} = a-decayed sum of the states of segments 0..p-1, seeded
+//   with the caller's initial state (or zero).
+// Summing the per-segment contributions is the associativity of the sum of
+// outer products ("Linear Attention: accumulating KV into a fixed-size state",
+// section "Adding to the same state in turn"); with gates, S_{<p+1} =
+// G_p S_{<p} + dS_p where G_p is the product of segment p's gates.
+// The order over segments is fixed, so the result is bitwise reproducible.
+// Grid: x = element blocks of 256, y = bh.
+__global__ __launch_bounds__(256) void seg_prefix(float *__restrict__ ws, const float *__restrict__ gam,
+                                                  const float *__restrict__ s_init, const float *__restrict__ z_init,
+                                                  int P, int DK, int DV) {
+    const int E = DK * DV + DK;
+    const int e = blockIdx.x * 256 + threadIdx.x;
+    const int bh = blockIdx.y;
+    if (e >= E) return;
+    float run = 0.f;
+    if (s_init) run = e < DK * DV ? s_init[(size_t)bh * DK * DV + e] : z_init[(size_t)bh * DK + (e - DK * DV)];
+    float *cell = ws + (size_t)bh * P * E + e;
+    for (int p = 0; p < P; ++p) {
+        const float d = cell[(size_t)p * E];
+        cell[(size_t)p * E] = run;
+        if (p + 1 < P) run = gam ? fmaf(gam[(size_t)bh * P + p], run, d) : run + d;
+    }
+}
+
+// Non-causal total: S = sum over all segments (fixed order), written to
+// total[bh] and, when requested, to the caller's s_out / z_out.
+__global__ __launch_bounds__(256) void seg_total(const float *__restrict__ ws, float *__restrict__ total,
+                                                 float *__restrict__ s_out, float *__restrict__ z_out, int P, int DK,
+                                                 int DV) {
+    const int E = DK * DV + DK;
+    const int e = blockIdx.x * 256 + threadIdx.x;
+    const int bh = blockIdx.y;
+    if (e >= E) return;
+    const float *cell = ws + (size_t)bh * P * E + e;
+    float run = 0.f;
+    for (int p = 0; p < P; ++p) run += cell[(size_t)p * E];
+    total[(size_t)bh * E + e] = run;
+    if (s_out) {
+        if (e < DK * DV)
+            s_out[(size_t)bh * DK * DV + e] = run;
+        else
+            z_out[(size_t)bh * DK + (e - DK * DV)] = run;
+    }
+}
+
+template <typename T> __device__ __forceinline__ float load_elem(const T *p, size_t i);
+template <> __device__ __forceinline__ float load_elem<float>(const float *p, size_t i) { return p[i]; }
+template <> __device__ __forceinline__ float load_elem<uint16_t>(const uint16_t *p, size_t i) {
+    return bf16_bits_to_f32(p[i]);
+}
+template <typename T> __device__ __forceinline__ void store_elem(T *p, size_t i, float v);
+template <> __device__ __forceinline__ void store_elem<float>(float *p, size_t i, float v) { p[i] = v; }
+template <> __device__ __forceinline__ void store_elem<uint16_t>(uint16_t *p, size_t i, float v) {
+    p[i] = (uint16_t)f32_to_bf16_bits(v);
+}
+
+// One decode step per (b, h), in place, streaming the fp32 state once:
+//   S <- a S + phi(k) v^T,  z <- a z + phi(k),  o = phi(q)^T S / (phi(q)^T z + eps)
+// (the read uses the updated state: "Linear Attention: accumulating KV into a
+// fixed-size state", section "State update and read as equations"; the
+// one-token-at-a-time RNN mode of the "Transformers are RNNs" review).
+// One workgroup of 256 threads per (b, h).  Thread -> (row group, float4
+// column): the DV/4 float4 columns of a row are covered by consecutive
+// threads, so every pass of the workgroup reads and writes whole rows
+// (coalesced), and all passes are issued before any is consumed.
+template <typename T, int DK, int DV>
+__global__ __launch_bounds__(256) void decode_step_kernel(const T *__restrict__ q, const T *__restrict__ k,
+                                                          const T *__restrict__ v, float *__restrict__ s,
+                                                          float *__restrict__ z, const float *__restrict__ alpha,
+                                                          T *__restrict__ o, int phi_mode, float eps) {
+    constexpr int C4 = DV / 4;                 // float4 columns per row
+    constexpr int RPP = 256 / C4;              // rows one pass of the workgroup covers
+    constexpr int ROWS = DK < RPP ? DK : RPP;  // rows per pass actually used
+    constexpr int PASSES = DK / ROWS;
+    constexpr int ACTIVE = ROWS * C4;          // threads holding state
+    __shared__ float sq[DK], sk[DK], sv[DV];
+    __shared__ __attribute__((aligned(16))) float red[ROWS][DV];
+    __shared__ float sden[4];
+
+    const int bh = blockIdx.x;
+    const int tid = threadIdx.x;
+    const float a = alpha ? alpha[bh] : 1.f;
+    f32x4 *sb = reinterpret_cast<f32x4 *>(s + (size_t)bh * DK * DV);
+    const int c4 = tid % C4, r0 = tid / C4;
+    const bool act = tid < ACTIVE;
+    f32x4 st[PASSES];
+    if (act) {
+#pragma unroll
+        for (int p = 0; p < PASSES; ++p) st[p] = __builtin_nontemporal_load(sb + (size_t)(r0 + p * ROWS) * C4 + c4);
+    }
+    if (tid < DK) {
+        sq[tid] = phi_exact(load_elem<T>(q, (size_t)bh * DK + tid), phi_mode);
+        sk[tid] = phi_exact(load_elem<T>(k, (size_t)bh * DK + tid), phi_mode);
+    }
+    if (tid < DV) sv[tid] = load_elem<T>(v, (size_t)bh * DV + tid);
+    __syncthreads();
+
+    // z <- a z + phi(k) and the denominator phi(q).z (threads 0..DK-1)
+    float dpart = 0.f;
+    if (tid < DK) {
+        const float zn = fmaf(a, z[(size_t)bh * DK + tid], sk[tid]);
+        z[(size_t)bh * DK + tid] = zn;
+        dpart = sq[tid] * zn;
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) dpart += __shfl_xor(dpart, m, 64);
+    if ((tid & 63) == 0) sden[tid >> 6] = dpart;
+
+    if (act) {
+        f32x4 num = {0.f, 0.f, 0.f, 0.f};
+        const f32x4 vv = {sv[4 * c4], sv[4 * c4 + 1], sv[4 * c4 + 2], sv[4 * c4 + 3]};
+#pragma unroll
+        for (int p = 0; p < PASSES; ++p) {
+            const int row = r0 + p * ROWS;
+            const float fk = sk[row], fq = sq[row];
+            f32x4 x = st[p];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                x[e] = fmaf(a, x[e], fk * vv[e]);
+                num[e] = fmaf(fq, x[e], num[e]);
+            }
+            __builtin_nontemporal_store(x, sb + (size_t)row * C4 + c4);
+        }
+        *reinterpret_cast<f32x4 *>(&red[r0][4 * c4]) = num;
+    }
+    __syncthreads();
+    if (tid < DV) {
+        float acc = 0.f;
+#pragma unroll 8
+        for (int r = 0; r < ROWS; ++r) acc += red[r][tid];
+        const float den = sden[0] + sden[1] + sden[2] + sden[3];
+        store_elem<T>(o, (size_t)bh * DV + tid, acc / (den + eps));
+    }
+}
+
+} // namespace linattn

@@ -1,0 +1,137 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol,
+and rejects bad arguments on the host before anything is launched.
+
+Every call here is built to fail validation (or is pure host arithmetic), so
+no kernel is ever launched on the fake pointers used below.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_attention_phi_amd import binding as b
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "linattn.h")
+
+OK, EINVAL, ESHAPE, EDTYPE, EWORKSPACE, ELAUNCH = 0, -1, -2, -3, -4, -5
+P = ctypes.c_void_p
+FAKE = [P((i + 1) << 36) for i in range(12)]  # far apart, never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\s*\*)\s*(linattn_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return b.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(L, n), n
+    # and the binding declares a signature for each of them
+    assert set(names) == set(b.SIGNATURES)
+
+
+def test_abi_version_matches_header(L):
+    m = re.search(r"#define LINATTN_ABI_VERSION (\d+)", open(HEADER).read())
+    assert L.linattn_abi_version() == int(m.group(1))
+
+
+def test_status_strings(L):
+    for rc in (OK, EINVAL, ESHAPE, EDTYPE, EWORKSPACE, ELAUNCH):
+        assert L.linattn_status_string(rc)
+    assert L.linattn_status_string(-99) == b"unknown status"
+
+
+def test_workspace_size_is_host_arithmetic(L):
+    ws = L.linattn_workspace_size
+    # one segment per head, no prefix needed
+    assert ws(0, 1, 1, 64, 16, 16, 0) == 0
+    assert ws(0, 256, 32, 64, 128, 128, 1) == 0
+    # long sequence on few heads: segments and their states
+    n = ws(0, 1, 16, 131072, 128, 128, 1)
+    assert n >= 16 * 2 * (128 * 128 + 128) * 4
+    assert ws(1, 1, 16, 131072, 128, 128, 1) > n  # plus the gate products
+    assert ws(2, 1, 1, 64, 16, 16, 0) > 0          # non-causal always needs the total
+    # invalid arguments -> 0
+    assert ws(3, 1, 1, 64, 16, 16, 0) == 0
+    assert ws(0, 0, 1, 64, 16, 16, 0) == 0
+    assert ws(0, 1, 1, 64, 48, 16, 0) == 0
+    assert ws(0, 1, 1, 64, 16, 16, 7) == 0
+
+
+def fwd(L, q=FAKE[0], k=FAKE[1], v=FAKE[2], o=FAKE[3], si=None, zi=None, sf=None, zf=None, B=1, H=1, N=64, Dk=16,
+        Dv=16, dtype=0, phi=0, eps=1e-6, ws=None, wsb=0):
+    return L.linattn_forward(q, k, v, o, si, zi, sf, zf, B, H, N, Dk, Dv, dtype, phi, eps, ws, wsb, None)
+
+
+def test_forward_rejects_bad_arguments(L):
+    assert fwd(L, q=None) == EINVAL
+    assert fwd(L, o=None) == EINVAL
+    assert fwd(L, B=0) == EINVAL
+    assert fwd(L, H=-1) == EINVAL
+    assert fwd(L, N=0) == EINVAL
+    assert fwd(L, eps=-1.0) == EINVAL
+    assert fwd(L, eps=float("nan")) == EINVAL
+    assert fwd(L, eps=float("inf")) == EINVAL
+    assert fwd(L, Dk=48) == ESHAPE
+    assert fwd(L, Dv=256) == ESHAPE
+    assert fwd(L, Dk=8) == ESHAPE
+    assert fwd(L, dtype=2) == EDTYPE
+    assert fwd(L, phi=5) == EDTYPE
+    assert fwd(L, si=FAKE[4]) == EINVAL           # s_init without z_init
+    assert fwd(L, zf=FAKE[5]) == EINVAL           # z_final without s_final
+    assert fwd(L, o=P(FAKE[0].value + 64)) == EINVAL  # o overlaps q
+    assert fwd(L, o=FAKE[2]) == EINVAL            # o is v
+    # a long sequence needs a workspace: none, or one byte short
+    need = L.linattn_workspace_size(0, 1, 2, 8192, 64, 64, 1)
+    assert need > 0
+    assert fwd(L, B=1, H=2, N=8192, Dk=64, Dv=64, dtype=1) == EWORKSPACE
+    assert fwd(L, B=1, H=2, N=8192, Dk=64, Dv=64, dtype=1, ws=FAKE[6], wsb=need - 1) == EWORKSPACE
+
+
+def test_gated_requires_alpha(L):
+    rc = L.linattn_forward_gated(FAKE[0], FAKE[1], FAKE[2], None, FAKE[3], None, None, None, None, 1, 1, 64, 16, 16,
+                                 0, 0, 1e-6, None, 0, None)
+    assert rc == EINVAL
+    need = L.linattn_workspace_size(1, 1, 1, 1 << 16, 32, 32, 1)
+    rc = L.linattn_forward_gated(FAKE[0], FAKE[1], FAKE[2], FAKE[4], FAKE[3], None, None, None, None, 1, 1, 1 << 16,
+                                 32, 32, 1, 0, 1e-6, FAKE[5], need - 1, None)
+    assert rc == EWORKSPACE
+
+
+def test_noncausal_rejects_bad_arguments(L):
+    f = L.linattn_forward_noncausal
+    assert f(FAKE[0], FAKE[1], FAKE[2], FAKE[3], FAKE[4], None, 1, 1, 64, 16, 16, 0, 0, 1e-6, FAKE[5], 1 << 20,
+             None) == EINVAL
+    assert f(FAKE[0], FAKE[1], FAKE[2], FAKE[3], None, None, 1, 1, 64, 16, 16, 0, 0, 1e-6, None, 0, None) == EWORKSPACE
+    assert f(FAKE[0], FAKE[1], FAKE[2], FAKE[3], None, None, 1, 1, 64, 24, 16, 0, 0, 1e-6, FAKE[5], 1 << 20,
+             None) == ESHAPE
+
+
+def test_decode_rejects_bad_arguments(L):
+    f = L.linattn_decode_step
+    assert f(FAKE[0], FAKE[1], FAKE[2], None, FAKE[4], None, FAKE[5], 2, 2, 16, 16, 0, 0, 1e-6, None) == EINVAL
+    assert f(FAKE[0], FAKE[1], FAKE[2], FAKE[3], FAKE[4], None, FAKE[5], 0, 2, 16, 16, 0, 0, 1e-6, None) == EINVAL
+    assert f(FAKE[0], FAKE[1], FAKE[2], FAKE[3], FAKE[4], None, FAKE[5], 2, 2, 16, 12, 0, 0, 1e-6, None) == ESHAPE
+    assert f(FAKE[0], FAKE[1], FAKE[2], FAKE[3], FAKE[4], None, FAKE[5], 2, 2, 16, 16, 3, 0, 1e-6, None) == EDTYPE
+    # s and z overlap (z inside s)
+    s = FAKE[3]
+    assert f(FAKE[0], FAKE[1], FAKE[2], s, P(s.value + 256), None, FAKE[5], 2, 2, 16, 16, 0, 0, 1e-6,
+             None) == EINVAL
+    # o inside s
+    assert f(FAKE[0], FAKE[1], FAKE[2], s, FAKE[4], None, P(s.value + 64), 2, 2, 16, 16, 0, 0, 1e-6, None) == EINVAL
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 1, 4, 16)
+    with pytest.raises(TypeError):
+        b.linattn_forward(x, x, x)
