@@ -23,13 +23,17 @@ namespace {
 // multiple of the 64-token chunk).  Segments run in parallel; the state each
 // segment starts from is the prefix of the states of the segments before it.
 // P is chosen so that P * B * H workgroups cover the 256 compute units.
-constexpr int kTargetGroupsMfma = 256;
+constexpr int kTargetGroupsMfma = 256;      // output pass: one workgroup per compute unit
+constexpr int kTargetGroupsState = 512;     // state pass: two per compute unit
 constexpr int kTargetWavesRecur = 2048;
 
 struct Plan {
     bool mfma = false;
-    int P = 1;        // segments per (b, h)
-    int seg_len = 0;  // tokens per segment
+    int P = 1;        // output segments per (b, h)
+    int seg_len = 0;  // tokens per output segment
+    int R = 1;        // state sub-segments per output segment
+    int Ps = 1;       // state cells per (b, h) = P * R
+    int sub_len = 0;  // tokens per state sub-segment
     int nvb = 1;      // 64-column value blocks (recurrence path)
     size_t E = 0;     // floats of one state (Dk * Dv + Dk)
     size_t ws_states = 0, ws_gam = 0, ws_total = 0, ws_bytes = 0;
@@ -51,10 +55,22 @@ Plan make_plan(int kind, int B, int H, int N, int Dk, int Dv, int dtype) {
     const int cps = (int)((nch + want - 1) / want);
     p.P = (nch + cps - 1) / cps;
     p.seg_len = cps * kChunk;
+    // The state pass streams only K and V and fits two workgroups per compute
+    // unit: split each output segment into R sub-segments (R divides cps).
+    if (p.mfma) {
+        const long long want_r = (kTargetGroupsState + (long long)p.P * BH - 1) / ((long long)p.P * BH);
+        for (int r = (int)(want_r < cps ? want_r : cps); r >= 1; --r)
+            if (cps % r == 0) {
+                p.R = r;
+                break;
+            }
+    }
+    p.Ps = p.P * p.R;
+    p.sub_len = p.seg_len / p.R;
     p.E = (size_t)Dk * Dv + Dk;
     const bool need_states = kind == LINATTN_KIND_NONCAUSAL || p.P > 1;
-    if (need_states) p.ws_states = align256((size_t)BH * p.P * p.E * sizeof(float));
-    if (kind == LINATTN_KIND_GATED && p.P > 1) p.ws_gam = align256((size_t)BH * p.P * sizeof(float));
+    if (need_states) p.ws_states = align256((size_t)BH * p.Ps * p.E * sizeof(float));
+    if (kind == LINATTN_KIND_GATED && p.P > 1) p.ws_gam = align256((size_t)BH * p.Ps * sizeof(float));
     if (kind == LINATTN_KIND_NONCAUSAL) p.ws_total = align256((size_t)BH * p.E * sizeof(float));
     p.ws_bytes = p.ws_states + p.ws_gam + p.ws_total;
     return p;
@@ -133,20 +149,22 @@ int run_mfma_causal(const Plan &pl, const void *q, const void *k, const void *v,
     if (pl.P > 1) {
         float *states = reinterpret_cast<float *>(ws);
         float *gam = GATED ? reinterpret_cast<float *>(ws + pl.ws_states) : nullptr;
-        const int P_run = pl.P - 1;
+        // the sub-segments of the last output segment are never needed
+        const int P_run = (pl.P - 1) * pl.R;
         LA_TRY(launch("seg_state_bf16", st, [&] {
             seg_state_bf16<DK, DV, GATED><<<dim3(P_run * BH), dim3(kThreads), 0, st>>>(
-                (const uint16_t *)k, (const uint16_t *)v, alpha, states, gam, N, pl.P, P_run, pl.seg_len, phi);
+                (const uint16_t *)k, (const uint16_t *)v, alpha, states, gam, N, pl.Ps, P_run, pl.sub_len, phi);
         }));
         LA_TRY(launch("seg_prefix", st, [&] {
             seg_prefix<<<dim3((unsigned)((pl.E + 255) / 256), BH), dim3(256), 0, st>>>(states, gam, s_init, z_init,
-                                                                                       pl.P, DK, DV);
+                                                                                       pl.Ps, P_run + 1, DK, DV);
         }));
+        // output segment p starts from the prefix before state cell p * R
         start = states;
         start_z = states + (size_t)DK * DV;
-        sbh = (size_t)pl.P * pl.E;
-        sseg = pl.E;
-        zbh = (size_t)pl.P * pl.E;
+        sbh = (size_t)pl.Ps * pl.E;
+        sseg = (size_t)pl.R * pl.E;
+        zbh = (size_t)pl.Ps * pl.E;
     }
     return launch(GATED ? "fwd_out_bf16_gated" : "fwd_out_bf16", st, [&] {
         fwd_out_bf16<DK, DV, GATED><<<dim3(pl.P * BH), dim3(kThreads), 0, st>>>(
@@ -161,11 +179,11 @@ int run_mfma_noncausal(const Plan &pl, const void *q, const void *k, const void 
     float *states = reinterpret_cast<float *>(ws);
     float *total = reinterpret_cast<float *>(ws + pl.ws_states + pl.ws_gam);
     LA_TRY(launch("seg_state_bf16", st, [&] {
-        seg_state_bf16<DK, DV, false><<<dim3(pl.P * BH), dim3(kThreads), 0, st>>>(
-            (const uint16_t *)k, (const uint16_t *)v, nullptr, states, nullptr, N, pl.P, pl.P, pl.seg_len, phi);
+        seg_state_bf16<DK, DV, false><<<dim3(pl.Ps * BH), dim3(kThreads), 0, st>>>(
+            (const uint16_t *)k, (const uint16_t *)v, nullptr, states, nullptr, N, pl.Ps, pl.Ps, pl.sub_len, phi);
     }));
     LA_TRY(launch("seg_total", st, [&] {
-        seg_total<<<dim3((unsigned)((pl.E + 255) / 256), BH), dim3(256), 0, st>>>(states, total, s_out, z_out, pl.P,
+        seg_total<<<dim3((unsigned)((pl.E + 255) / 256), BH), dim3(256), 0, st>>>(states, total, s_out, z_out, pl.Ps,
                                                                                   DK, DV);
     }));
     const int nch = (N + kChunk - 1) / kChunk;
@@ -198,7 +216,7 @@ int run_recur_causal(const Plan &pl, const void *q, const void *k, const void *v
         }));
         LA_TRY(launch("seg_prefix", st, [&] {
             seg_prefix<<<dim3((unsigned)((E + 255) / 256), BH), dim3(256), 0, st>>>(states, gam, s_init, z_init, pl.P,
-                                                                                    DK, Dv);
+                                                                                    pl.P, DK, Dv);
         }));
         start = states;
         start_z = states + (size_t)DK * Dv;

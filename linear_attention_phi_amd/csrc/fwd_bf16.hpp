@@ -301,12 +301,17 @@ __device__ __forceinline__ void rows_to_end_decay(const ChunkGates &cg, int last
 }
 
 // ====================================================================== kernels
+// Both chunk kernels keep two chunks of loads in flight: the registers of
+// buffer c % 2 are staged into LDS for chunk c and immediately reloaded with
+// chunk c + 2, so the loads of two chunks overlap the compute of one.
+
 // Segment-state pass: for segment p of (b, h), the state the segment adds when
 // started from zero: dS = sum phi(k_j) v_j^T (decayed to the segment end when
 // gated), dz likewise, and the segment's total gate product.
-// Grid: one workgroup per (segment, bh) with segment index fastest.
+// Grid: one workgroup per (segment, bh) with segment index fastest; P_run
+// segments are computed, their results stored at stride P.
 template <int DK, int DV, bool GATED>
-__global__ __launch_bounds__(kThreads, 1) void seg_state_bf16(const uint16_t *__restrict__ k,
+__global__ __launch_bounds__(kThreads, 2) void seg_state_bf16(const uint16_t *__restrict__ k,
                                                               const uint16_t *__restrict__ v,
                                                               const float *__restrict__ alpha, float *__restrict__ ws,
                                                               float *__restrict__ gam, int N, int P, int P_run,
@@ -329,42 +334,48 @@ __global__ __launch_bounds__(kThreads, 1) void seg_state_bf16(const uint16_t *__
     float seg_lsum = 0.f;
     int seg_zeros = 0;
 
-    ChunkRows<DK> kr;
-    ChunkRows<DV> vr;
-    float areg = 1.f;
-    int valid0 = min(kChunk, t_end - t_begin);
-    kr.load(kb, valid0, tid);
-    vr.load(vb, valid0, tid);
-    if (GATED) areg = lane < valid0 ? ab[lane] : 1.f;
-
-    for (int c = 0; c < nch; ++c) {
-        const int valid = min(kChunk, t_end - t_begin - c * kChunk);
+    struct Buf {
+        ChunkRows<DK> kr;
+        ChunkRows<DV> vr;
+        float a;
+    };
+    auto rows_in = [&](int c) { return min(kChunk, t_end - t_begin - c * kChunk); };
+    auto issue = [&](Buf &b, int c) {
+        const int nv = rows_in(c);
+        b.kr.load(kb + (size_t)c * kChunk * DK, nv, tid);
+        b.vr.load(vb + (size_t)c * kChunk * DV, nv, tid);
+        if (GATED) b.a = lane < nv ? ab[c * kChunk + lane] : 1.f;
+    };
+    auto step = [&](Buf &b, int c) {
+        const int valid = rows_in(c);
         float dC = 1.f;
         if (GATED) {
             ChunkGates cg;
-            cg.build(areg, lane < valid);
+            cg.build(b.a, lane < valid);
             float rs[ChunkRows<DK>::TPT];
             rows_to_end_decay<DK>(cg, valid - 1, tid, rs);
-            store_transposed<DK, true, true>(kr, sKt, L::ST, valid, tid, phi_mode, rs);
+            store_transposed<DK, true, true>(b.kr, sKt, L::ST, valid, tid, phi_mode, rs);
             const float le = cg.lsum_at(valid - 1);
             const int ze = cg.zeros_at(valid - 1);
             dC = decay_between(le, ze, 0.f, 0);
             seg_lsum += le;
             seg_zeros += ze;
         } else {
-            store_transposed<DK, true, false>(kr, sKt, L::ST, valid, tid, phi_mode, nullptr);
+            store_transposed<DK, true, false>(b.kr, sKt, L::ST, valid, tid, phi_mode, nullptr);
         }
-        store_transposed<DV, false, false>(vr, sVt, L::ST, valid, tid, phi_mode, nullptr);
-        if (c + 1 < nch) {
-            const int nv = min(kChunk, t_end - t_begin - (c + 1) * kChunk);
-            kr.load(kb + (size_t)(c + 1) * kChunk * DK, nv, tid);
-            vr.load(vb + (size_t)(c + 1) * kChunk * DV, nv, tid);
-            if (GATED) areg = lane < nv ? ab[(c + 1) * kChunk + lane] : 1.f;
-        }
+        store_transposed<DV, false, false>(b.vr, sVt, L::ST, valid, tid, phi_mode, nullptr);
+        if (c + 2 < nch) issue(b, c + 2);
         __syncthreads();
         if (GATED) state_scale<DK, DV>(sr, dC);
         state_update<DK, DV>(sr, sKt, sVt, w, lane);
         __syncthreads();
+    };
+    Buf b0, b1;
+    issue(b0, 0);
+    if (nch > 1) issue(b1, 1);
+    for (int c = 0; c < nch; c += 2) {
+        step(b0, c);
+        if (c + 1 < nch) step(b1, c + 1);
     }
     float *dst = ws + ((size_t)bh * P + seg) * (size_t)(DK * DV + DK);
     state_store<DK, DV>(sr, dst, dst + DK * DV, w, lane);
@@ -408,44 +419,40 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_out_bf16(
     }
     state_to_lds<DK, DV>(sr, sSt, sZ, w, lane);
 
-    ChunkRows<DK> kr;
-    ChunkRows<DV> vr;
-    QueryRows<DK> qr;
-    float areg = 1.f;
-    {
-        const int v0 = min(kChunk, t_end - t_begin);
-        kr.load(kb, v0, tid);
-        vr.load(vb, v0, tid);
-        qr.load(qb, v0, w, lane);
-        if (GATED) areg = lane < v0 ? ab[lane] : 1.f;
-    }
-
-    for (int c = 0; c < nch; ++c) {
-        const int valid = min(kChunk, t_end - t_begin - c * kChunk);
+    struct Buf {
+        ChunkRows<DK> kr;
+        ChunkRows<DV> vr;
+        QueryRows<DK> qr;
+        float a;
+    };
+    auto rows_in = [&](int c) { return min(kChunk, t_end - t_begin - c * kChunk); };
+    auto issue = [&](Buf &b, int c) {
+        const int nv = rows_in(c);
+        b.kr.load(kb + (size_t)c * kChunk * DK, nv, tid);
+        b.vr.load(vb + (size_t)c * kChunk * DV, nv, tid);
+        b.qr.load(qb + (size_t)c * kChunk * DK, nv, w, lane);
+        if (GATED) b.a = lane < nv ? ab[c * kChunk + lane] : 1.f;
+    };
+    auto step = [&](Buf &b, int c) {
+        const int valid = rows_in(c);
         // ---- stage the chunk: phi(K) both ways, V^T, phi(Q) operands, gates
         bf16x8 qa[L::KS];
-        qr.to_operands(qa, valid, w, lane, phi_mode);
+        b.qr.to_operands(qa, valid, w, lane, phi_mode);
         ChunkGates cg;
         float dC = 1.f;
         if (GATED) {
-            cg.build(areg, lane < valid);
+            cg.build(b.a, lane < valid);
             float rs[ChunkRows<DK>::TPT];
             rows_to_end_decay<DK>(cg, valid - 1, tid, rs);
-            store_transposed<DK, true, true>(kr, sKt, L::ST, valid, tid, phi_mode, rs);
+            store_transposed<DK, true, true>(b.kr, sKt, L::ST, valid, tid, phi_mode, rs);
             dC = decay_between(cg.lsum_at(valid - 1), cg.zeros_at(valid - 1), 0.f, 0);
         } else {
-            store_transposed<DK, true, false>(kr, sKt, L::ST, valid, tid, phi_mode, nullptr);
+            store_transposed<DK, true, false>(b.kr, sKt, L::ST, valid, tid, phi_mode, nullptr);
         }
-        store_rows_phi<DK>(kr, sK, L::SK, valid, tid, phi_mode);
-        store_transposed<DV, false, false>(vr, sVt, L::ST, valid, tid, phi_mode, nullptr);
-        // ---- prefetch the next chunk while this one is computed
-        if (c + 1 < nch) {
-            const int nv = min(kChunk, t_end - t_begin - (c + 1) * kChunk);
-            kr.load(kb + (size_t)(c + 1) * kChunk * DK, nv, tid);
-            vr.load(vb + (size_t)(c + 1) * kChunk * DV, nv, tid);
-            qr.load(qb + (size_t)(c + 1) * kChunk * DK, nv, w, lane);
-            if (GATED) areg = lane < nv ? ab[(c + 1) * kChunk + lane] : 1.f;
-        }
+        store_rows_phi<DK>(b.kr, sK, L::SK, valid, tid, phi_mode);
+        store_transposed<DV, false, false>(b.vr, sVt, L::ST, valid, tid, phi_mode, nullptr);
+        // ---- refill this buffer with the chunk after next
+        if (c + 2 < nch) issue(b, c + 2);
         __syncthreads();
 
         // ---- scores A^T[key][query] for key blocks 0..w
@@ -518,13 +525,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_out_bf16(
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
             if (2 * s2 <= w) {
-                bf16x8 bop;
                 uint4 bu;
                 bu.x = pack_bf16x2(sc[2 * s2][0], sc[2 * s2][1]);
                 bu.y = pack_bf16x2(sc[2 * s2][2], sc[2 * s2][3]);
                 bu.z = pack_bf16x2(sc[2 * s2 + 1][0], sc[2 * s2 + 1][1]);
                 bu.w = pack_bf16x2(sc[2 * s2 + 1][2], sc[2 * s2 + 1][3]);
-                bop = as_bf16x8(bu);
+                const bf16x8 bop = as_bf16x8(bu);
 #pragma unroll
                 for (int nt = 0; nt < L::NT; ++nt) {
                     const int dv = perm_dv(nt, l16);
@@ -555,6 +561,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_out_bf16(
         state_update<DK, DV>(sr, sKt, sVt, w, lane);
         __syncthreads();
         if (c + 1 < nch) state_to_lds<DK, DV>(sr, sSt, sZ, w, lane);
+    };
+
+    Buf b0, b1;
+    issue(b0, 0);
+    if (nch > 1) issue(b1, 1);
+    for (int c = 0; c < nch; c += 2) {
+        step(b0, c);
+        if (c + 1 < nch) step(b1, c + 1);
     }
     if (s_final && seg == P - 1)
         state_store<DK, DV>(sr, s_final + (size_t)bh * DK * DV, z_final + (size_t)bh * DK, w, lane);

@@ -15,9 +15,11 @@ namespace linattn {
 // G_p S_{<p} + dS_p where G_p is the product of segment p's gates.
 // The order over segments is fixed, so the result is bitwise reproducible.
 // Grid: x = element blocks of 256, y = bh.
+// Cells 0..cells-2 hold segment states on entry; cells 0..cells-1 receive the
+// prefix (cell p gets the state before segment p).  P is the cell stride.
 __global__ __launch_bounds__(256) void seg_prefix(float *__restrict__ ws, const float *__restrict__ gam,
                                                   const float *__restrict__ s_init, const float *__restrict__ z_init,
-                                                  int P, int DK, int DV) {
+                                                  int P, int cells, int DK, int DV) {
     const int E = DK * DV + DK;
     const int e = blockIdx.x * 256 + threadIdx.x;
     const int bh = blockIdx.y;
@@ -25,11 +27,12 @@ __global__ __launch_bounds__(256) void seg_prefix(float *__restrict__ ws, const 
     float run = 0.f;
     if (s_init) run = e < DK * DV ? s_init[(size_t)bh * DK * DV + e] : z_init[(size_t)bh * DK + (e - DK * DV)];
     float *cell = ws + (size_t)bh * P * E + e;
-    for (int p = 0; p < P; ++p) {
+    for (int p = 0; p + 1 < cells; ++p) {
         const float d = cell[(size_t)p * E];
         cell[(size_t)p * E] = run;
-        if (p + 1 < P) run = gam ? fmaf(gam[(size_t)bh * P + p], run, d) : run + d;
+        run = gam ? fmaf(gam[(size_t)bh * P + p], run, d) : run + d;
     }
+    cell[(size_t)(cells - 1) * E] = run;
 }
 
 // Non-causal total: S = sum over all segments (fixed order), written to
