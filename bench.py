@@ -267,7 +267,7 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def path_entry(w, fn, nbytes, stream, args, tokens, reset=None, flops=None):
+def path_entry(w, fn, nbytes, stream, args, tokens, reset=None, flops=None, key=None):
     ms = timed(fn, args.steps, args.warmup, stream)
     if reset:
         reset()
@@ -275,9 +275,10 @@ def path_entry(w, fn, nbytes, stream, args, tokens, reset=None, flops=None):
     if reset:
         reset()
     dom = max(kt, key=lambda n: kt[n]["avg_ms"] * kt[n]["launches"])
-    return {"workload": w.name, "ms_per_step": round(ms, 4), "Mtokens_per_s": round(tokens / (ms * 1e-3) / 1e6, 3),
+    key = key or w.name
+    return {"workload": key, "ms_per_step": round(ms, 4), "Mtokens_per_s": round(tokens / (ms * 1e-3) / 1e6, 3),
             "path_roofline_frac": round(rf.hbm_time_s(nbytes) / (ms * 1e-3), 4),
-            "roofline": roofline_entry(dom, kt[dom]["avg_ms"], kernel_bytes(dom, w), w.name,
+            "roofline": roofline_entry(dom, kt[dom]["avg_ms"], kernel_bytes(dom, w), key,
                                        flops if dom.startswith("fwd_out") else None),
             "kernels_ms": {n: round(e["avg_ms"], 4) for n, e in kt.items()}}
 
@@ -296,7 +297,7 @@ def other_paths(args, dev, stream, headline_inputs):
     del fn
     log("[bench] non-causal form")
     w, fn, nbytes = noncausal_case(HEADLINE, dev, headline_inputs)
-    out["noncausal"] = path_entry(w, fn, nbytes, stream, args, w.B * w.N)
+    out["noncausal"] = path_entry(w, fn, nbytes, stream, args, w.B * w.N, key="noncausal_" + w.name)
     return out
 
 
@@ -309,7 +310,7 @@ def run_single_path(args, dev, stream):
         r = path_entry(w, fn, nbytes, stream, args, w.B, reset=reset)
     else:
         w, fn, nbytes = noncausal_case(HEADLINE, dev)
-        r = path_entry(w, fn, nbytes, stream, args, w.B * w.N)
+        r = path_entry(w, fn, nbytes, stream, args, w.B * w.N, key="noncausal_" + w.name)
     print(json.dumps(r), flush=True)
 
 
