@@ -11,6 +11,7 @@
 
 #include "../../include/linattn.h"
 #include "fwd_bf16.hpp"
+#include "fwd8_bf16.hpp"
 #include "recur.hpp"
 #include "scan_decode.hpp"
 
@@ -140,6 +141,10 @@ int check_common(int B, int H, int N, int Dk, int Dv, int dtype, int phi, float 
 }
 
 // ------------------------------------------------------------------ dispatch
+// Head dims of 64 and 128 use the eight-wave kernels (fwd8_bf16.hpp); 32 uses
+// the four-wave ones.
+template <int DK, int DV> constexpr bool kEight = DK >= 64 && DV >= 64;
+
 template <int DK, int DV, bool GATED>
 int run_mfma_causal(const Plan &pl, const void *q, const void *k, const void *v, const float *alpha, void *o,
                     const float *s_init, const float *z_init, float *s_final, float *z_final, int BH, int N,
@@ -152,8 +157,12 @@ int run_mfma_causal(const Plan &pl, const void *q, const void *k, const void *v,
         // the sub-segments of the last output segment are never needed
         const int P_run = (pl.P - 1) * pl.R;
         LA_TRY(launch("seg_state_bf16", st, [&] {
-            seg_state_bf16<DK, DV, GATED><<<dim3(P_run * BH), dim3(kThreads), 0, st>>>(
-                (const uint16_t *)k, (const uint16_t *)v, alpha, states, gam, N, pl.Ps, P_run, pl.sub_len, phi);
+            if constexpr (kEight<DK, DV>)
+                seg_state8_bf16<DK, DV, GATED><<<dim3(P_run * BH), dim3(kThreads8), 0, st>>>(
+                    (const uint16_t *)k, (const uint16_t *)v, alpha, states, gam, N, pl.Ps, P_run, pl.sub_len, phi);
+            else
+                seg_state_bf16<DK, DV, GATED><<<dim3(P_run * BH), dim3(kThreads), 0, st>>>(
+                    (const uint16_t *)k, (const uint16_t *)v, alpha, states, gam, N, pl.Ps, P_run, pl.sub_len, phi);
         }));
         LA_TRY(launch("seg_prefix", st, [&] {
             seg_prefix<<<dim3((unsigned)((pl.E + 255) / 256), BH), dim3(256), 0, st>>>(states, gam, s_init, z_init,
@@ -167,9 +176,14 @@ int run_mfma_causal(const Plan &pl, const void *q, const void *k, const void *v,
         zbh = (size_t)pl.Ps * pl.E;
     }
     return launch(GATED ? "fwd_out_bf16_gated" : "fwd_out_bf16", st, [&] {
-        fwd_out_bf16<DK, DV, GATED><<<dim3(pl.P * BH), dim3(kThreads), 0, st>>>(
-            (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, alpha, (uint16_t *)o, start, sbh, sseg,
-            start_z, zbh, s_final, z_final, N, pl.P, pl.seg_len, phi, eps);
+        if constexpr (kEight<DK, DV>)
+            fwd_out8_bf16<DK, DV, GATED><<<dim3(pl.P * BH), dim3(kThreads8), 0, st>>>(
+                (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, alpha, (uint16_t *)o, start, sbh, sseg,
+                start_z, zbh, s_final, z_final, N, pl.P, pl.seg_len, phi, eps);
+        else
+            fwd_out_bf16<DK, DV, GATED><<<dim3(pl.P * BH), dim3(kThreads), 0, st>>>(
+                (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, alpha, (uint16_t *)o, start, sbh, sseg,
+                start_z, zbh, s_final, z_final, N, pl.P, pl.seg_len, phi, eps);
     });
 }
 
@@ -179,8 +193,12 @@ int run_mfma_noncausal(const Plan &pl, const void *q, const void *k, const void 
     float *states = reinterpret_cast<float *>(ws);
     float *total = reinterpret_cast<float *>(ws + pl.ws_states + pl.ws_gam);
     LA_TRY(launch("seg_state_bf16", st, [&] {
-        seg_state_bf16<DK, DV, false><<<dim3(pl.Ps * BH), dim3(kThreads), 0, st>>>(
-            (const uint16_t *)k, (const uint16_t *)v, nullptr, states, nullptr, N, pl.Ps, pl.Ps, pl.sub_len, phi);
+        if constexpr (kEight<DK, DV>)
+            seg_state8_bf16<DK, DV, false><<<dim3(pl.Ps * BH), dim3(kThreads8), 0, st>>>(
+                (const uint16_t *)k, (const uint16_t *)v, nullptr, states, nullptr, N, pl.Ps, pl.Ps, pl.sub_len, phi);
+        else
+            seg_state_bf16<DK, DV, false><<<dim3(pl.Ps * BH), dim3(kThreads), 0, st>>>(
+                (const uint16_t *)k, (const uint16_t *)v, nullptr, states, nullptr, N, pl.Ps, pl.Ps, pl.sub_len, phi);
     }));
     LA_TRY(launch("seg_total", st, [&] {
         seg_total<<<dim3((unsigned)((pl.E + 255) / 256), BH), dim3(256), 0, st>>>(states, total, s_out, z_out, pl.Ps,

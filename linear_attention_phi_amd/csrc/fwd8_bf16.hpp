@@ -1,0 +1,539 @@
+// fwd8_bf16.hpp -- chunked causal linear attention, eight-wave version for
+// head dims Dk, Dv in {64, 128} (bf16 inputs, bf16 MFMA, fp32 state).
+//
+// Same algebra as fwd_bf16.hpp (per 64-token chunk: scores tril(phi(Q) phi(K)^T),
+// in-chunk output, read of the carried summary, state update), arranged for
+// gfx950:
+//  * 8 waves per workgroup (two per SIMD) so matrix, vector and LDS work of
+//    one wave overlaps the other's;
+//  * all chunk data sits in LDS row-major, [token][d], written with 16-byte
+//    stores; the token-contiguous operands of the contractions over tokens
+//    (phi(K)^T, V^T and V) are read with the gfx950 transposing LDS load
+//    ds_read_b64_tr_b16 instead of being written transposed;
+//  * rows are padded by 32 elements and their 16-byte chunks XOR-swizzled by
+//    row, which keeps the row reads, the transposing reads and the S^T copy at
+//    the minimum number of LDS cycles;
+//  * phi is evaluated once per element, V is staged without conversion.
+#pragma once
+
+#include "common.hpp"
+#include "fwd_bf16.hpp"
+
+namespace linattn {
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+constexpr int kThreads8 = 512;
+
+// Row-major bf16 tile in LDS with D + 32 elements per row and the 16-byte
+// chunk index XOR-ed with 2 * ((row >> 3) & 3).  Element offsets; columns
+// accessed in groups of 4 or 8 stay contiguous.
+template <int D>
+struct Tile {
+    static constexpr int RS = D + 32;
+    __device__ static __forceinline__ int off(int r, int c) {
+        return r * RS + ((((c >> 3) ^ (((r >> 3) & 3) << 1)) << 3) | (c & 7));
+    }
+};
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
+// (i % 4) of the 4-element segments addressed by lanes 4j + i/4, j = 0..3.
+__device__ __forceinline__ uint2 lds_tr16(const uint16_t *p) {
+    const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16 *)p);
+    return __builtin_bit_cast(uint2, v);
+}
+
+// MFMA operand with k along the rows of a row-major tile M[k][col]:
+// lane (G = lane >> 4, i = lane & 15) receives M[klo + j][col_i] (j = 0..3)
+// then M[khi + j][col_i] (j = 0..3), where col_i = colq(i / 4) + i % 4.  Each
+// lane passes klo / khi of its own group and colq of its own quad (lane & 3).
+template <int D>
+__device__ __forceinline__ bf16x8 tr_operand(const uint16_t *tile, int klo, int khi, int colq, int lane) {
+    const int src = lane & 15;
+    const uint2 a = lds_tr16(tile + Tile<D>::off(klo + (src >> 2), colq));
+    const uint2 b = lds_tr16(tile + Tile<D>::off(khi + (src >> 2), colq));
+    return as_bf16x8(make_uint4(a.x, a.y, b.x, b.y));
+}
+
+// phi of 8 packed bf16 values, written both plain and scaled (two packs, one phi).
+__device__ __forceinline__ void phi_pack8x2(uint4 raw, int phi_mode, bool ok, float scale, uint4 &plain,
+                                            uint4 &scaled) {
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    uint32_t *op = reinterpret_cast<uint32_t *>(&plain);
+    uint32_t *os = reinterpret_cast<uint32_t *>(&scaled);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float lo = phi_fast(bf_lo(w[e]), phi_mode), hi = phi_fast(bf_hi(w[e]), phi_mode);
+        op[e] = ok ? pack_bf16x2(lo, hi) : 0u;
+        os[e] = ok ? pack_bf16x2(lo * scale, hi * scale) : 0u;
+    }
+}
+
+__device__ __forceinline__ uint4 phi_pack8(uint4 raw, int phi_mode, bool ok, float scale) {
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    uint4 o;
+    uint32_t *ow = reinterpret_cast<uint32_t *>(&o);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float lo = phi_fast(bf_lo(w[e]), phi_mode) * scale;
+        const float hi = phi_fast(bf_hi(w[e]), phi_mode) * scale;
+        ow[e] = ok ? pack_bf16x2(lo, hi) : 0u;
+    }
+    return o;
+}
+
+// Per-thread share of a 64 x D chunk: units of 8 columns of one row, unit
+// u = tid + 512 r -> row u / (D / 8), column group u % (D / 8).
+template <int D>
+struct Units {
+    static constexpr int CG = D / 8;
+    static constexpr int N = kChunk * CG / kThreads8;
+    uint4 r[N];
+    __device__ __forceinline__ void load(const uint16_t *__restrict__ base, int rows_valid, int tid) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int u = tid + kThreads8 * i, row = u / CG, cg = u % CG;
+            r[i] = row < rows_valid ? *reinterpret_cast<const uint4 *>(base + (size_t)row * D + cg * 8)
+                                    : make_uint4(0, 0, 0, 0);
+        }
+    }
+    __device__ static __forceinline__ int row_of(int tid, int i) { return (tid + kThreads8 * i) / CG; }
+    __device__ static __forceinline__ int col_of(int tid, int i) { return ((tid + kThreads8 * i) % CG) * 8; }
+};
+
+// State tiles of one wave: 2 x 4 wave grid over (Dk, Dv).  z lives outside
+// the matrix cores: thread t < Dk owns z[t] (see ZSum).
+template <int DK, int DV>
+struct State8 {
+    static constexpr int MT = DK / 16, NT = DV / 16;
+    static constexpr int MTW = MT / 2, NTW = NT / 4;
+    f32x4 s[MTW][NTW];
+};
+
+// z += column sums of a staged chunk of phi(K): thread (dk = tid % Dk,
+// part = tid / Dk) sums its share of the 64 rows, the partial sums meet in LDS
+// and thread dk adds them in a fixed order.
+template <int DK>
+struct ZSum {
+    static constexpr int PARTS = kThreads8 / DK, ROWS = kChunk / PARTS;
+    __device__ static __forceinline__ void partial(const uint16_t *kt, float *zpart, int tid) {
+        const int dk = tid % DK, part = tid / DK;
+        float acc = 0.f;
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) acc += bf16_bits_to_f32(kt[Tile<DK>::off(part * ROWS + r, dk)]);
+        zpart[part * DK + dk] = acc;
+    }
+    __device__ static __forceinline__ float gather(const float *zpart, int tid) {
+        float acc = 0.f;
+#pragma unroll
+        for (int p = 0; p < PARTS; ++p) acc += zpart[p * DK + tid];
+        return acc;
+    }
+};
+
+template <int DK, int DV>
+__device__ __forceinline__ void state8_load(State8<DK, DV> &st, const float *s, int w, int lane) {
+    using S = State8<DK, DV>;
+    const int l16 = lane & 15, g = lane >> 4, mt0 = (w >> 2) * S::MTW, nt0 = (w & 3) * S::NTW;
+#pragma unroll
+    for (int mi = 0; mi < S::MTW; ++mi) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int dk = 16 * (mt0 + mi) + 4 * g + i;
+#pragma unroll
+            for (int ni = 0; ni < S::NTW; ++ni) st.s[mi][ni][i] = s ? s[dk * DV + 16 * (nt0 + ni) + l16] : 0.f;
+        }
+    }
+}
+
+template <int DK, int DV>
+__device__ __forceinline__ void state8_store(const State8<DK, DV> &st, float *s, int w, int lane) {
+    using S = State8<DK, DV>;
+    const int l16 = lane & 15, g = lane >> 4, mt0 = (w >> 2) * S::MTW, nt0 = (w & 3) * S::NTW;
+#pragma unroll
+    for (int mi = 0; mi < S::MTW; ++mi) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int dk = 16 * (mt0 + mi) + 4 * g + i;
+#pragma unroll
+            for (int ni = 0; ni < S::NTW; ++ni) s[dk * DV + 16 * (nt0 + ni) + l16] = st.s[mi][ni][i];
+        }
+    }
+}
+
+template <int DK, int DV>
+__device__ __forceinline__ void state8_scale(State8<DK, DV> &st, float d) {
+    using S = State8<DK, DV>;
+#pragma unroll
+    for (int mi = 0; mi < S::MTW; ++mi) {
+#pragma unroll
+        for (int ni = 0; ni < S::NTW; ++ni) st.s[mi][ni] *= d;
+    }
+}
+
+// S += phi(K)^T V over one chunk for this wave's tiles.
+// kt: phi(K) rows (decayed to the chunk end when gated), vt: V rows.
+template <int DK, int DV>
+__device__ __forceinline__ void state8_update(State8<DK, DV> &st, const uint16_t *kt, const uint16_t *vt, int w,
+                                              int lane) {
+    using S = State8<DK, DV>;
+    const int G = lane >> 4, q = lane & 3, mt0 = (w >> 2) * S::MTW, nt0 = (w & 3) * S::NTW;
+#pragma unroll
+    for (int ks = 0; ks < kChunk / 32; ++ks) {
+        const int klo = 32 * ks + 8 * G, khi = klo + 4;
+        bf16x8 a[S::MTW], b[S::NTW];
+#pragma unroll
+        for (int mi = 0; mi < S::MTW; ++mi) a[mi] = tr_operand<DK>(kt, klo, khi, 16 * (mt0 + mi) + 4 * q, lane);
+#pragma unroll
+        for (int ni = 0; ni < S::NTW; ++ni) b[ni] = tr_operand<DV>(vt, klo, khi, 16 * (nt0 + ni) + 4 * q, lane);
+#pragma unroll
+        for (int mi = 0; mi < S::MTW; ++mi) {
+#pragma unroll
+            for (int ni = 0; ni < S::NTW; ++ni) st.s[mi][ni] = mfma16x16x32(a[mi], b[ni], st.s[mi][ni]);
+        }
+    }
+}
+
+// bf16 S^T [dv][dk] (swizzled rows of Dk) into LDS.
+template <int DK, int DV>
+__device__ __forceinline__ void state8_to_lds(const State8<DK, DV> &st, uint16_t *sSt, int w, int lane) {
+    using S = State8<DK, DV>;
+    const int l16 = lane & 15, g = lane >> 4, mt0 = (w >> 2) * S::MTW, nt0 = (w & 3) * S::NTW;
+#pragma unroll
+    for (int mi = 0; mi < S::MTW; ++mi) {
+#pragma unroll
+        for (int ni = 0; ni < S::NTW; ++ni) {
+            uint2 u;
+            u.x = pack_bf16x2(st.s[mi][ni][0], st.s[mi][ni][1]);
+            u.y = pack_bf16x2(st.s[mi][ni][2], st.s[mi][ni][3]);
+            *reinterpret_cast<uint2 *>(sSt + Tile<DK>::off(16 * (nt0 + ni) + l16, 16 * (mt0 + mi) + 4 * g)) = u;
+        }
+    }
+}
+
+// ====================================================================== kernels
+// Segment-state pass (see seg_state_bf16): dS = phi(K)^T V and dz over one
+// state sub-segment, plus the segment's gate product.
+template <int DK, int DV, bool GATED>
+__global__ __launch_bounds__(kThreads8, 2) void seg_state8_bf16(const uint16_t *__restrict__ k,
+                                                                const uint16_t *__restrict__ v,
+                                                                const float *__restrict__ alpha,
+                                                                float *__restrict__ ws, float *__restrict__ gam, int N,
+                                                                int P, int P_run, int seg_len, int phi_mode) {
+    __shared__ __attribute__((aligned(16))) uint16_t sK[kChunk * Tile<DK>::RS];
+    __shared__ __attribute__((aligned(16))) uint16_t sV[kChunk * Tile<DV>::RS];
+    __shared__ __attribute__((aligned(16))) float zpart[kThreads8];
+
+    const int seg = blockIdx.x % P_run, bh = blockIdx.x / P_run;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int t_begin = seg * seg_len;
+    const int t_end = min(N, t_begin + seg_len);
+    const int nch = (t_end - t_begin + kChunk - 1) / kChunk;
+    const uint16_t *kb = k + ((size_t)bh * N + t_begin) * DK;
+    const uint16_t *vb = v + ((size_t)bh * N + t_begin) * DV;
+    const float *ab = GATED ? alpha + (size_t)bh * N + t_begin : nullptr;
+
+    State8<DK, DV> st;
+    state8_load<DK, DV>(st, nullptr, w, lane);
+    float zr = 0.f; // z[tid] for tid < DK
+    float seg_lsum = 0.f;
+    int seg_zeros = 0;
+
+    struct Buf {
+        Units<DK> k;
+        Units<DV> v;
+        float a;
+    };
+    auto rows_in = [&](int c) { return min(kChunk, t_end - t_begin - c * kChunk); };
+    auto issue = [&](Buf &b, int c) {
+        const int nv = rows_in(c);
+        b.k.load(kb + (size_t)c * kChunk * DK, nv, tid);
+        b.v.load(vb + (size_t)c * kChunk * DV, nv, tid);
+        if (GATED) b.a = lane < nv ? ab[c * kChunk + lane] : 1.f;
+    };
+    auto step = [&](Buf &b, int c) {
+        const int valid = rows_in(c);
+        float dC = 1.f;
+        ChunkGates cg;
+        if (GATED) {
+            cg.build(b.a, lane < valid);
+            const float le = cg.lsum_at(valid - 1);
+            const int ze = cg.zeros_at(valid - 1);
+            dC = decay_between(le, ze, 0.f, 0);
+            seg_lsum += le;
+            seg_zeros += ze;
+        }
+#pragma unroll
+        for (int i = 0; i < Units<DK>::N; ++i) {
+            const int row = Units<DK>::row_of(tid, i);
+            const float sc = GATED ? decay_between(cg.lsum_at(valid - 1), cg.zeros_at(valid - 1), cg.lsum_at(row),
+                                                   cg.zeros_at(row))
+                                   : 1.f;
+            *reinterpret_cast<uint4 *>(sK + Tile<DK>::off(row, Units<DK>::col_of(tid, i))) =
+                phi_pack8(b.k.r[i], phi_mode, row < valid, sc);
+        }
+#pragma unroll
+        for (int i = 0; i < Units<DV>::N; ++i)
+            *reinterpret_cast<uint4 *>(sV + Tile<DV>::off(Units<DV>::row_of(tid, i), Units<DV>::col_of(tid, i))) =
+                b.v.r[i];
+        if (c + 2 < nch) issue(b, c + 2);
+        __syncthreads();
+        if (GATED) state8_scale<DK, DV>(st, dC);
+        state8_update<DK, DV>(st, sK, sV, w, lane);
+        ZSum<DK>::partial(sK, zpart, tid);
+        __syncthreads();
+        if (tid < DK) zr = fmaf(dC, zr, ZSum<DK>::gather(zpart, tid));
+    };
+    Buf b0, b1;
+    issue(b0, 0);
+    if (nch > 1) issue(b1, 1);
+    for (int c = 0; c < nch; c += 2) {
+        step(b0, c);
+        if (c + 1 < nch) step(b1, c + 1);
+    }
+    float *dst = ws + ((size_t)bh * P + seg) * (size_t)(DK * DV + DK);
+    state8_store<DK, DV>(st, dst, w, lane);
+    if (tid < DK) dst[DK * DV + tid] = zr;
+    if (GATED && tid == 0) gam[(size_t)bh * P + seg] = seg_zeros > 0 ? 0.f : __builtin_amdgcn_exp2f(seg_lsum);
+}
+
+// Causal output pass (see fwd_out_bf16): wave w serves query block w / 2 and
+// half w % 2 of the value columns; the state tiles are split 2 x 4.
+template <int DK, int DV, bool GATED>
+__global__ __launch_bounds__(kThreads8, 1) void fwd_out8_bf16(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    const float *__restrict__ alpha, uint16_t *__restrict__ o, const float *__restrict__ start, size_t start_stride_bh,
+    size_t start_stride_seg, const float *__restrict__ start_z, size_t start_z_stride_bh, float *__restrict__ s_final,
+    float *__restrict__ z_final, int N, int P, int seg_len, int phi_mode, float eps) {
+    using TK = Tile<DK>;
+    using TV = Tile<DV>;
+    constexpr int KS = DK / 32;
+    constexpr int NT = DV / 16;
+    constexpr int NTO = NT / 2; // output tiles per wave
+    __shared__ __attribute__((aligned(16))) uint16_t sQ[kChunk * TK::RS];
+    __shared__ __attribute__((aligned(16))) uint16_t sK[kChunk * TK::RS];
+    __shared__ __attribute__((aligned(16))) uint16_t sKs[GATED ? kChunk * TK::RS : 8];
+    __shared__ __attribute__((aligned(16))) uint16_t sV[kChunk * TV::RS];
+    __shared__ __attribute__((aligned(16))) uint16_t sSt[DV * TK::RS];
+    __shared__ __attribute__((aligned(16))) float sZ[DK];
+    __shared__ __attribute__((aligned(16))) float zpart[kThreads8];
+
+    const int seg = blockIdx.x % P, bh = blockIdx.x / P;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int l16 = lane & 15, g = lane >> 4, qd = lane & 3;
+    const int qblk = w >> 1, dh = w & 1;
+    const int t_begin = seg * seg_len;
+    const int t_end = min(N, t_begin + seg_len);
+    const int nch = (t_end - t_begin + kChunk - 1) / kChunk;
+    const size_t row0 = (size_t)bh * N + t_begin;
+    const uint16_t *qbp = q + row0 * DK;
+    const uint16_t *kbp = k + row0 * DK;
+    const uint16_t *vbp = v + row0 * DV;
+    uint16_t *obp = o + row0 * DV;
+    const float *ab = GATED ? alpha + row0 : nullptr;
+
+    State8<DK, DV> st;
+    float zr = 0.f; // z[tid] for tid < DK
+    {
+        const float *s0 = start ? start + bh * start_stride_bh + seg * start_stride_seg : nullptr;
+        const float *z0 = start_z ? start_z + bh * start_z_stride_bh + seg * start_stride_seg : nullptr;
+        state8_load<DK, DV>(st, s0, w, lane);
+        if (tid < DK) {
+            zr = z0 ? z0[tid] : 0.f;
+            sZ[tid] = zr;
+        }
+    }
+    state8_to_lds<DK, DV>(st, sSt, w, lane);
+
+    // K, V (and gates) are loaded two chunks ahead (one with gates, where the
+    // decay bookkeeping needs the registers), Q one chunk ahead.
+    constexpr int DEPTH = GATED ? 1 : 2;
+    struct Buf {
+        Units<DK> k;
+        Units<DV> v;
+        float a;
+    };
+    Units<DK> qbuf;
+    auto rows_in = [&](int c) { return min(kChunk, t_end - t_begin - c * kChunk); };
+    auto issue = [&](Buf &b, int c) {
+        const int nv = rows_in(c);
+        b.k.load(kbp + (size_t)c * kChunk * DK, nv, tid);
+        b.v.load(vbp + (size_t)c * kChunk * DV, nv, tid);
+        if (GATED) b.a = lane < nv ? ab[c * kChunk + lane] : 1.f;
+    };
+    auto step = [&](Buf &b, int c) {
+        const int valid = rows_in(c);
+        // ---- stage: phi(Q), phi(K) (and decayed phi(K)), V, all row-major
+        ChunkGates cg;
+        float dC = 1.f, le = 0.f;
+        int ze = 0;
+        if (GATED) {
+            cg.build(b.a, lane < valid);
+            le = cg.lsum_at(valid - 1);
+            ze = cg.zeros_at(valid - 1);
+            dC = decay_between(le, ze, 0.f, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < Units<DK>::N; ++i) {
+            const int row = Units<DK>::row_of(tid, i), col = Units<DK>::col_of(tid, i);
+            const bool ok = row < valid;
+            *reinterpret_cast<uint4 *>(sQ + TK::off(row, col)) = phi_pack8(qbuf.r[i], phi_mode, ok, 1.f);
+            if (GATED) {
+                const float sc = decay_between(le, ze, cg.lsum_at(row), cg.zeros_at(row));
+                uint4 plain, scaled;
+                phi_pack8x2(b.k.r[i], phi_mode, ok, sc, plain, scaled);
+                *reinterpret_cast<uint4 *>(sK + TK::off(row, col)) = plain;
+                *reinterpret_cast<uint4 *>(sKs + TK::off(row, col)) = scaled;
+            } else {
+                *reinterpret_cast<uint4 *>(sK + TK::off(row, col)) = phi_pack8(b.k.r[i], phi_mode, ok, 1.f);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < Units<DV>::N; ++i)
+            *reinterpret_cast<uint4 *>(sV + TV::off(Units<DV>::row_of(tid, i), Units<DV>::col_of(tid, i))) =
+                b.v.r[i];
+        if (c + 1 < nch) qbuf.load(qbp + (size_t)(c + 1) * kChunk * DK, rows_in(c + 1), tid);
+        if (c + DEPTH < nch) issue(b, c + DEPTH);
+        __syncthreads();
+
+        // ---- phi(Q) operands of this wave's query block
+        bf16x8 qa[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            qa[ks] = *reinterpret_cast<const bf16x8 *>(sQ + TK::off(16 * qblk + l16, 32 * ks + 8 * g));
+
+        // ---- scores A^T[key][query], key blocks 0..qblk
+        f32x4 sc[4];
+#pragma unroll
+        for (int kb4 = 0; kb4 < 4; ++kb4) {
+            sc[kb4] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (kb4 <= qblk) {
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(sK + TK::off(16 * kb4 + l16, 32 * ks + 8 * g));
+                    sc[kb4] = mfma16x16x32(a, qa[ks], sc[kb4]);
+                }
+            }
+        }
+        const int tq = 16 * qblk + l16;
+        float lq = 0.f;
+        int zq = 0;
+        if (GATED) {
+            lq = cg.lsum_at(tq);
+            zq = cg.zeros_at(tq);
+        }
+        float den = 0.f;
+#pragma unroll
+        for (int kb4 = 0; kb4 < 4; ++kb4) {
+            if (kb4 <= qblk) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int tk = 16 * kb4 + 4 * g + i;
+                    float s = sc[kb4][i];
+                    if (kb4 == qblk && tk > tq) s = 0.f;
+                    if (GATED) s *= decay_between(lq, zq, cg.lsum_at(tk), cg.zeros_at(tk));
+                    sc[kb4][i] = s;
+                    den += s;
+                }
+            }
+        }
+        den = sum_over_groups(den);
+
+        // ---- summary read: O^T = S^T phi(Q)^T for this wave's value columns
+        f32x4 oacc[NTO];
+#pragma unroll
+        for (int j = 0; j < NTO; ++j) {
+            oacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const int dvr = perm_dv(dh * NTO + j, l16);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(sSt + TK::off(dvr, 32 * ks + 8 * g));
+                oacc[j] = mfma16x16x32(a, qa[ks], oacc[j]);
+            }
+        }
+        float dz = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const float4 z0 = *reinterpret_cast<const float4 *>(sZ + 32 * ks + 8 * g);
+            const float4 z1 = *reinterpret_cast<const float4 *>(sZ + 32 * ks + 8 * g + 4);
+            const uint4 u = as_u4(qa[ks]);
+            dz += bf_lo(u.x) * z0.x + bf_hi(u.x) * z0.y + bf_lo(u.y) * z0.z + bf_hi(u.y) * z0.w;
+            dz += bf_lo(u.z) * z1.x + bf_hi(u.z) * z1.y + bf_lo(u.w) * z1.z + bf_hi(u.w) * z1.w;
+        }
+        dz = sum_over_groups(dz);
+        if (GATED) {
+            const float dq = decay_between(lq, zq, 0.f, 0);
+            dz *= dq;
+#pragma unroll
+            for (int j = 0; j < NTO; ++j) oacc[j] *= dq;
+        }
+        den += dz;
+
+        // ---- in-chunk part: O^T += V^T A^T (keys permuted within 32-key steps)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            if (2 * s2 <= qblk) {
+                uint4 bu;
+                bu.x = pack_bf16x2(sc[2 * s2][0], sc[2 * s2][1]);
+                bu.y = pack_bf16x2(sc[2 * s2][2], sc[2 * s2][3]);
+                bu.z = pack_bf16x2(sc[2 * s2 + 1][0], sc[2 * s2 + 1][1]);
+                bu.w = pack_bf16x2(sc[2 * s2 + 1][2], sc[2 * s2 + 1][3]);
+                const bf16x8 bop = as_bf16x8(bu);
+                const int klo = 32 * s2 + 4 * g, khi = klo + 16;
+#pragma unroll
+                for (int j = 0; j < NTO; ++j) {
+                    const int nt = dh * NTO + j;
+                    const int colq = 32 * (nt >> 1) + 8 * qd + 4 * (nt & 1);
+                    oacc[j] = mfma16x16x32(tr_operand<DV>(sV, klo, khi, colq, lane), bop, oacc[j]);
+                }
+            }
+        }
+
+        // ---- normalize and store: 16 rows x this wave's half of Dv
+        if (tq < valid) {
+            const float inv = 1.f / (den + eps);
+            uint16_t *orow = obp + ((size_t)c * kChunk + tq) * DV;
+#pragma unroll
+            for (int pp = 0; pp < NTO / 2; ++pp) {
+                const int p = dh * (NTO / 2) + pp;
+                uint4 u;
+                u.x = pack_bf16x2(oacc[2 * pp][0] * inv, oacc[2 * pp][1] * inv);
+                u.y = pack_bf16x2(oacc[2 * pp][2] * inv, oacc[2 * pp][3] * inv);
+                u.z = pack_bf16x2(oacc[2 * pp + 1][0] * inv, oacc[2 * pp + 1][1] * inv);
+                u.w = pack_bf16x2(oacc[2 * pp + 1][2] * inv, oacc[2 * pp + 1][3] * inv);
+                *reinterpret_cast<uint4 *>(orow + 32 * p + 8 * g) = u;
+            }
+        }
+
+        // ---- carry the state across the chunk
+        if (GATED) state8_scale<DK, DV>(st, dC);
+        state8_update<DK, DV>(st, GATED ? sKs : sK, sV, w, lane);
+        ZSum<DK>::partial(GATED ? sKs : sK, zpart, tid);
+        __syncthreads();
+        if (tid < DK) {
+            zr = fmaf(dC, zr, ZSum<DK>::gather(zpart, tid));
+            sZ[tid] = zr;
+        }
+        if (c + 1 < nch) state8_to_lds<DK, DV>(st, sSt, w, lane);
+    };
+
+    qbuf.load(qbp, rows_in(0), tid);
+    if constexpr (DEPTH == 2) {
+        Buf b0, b1;
+        issue(b0, 0);
+        if (nch > 1) issue(b1, 1);
+        for (int c = 0; c < nch; c += 2) {
+            step(b0, c);
+            if (c + 1 < nch) step(b1, c + 1);
+        }
+    } else {
+        Buf b0;
+        issue(b0, 0);
+        for (int c = 0; c < nch; ++c) step(b0, c);
+    }
+    if (s_final && seg == P - 1) {
+        state8_store<DK, DV>(st, s_final + (size_t)bh * DK * DV, w, lane);
+        if (tid < DK) z_final[(size_t)bh * DK + tid] = zr;
+    }
+}
+
+} // namespace linattn
