@@ -40,9 +40,16 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
     __bf16 b = static_cast<__bf16>(f);
     return (uint32_t)__builtin_bit_cast(unsigned short, b);
 }
+// Two floats -> packed bf16 pair (one v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
+
+// The wave index as a scalar, so that conditions on it branch on the scalar unit.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // ---------------------------------------------------------------- MFMA
 // 16x16x32 bf16 -> fp32.  Lane l supplies A[l%16][8(l/16)+i], B[8(l/16)+i][l%16]

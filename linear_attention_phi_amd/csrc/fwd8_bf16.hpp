@@ -88,6 +88,8 @@ struct Units {
     static constexpr int CG = D / 8;
     static constexpr int N = kChunk * CG / kThreads8;
     uint4 r[N];
+    // Per-row guard, not a branch around the whole load: a branch would make
+    // the compiler wait for every outstanding load where the paths join.
     __device__ __forceinline__ void load(const uint16_t *__restrict__ base, int rows_valid, int tid) {
 #pragma unroll
         for (int i = 0; i < N; ++i) {
@@ -224,7 +226,7 @@ __global__ __launch_bounds__(kThreads8, 2) void seg_state8_bf16(const uint16_t *
     __shared__ __attribute__((aligned(16))) float zpart[kThreads8];
 
     const int seg = blockIdx.x % P_run, bh = blockIdx.x / P_run;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
     const int t_begin = seg * seg_len;
     const int t_end = min(N, t_begin + seg_len);
     const int nch = (t_end - t_begin + kChunk - 1) / kChunk;
@@ -318,7 +320,7 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd_out8_bf16(
     __shared__ __attribute__((aligned(16))) float zpart[kThreads8];
 
     const int seg = blockIdx.x % P, bh = blockIdx.x / P;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
     const int l16 = lane & 15, g = lane >> 4, qd = lane & 3;
     const int qblk = w >> 1, dh = w & 1;
     const int t_begin = seg * seg_len;
@@ -490,7 +492,7 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd_out8_bf16(
 
         // ---- normalize and store: 16 rows x this wave's half of Dv
         if (tq < valid) {
-            const float inv = 1.f / (den + eps);
+            const float inv = __builtin_amdgcn_rcpf(den + eps); // 1 ulp; the result is rounded to bf16
             uint16_t *orow = obp + ((size_t)c * kChunk + tq) * DV;
 #pragma unroll
             for (int pp = 0; pp < NTO / 2; ++pp) {

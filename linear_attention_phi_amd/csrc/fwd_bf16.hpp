@@ -543,7 +543,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_out_bf16(
 
         // ---- normalize and store this wave's 16 rows
         if (tq < valid) {
-            const float inv = 1.f / (den + eps);
+            const float inv = __builtin_amdgcn_rcpf(den + eps); // 1 ulp; the result is rounded to bf16
             uint16_t *orow = ob + ((size_t)c * kChunk + tq) * DV;
 #pragma unroll
             for (int p = 0; p < DV / 32; ++p) {
@@ -627,7 +627,7 @@ __global__ __launch_bounds__(kThreads, 2) void noncausal_apply_bf16(const uint16
         den = sum_over_groups(den);
         const int tq = 16 * w + l16;
         if (tq < valid) {
-            const float inv = 1.f / (den + eps);
+            const float inv = __builtin_amdgcn_rcpf(den + eps); // 1 ulp; the result is rounded to bf16
             uint16_t *orow = o + ((size_t)bh * N + (size_t)c * kChunk + tq) * DV;
 #pragma unroll
             for (int p = 0; p < DV / 32; ++p) {
