@@ -54,31 +54,29 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint16_t *tile, int klo, int 
     return as_bf16x8(make_uint4(a.x, a.y, b.x, b.y));
 }
 
-// phi of 8 packed bf16 values, written both plain and scaled (two packs, one phi).
-__device__ __forceinline__ void phi_pack8x2(uint4 raw, int phi_mode, bool ok, float scale, uint4 &plain,
-                                            uint4 &scaled) {
+// phi of 8 packed bf16 values.  Rows past the end of the sequence are not
+// masked here: their V rows are zero and causality hides their keys from every
+// valid query; only the z column sums skip them (ZSum).
+__device__ __forceinline__ uint4 phi_pack8(uint4 raw, int phi_mode) {
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    uint4 o;
+    uint32_t *ow = reinterpret_cast<uint32_t *>(&o);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ow[e] = pack_bf16x2(phi_fast(bf_lo(w[e]), phi_mode), phi_fast(bf_hi(w[e]), phi_mode));
+    return o;
+}
+
+// The same, written both plain and scaled (one phi, two packs).
+__device__ __forceinline__ void phi_pack8x2(uint4 raw, int phi_mode, float scale, uint4 &plain, uint4 &scaled) {
     const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
     uint32_t *op = reinterpret_cast<uint32_t *>(&plain);
     uint32_t *os = reinterpret_cast<uint32_t *>(&scaled);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const float lo = phi_fast(bf_lo(w[e]), phi_mode), hi = phi_fast(bf_hi(w[e]), phi_mode);
-        op[e] = ok ? pack_bf16x2(lo, hi) : 0u;
-        os[e] = ok ? pack_bf16x2(lo * scale, hi * scale) : 0u;
+        op[e] = pack_bf16x2(lo, hi);
+        os[e] = pack_bf16x2(lo * scale, hi * scale);
     }
-}
-
-__device__ __forceinline__ uint4 phi_pack8(uint4 raw, int phi_mode, bool ok, float scale) {
-    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-    uint4 o;
-    uint32_t *ow = reinterpret_cast<uint32_t *>(&o);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const float lo = phi_fast(bf_lo(w[e]), phi_mode) * scale;
-        const float hi = phi_fast(bf_hi(w[e]), phi_mode) * scale;
-        ow[e] = ok ? pack_bf16x2(lo, hi) : 0u;
-    }
-    return o;
 }
 
 // Per-thread share of a 64 x D chunk: units of 8 columns of one row, unit
@@ -117,11 +115,14 @@ struct State8 {
 template <int DK>
 struct ZSum {
     static constexpr int PARTS = kThreads8 / DK, ROWS = kChunk / PARTS;
-    __device__ static __forceinline__ void partial(const uint16_t *kt, float *zpart, int tid) {
+    __device__ static __forceinline__ void partial(const uint16_t *kt, float *zpart, int tid, int rows_valid) {
         const int dk = tid % DK, part = tid / DK;
         float acc = 0.f;
 #pragma unroll
-        for (int r = 0; r < ROWS; ++r) acc += bf16_bits_to_f32(kt[Tile<DK>::off(part * ROWS + r, dk)]);
+        for (int r = 0; r < ROWS; ++r) {
+            const float x = bf16_bits_to_f32(kt[Tile<DK>::off(part * ROWS + r, dk)]);
+            acc += part * ROWS + r < rows_valid ? x : 0.f;
+        }
         zpart[part * DK + dk] = acc;
     }
     __device__ static __forceinline__ float gather(const float *zpart, int tid) {
@@ -270,8 +271,9 @@ __global__ __launch_bounds__(kThreads8, 2) void seg_state8_bf16(const uint16_t *
             const float sc = GATED ? decay_between(cg.lsum_at(valid - 1), cg.zeros_at(valid - 1), cg.lsum_at(row),
                                                    cg.zeros_at(row))
                                    : 1.f;
-            *reinterpret_cast<uint4 *>(sK + Tile<DK>::off(row, Units<DK>::col_of(tid, i))) =
-                phi_pack8(b.k.r[i], phi_mode, row < valid, sc);
+            uint4 plain, scaled;
+            phi_pack8x2(b.k.r[i], phi_mode, sc, plain, scaled);
+            *reinterpret_cast<uint4 *>(sK + Tile<DK>::off(row, Units<DK>::col_of(tid, i))) = GATED ? scaled : plain;
         }
 #pragma unroll
         for (int i = 0; i < Units<DV>::N; ++i)
@@ -281,7 +283,7 @@ __global__ __launch_bounds__(kThreads8, 2) void seg_state8_bf16(const uint16_t *
         __syncthreads();
         if (GATED) state8_scale<DK, DV>(st, dC);
         state8_update<DK, DV>(st, sK, sV, w, lane);
-        ZSum<DK>::partial(sK, zpart, tid);
+        ZSum<DK>::partial(sK, zpart, tid, valid);
         __syncthreads();
         if (tid < DK) zr = fmaf(dC, zr, ZSum<DK>::gather(zpart, tid));
     };
@@ -315,14 +317,19 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd_out8_bf16(
     __shared__ __attribute__((aligned(16))) uint16_t sK[kChunk * TK::RS];
     __shared__ __attribute__((aligned(16))) uint16_t sKs[GATED ? kChunk * TK::RS : 8];
     __shared__ __attribute__((aligned(16))) uint16_t sV[kChunk * TV::RS];
-    __shared__ __attribute__((aligned(16))) uint16_t sSt[DV * TK::RS];
-    __shared__ __attribute__((aligned(16))) float sZ[DK];
+    // S^T in bf16, then 16 more rows: z in rows Dv, Dv+4, Dv+8, Dv+12, zeros
+    // elsewhere, so one extra MFMA tile of the summary read yields phi(q).z in
+    // element 0 of every lane.
+    __shared__ __attribute__((aligned(16))) uint16_t sSt[(DV + 16) * TK::RS];
     __shared__ __attribute__((aligned(16))) float zpart[kThreads8];
 
     const int seg = blockIdx.x % P, bh = blockIdx.x / P;
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
     const int l16 = lane & 15, g = lane >> 4, qd = lane & 3;
     const int qblk = w >> 1, dh = w & 1;
+    bf16x8 ones;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ones[i] = (__bf16)1.0f;
     const int t_begin = seg * seg_len;
     const int t_end = min(N, t_begin + seg_len);
     const int nch = (t_end - t_begin + kChunk - 1) / kChunk;
@@ -335,13 +342,20 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd_out8_bf16(
 
     State8<DK, DV> st;
     float zr = 0.f; // z[tid] for tid < DK
+    auto z_rows_to_lds = [&](float zv) {
+        const uint16_t zb = (uint16_t)f32_to_bf16_bits(zv);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sSt[TK::off(DV + 4 * r, tid)] = zb;
+    };
     {
         const float *s0 = start ? start + bh * start_stride_bh + seg * start_stride_seg : nullptr;
         const float *z0 = start_z ? start_z + bh * start_z_stride_bh + seg * start_stride_seg : nullptr;
         state8_load<DK, DV>(st, s0, w, lane);
+        for (int e = tid; e < 16 * TK::RS; e += kThreads8) sSt[DV * TK::RS + e] = 0;
+        __syncthreads();
         if (tid < DK) {
             zr = z0 ? z0[tid] : 0.f;
-            sZ[tid] = zr;
+            z_rows_to_lds(zr);
         }
     }
     state8_to_lds<DK, DV>(st, sSt, w, lane);
@@ -377,16 +391,15 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd_out8_bf16(
 #pragma unroll
         for (int i = 0; i < Units<DK>::N; ++i) {
             const int row = Units<DK>::row_of(tid, i), col = Units<DK>::col_of(tid, i);
-            const bool ok = row < valid;
-            *reinterpret_cast<uint4 *>(sQ + TK::off(row, col)) = phi_pack8(qbuf.r[i], phi_mode, ok, 1.f);
+            *reinterpret_cast<uint4 *>(sQ + TK::off(row, col)) = phi_pack8(qbuf.r[i], phi_mode);
             if (GATED) {
                 const float sc = decay_between(le, ze, cg.lsum_at(row), cg.zeros_at(row));
                 uint4 plain, scaled;
-                phi_pack8x2(b.k.r[i], phi_mode, ok, sc, plain, scaled);
+                phi_pack8x2(b.k.r[i], phi_mode, sc, plain, scaled);
                 *reinterpret_cast<uint4 *>(sK + TK::off(row, col)) = plain;
                 *reinterpret_cast<uint4 *>(sKs + TK::off(row, col)) = scaled;
             } else {
-                *reinterpret_cast<uint4 *>(sK + TK::off(row, col)) = phi_pack8(b.k.r[i], phi_mode, ok, 1.f);
+                *reinterpret_cast<uint4 *>(sK + TK::off(row, col)) = phi_pack8(b.k.r[i], phi_mode);
             }
         }
 #pragma unroll
@@ -423,7 +436,6 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd_out8_bf16(
             lq = cg.lsum_at(tq);
             zq = cg.zeros_at(tq);
         }
-        float den = 0.f;
 #pragma unroll
         for (int kb4 = 0; kb4 < 4; ++kb4) {
             if (kb4 <= qblk) {
@@ -434,11 +446,9 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd_out8_bf16(
                     if (kb4 == qblk && tk > tq) s = 0.f;
                     if (GATED) s *= decay_between(lq, zq, cg.lsum_at(tk), cg.zeros_at(tk));
                     sc[kb4][i] = s;
-                    den += s;
                 }
             }
         }
-        den = sum_over_groups(den);
 
         // ---- summary read: O^T = S^T phi(Q)^T for this wave's value columns
         f32x4 oacc[NTO];
@@ -452,23 +462,19 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd_out8_bf16(
                 oacc[j] = mfma16x16x32(a, qa[ks], oacc[j]);
             }
         }
-        float dz = 0.f;
+        // denominator tile: phi(q).z from the z rows (element 0 of every lane)
+        f32x4 dt = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const float4 z0 = *reinterpret_cast<const float4 *>(sZ + 32 * ks + 8 * g);
-            const float4 z1 = *reinterpret_cast<const float4 *>(sZ + 32 * ks + 8 * g + 4);
-            const uint4 u = as_u4(qa[ks]);
-            dz += bf_lo(u.x) * z0.x + bf_hi(u.x) * z0.y + bf_lo(u.y) * z0.z + bf_hi(u.y) * z0.w;
-            dz += bf_lo(u.z) * z1.x + bf_hi(u.z) * z1.y + bf_lo(u.w) * z1.z + bf_hi(u.w) * z1.w;
+            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(sSt + TK::off(DV + l16, 32 * ks + 8 * g));
+            dt = mfma16x16x32(a, qa[ks], dt);
         }
-        dz = sum_over_groups(dz);
         if (GATED) {
             const float dq = decay_between(lq, zq, 0.f, 0);
-            dz *= dq;
+            dt *= dq;
 #pragma unroll
             for (int j = 0; j < NTO; ++j) oacc[j] *= dq;
         }
-        den += dz;
 
         // ---- in-chunk part: O^T += V^T A^T (keys permuted within 32-key steps)
 #pragma unroll
@@ -480,6 +486,8 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd_out8_bf16(
                 bu.z = pack_bf16x2(sc[2 * s2 + 1][0], sc[2 * s2 + 1][1]);
                 bu.w = pack_bf16x2(sc[2 * s2 + 1][2], sc[2 * s2 + 1][3]);
                 const bf16x8 bop = as_bf16x8(bu);
+                // row sums of the scores into the denominator tile
+                dt = mfma16x16x32(ones, bop, dt);
                 const int klo = 32 * s2 + 4 * g, khi = klo + 16;
 #pragma unroll
                 for (int j = 0; j < NTO; ++j) {
@@ -492,7 +500,7 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd_out8_bf16(
 
         // ---- normalize and store: 16 rows x this wave's half of Dv
         if (tq < valid) {
-            const float inv = __builtin_amdgcn_rcpf(den + eps); // 1 ulp; the result is rounded to bf16
+            const float inv = __builtin_amdgcn_rcpf(dt[0] + eps); // 1 ulp; the result is rounded to bf16
             uint16_t *orow = obp + ((size_t)c * kChunk + tq) * DV;
 #pragma unroll
             for (int pp = 0; pp < NTO / 2; ++pp) {
@@ -509,11 +517,11 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd_out8_bf16(
         // ---- carry the state across the chunk
         if (GATED) state8_scale<DK, DV>(st, dC);
         state8_update<DK, DV>(st, GATED ? sKs : sK, sV, w, lane);
-        ZSum<DK>::partial(GATED ? sKs : sK, zpart, tid);
+        ZSum<DK>::partial(GATED ? sKs : sK, zpart, tid, valid);
         __syncthreads();
         if (tid < DK) {
             zr = fmaf(dC, zr, ZSum<DK>::gather(zpart, tid));
-            sZ[tid] = zr;
+            z_rows_to_lds(zr);
         }
         if (c + 1 < nch) state8_to_lds<DK, DV>(st, sSt, w, lane);
     };
