@@ -92,8 +92,7 @@ struct Units {
 #pragma unroll
         for (int i = 0; i < N; ++i) {
             const int u = tid + kThreads8 * i, row = u / CG, cg = u % CG;
-            r[i] = row < rows_valid ? *reinterpret_cast<const uint4 *>(base + (size_t)row * D + cg * 8)
-                                    : make_uint4(0, 0, 0, 0);
+            r[i] = row < rows_valid ? load_stream16(base + (size_t)row * D + cg * 8) : make_uint4(0, 0, 0, 0);
         }
     }
     __device__ static __forceinline__ int row_of(int tid, int i) { return (tid + kThreads8 * i) / CG; }

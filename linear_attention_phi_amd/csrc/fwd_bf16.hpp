@@ -67,7 +67,7 @@ struct ChunkRows {
         for (int i = 0; i < TPT; ++i) {
             const int t = tg * TPT + i;
             if (t < rows_valid)
-                r[i] = *reinterpret_cast<const uint4 *>(base + (size_t)t * D + dg * 8);
+                r[i] = load_stream16(base + (size_t)t * D + dg * 8);
             else
                 r[i] = make_uint4(0, 0, 0, 0);
         }
@@ -146,8 +146,7 @@ struct QueryRows {
         const int t = 16 * w + (lane & 15), g = lane >> 4;
 #pragma unroll
         for (int ks = 0; ks < DK / 32; ++ks)
-            r[ks] = t < rows_valid ? *reinterpret_cast<const uint4 *>(base + (size_t)t * DK + 32 * ks + 8 * g)
-                                   : make_uint4(0, 0, 0, 0);
+            r[ks] = t < rows_valid ? load_stream16(base + (size_t)t * DK + 32 * ks + 8 * g) : make_uint4(0, 0, 0, 0);
     }
     // phi applied, rounded to bf16; rows past the end become zero.
     __device__ __forceinline__ void to_operands(bf16x8 *qa, int rows_valid, int w, int lane, int phi_mode) const {
