@@ -216,7 +216,7 @@ __device__ __forceinline__ void state8_to_lds(const State8<DK, DV> &st, uint16_t
 // Segment-state pass (see seg_state_bf16): dS = phi(K)^T V and dz over one
 // state sub-segment, plus the segment's gate product.
 template <int DK, int DV, bool GATED>
-__global__ __launch_bounds__(kThreads8, 2) void seg_state8_bf16(const uint16_t *__restrict__ k,
+__global__ __launch_bounds__(kThreads8, 4) void seg_state8_bf16(const uint16_t *__restrict__ k,
                                                                 const uint16_t *__restrict__ v,
                                                                 const float *__restrict__ alpha,
                                                                 float *__restrict__ ws, float *__restrict__ gam, int N,
@@ -278,7 +278,7 @@ __global__ __launch_bounds__(kThreads8, 2) void seg_state8_bf16(const uint16_t *
         for (int i = 0; i < Units<DV>::N; ++i)
             *reinterpret_cast<uint4 *>(sV + Tile<DV>::off(Units<DV>::row_of(tid, i), Units<DV>::col_of(tid, i))) =
                 b.v.r[i];
-        if (c + 2 < nch) issue(b, c + 2);
+        if (c + 1 < nch) issue(b, c + 1);
         __syncthreads();
         if (GATED) state8_scale<DK, DV>(st, dC);
         state8_update<DK, DV>(st, sK, sV, w, lane);
@@ -286,13 +286,11 @@ __global__ __launch_bounds__(kThreads8, 2) void seg_state8_bf16(const uint16_t *
         __syncthreads();
         if (tid < DK) zr = fmaf(dC, zr, ZSum<DK>::gather(zpart, tid));
     };
-    Buf b0, b1;
+    // Two workgroups share a compute unit, so one chunk of loads in flight
+    // per workgroup (refilled as soon as it is staged) keeps both fed.
+    Buf b0;
     issue(b0, 0);
-    if (nch > 1) issue(b1, 1);
-    for (int c = 0; c < nch; c += 2) {
-        step(b0, c);
-        if (c + 1 < nch) step(b1, c + 1);
-    }
+    for (int c = 0; c < nch; ++c) step(b0, c);
     float *dst = ws + ((size_t)bh * P + seg) * (size_t)(DK * DV + DK);
     state8_store<DK, DV>(st, dst, w, lane);
     if (tid < DK) dst[DK * DV + tid] = zr;
