@@ -114,21 +114,20 @@ struct State8 {
 template <int DK>
 struct ZSum {
     static constexpr int PARTS = kThreads8 / DK, ROWS = kChunk / PARTS;
-    __device__ static __forceinline__ void partial(const uint16_t *kt, float *zpart, int tid, int rows_valid) {
+    __device__ static __forceinline__ void partial(const uint16_t *kt, float *zpart, int tid) {
         const int dk = tid % DK, part = tid / DK;
         float acc = 0.f;
 #pragma unroll
-        for (int r = 0; r < ROWS; ++r) {
-            const float x = bf16_bits_to_f32(kt[Tile<DK>::off(part * ROWS + r, dk)]);
-            acc += part * ROWS + r < rows_valid ? x : 0.f;
-        }
+        for (int r = 0; r < ROWS; ++r) acc += bf16_bits_to_f32(kt[Tile<DK>::off(part * ROWS + r, dk)]);
         zpart[part * DK + dk] = acc;
     }
-    __device__ static __forceinline__ float gather(const float *zpart, int tid) {
+    // Rows past the end hold phi(0) (the raw rows are zero, gate 1): exactly
+    // 1 for elu + 1 and 0 for the identity map; they are taken back out here.
+    __device__ static __forceinline__ float gather(const float *zpart, int tid, int rows_valid, int phi_mode) {
         float acc = 0.f;
 #pragma unroll
         for (int p = 0; p < PARTS; ++p) acc += zpart[p * DK + tid];
-        return acc;
+        return phi_mode ? acc : acc - (float)(kChunk - rows_valid);
     }
 };
 
@@ -282,9 +281,9 @@ __global__ __launch_bounds__(kThreads8, 4) void seg_state8_bf16(const uint16_t *
         __syncthreads();
         if (GATED) state8_scale<DK, DV>(st, dC);
         state8_update<DK, DV>(st, sK, sV, w, lane);
-        ZSum<DK>::partial(sK, zpart, tid, valid);
+        ZSum<DK>::partial(sK, zpart, tid);
         __syncthreads();
-        if (tid < DK) zr = fmaf(dC, zr, ZSum<DK>::gather(zpart, tid));
+        if (tid < DK) zr = fmaf(dC, zr, ZSum<DK>::gather(zpart, tid, valid, phi_mode));
     };
     // Two workgroups share a compute unit, so one chunk of loads in flight
     // per workgroup (refilled as soon as it is staged) keeps both fed.
@@ -323,7 +322,9 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd_out8_bf16(
     const int seg = blockIdx.x % P, bh = blockIdx.x / P;
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
     const int l16 = lane & 15, g = lane >> 4, qd = lane & 3;
-    const int qblk = w >> 1, dh = w & 1;
+    // Query block per wave: waves w and w + 4 share a SIMD, so blocks (0, 3) and
+    // (1, 2) -- light and heavy ends of the causal triangle -- are paired.
+    const int qblk = w < 4 ? (w >> 1) : 5 - (w >> 1), dh = w & 1;
     bf16x8 ones;
 #pragma unroll
     for (int i = 0; i < 8; ++i) ones[i] = (__bf16)1.0f;
@@ -514,10 +515,10 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd_out8_bf16(
         // ---- carry the state across the chunk
         if (GATED) state8_scale<DK, DV>(st, dC);
         state8_update<DK, DV>(st, GATED ? sKs : sK, sV, w, lane);
-        ZSum<DK>::partial(GATED ? sKs : sK, zpart, tid, valid);
+        ZSum<DK>::partial(GATED ? sKs : sK, zpart, tid);
         __syncthreads();
         if (tid < DK) {
-            zr = fmaf(dC, zr, ZSum<DK>::gather(zpart, tid));
+            zr = fmaf(dC, zr, ZSum<DK>::gather(zpart, tid, valid, phi_mode));
             z_rows_to_lds(zr);
         }
         if (c + 1 < nch) state8_to_lds<DK, DV>(st, sSt, w, lane);
