@@ -318,6 +318,9 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd_out8_bf16(
     // element 0 of every lane.
     __shared__ __attribute__((aligned(16))) uint16_t sSt[(DV + 16) * TK::RS];
     __shared__ __attribute__((aligned(16))) float zpart[kThreads8];
+    // gated: the chunk's inclusive gate prefix (log2 sum, zero count) per token
+    __shared__ __attribute__((aligned(16))) float sGl[GATED ? kChunk : 4];
+    __shared__ __attribute__((aligned(16))) int sGz[GATED ? kChunk : 4];
 
     const int seg = blockIdx.x % P, bh = blockIdx.x / P;
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
@@ -360,7 +363,7 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd_out8_bf16(
 
     // K, V (and gates) are loaded two chunks ahead (one with gates, where the
     // decay bookkeeping needs the registers), Q one chunk ahead.
-    constexpr int DEPTH = GATED ? 1 : 2;
+    constexpr int DEPTH = 2;
     struct Buf {
         Units<DK> k;
         Units<DV> v;
@@ -385,6 +388,10 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd_out8_bf16(
             le = cg.lsum_at(valid - 1);
             ze = cg.zeros_at(valid - 1);
             dC = decay_between(le, ze, 0.f, 0);
+            if (w == 0) {
+                sGl[lane] = cg.lsum;
+                sGz[lane] = cg.zeros;
+            }
         }
 #pragma unroll
         for (int i = 0; i < Units<DK>::N; ++i) {
@@ -431,18 +438,26 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd_out8_bf16(
         float lq = 0.f;
         int zq = 0;
         if (GATED) {
-            lq = cg.lsum_at(tq);
-            zq = cg.zeros_at(tq);
+            lq = sGl[tq];
+            zq = sGz[tq];
         }
 #pragma unroll
         for (int kb4 = 0; kb4 < 4; ++kb4) {
             if (kb4 <= qblk) {
+                float4 lk = make_float4(0.f, 0.f, 0.f, 0.f);
+                int4 zk = make_int4(0, 0, 0, 0);
+                if (GATED) {
+                    lk = *reinterpret_cast<const float4 *>(sGl + 16 * kb4 + 4 * g);
+                    zk = *reinterpret_cast<const int4 *>(sGz + 16 * kb4 + 4 * g);
+                }
+                const float lka[4] = {lk.x, lk.y, lk.z, lk.w};
+                const int zka[4] = {zk.x, zk.y, zk.z, zk.w};
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int tk = 16 * kb4 + 4 * g + i;
                     float s = sc[kb4][i];
                     if (kb4 == qblk && tk > tq) s = 0.f;
-                    if (GATED) s *= decay_between(lq, zq, cg.lsum_at(tk), cg.zeros_at(tk));
+                    if (GATED) s *= decay_between(lq, zq, lka[i], zka[i]);
                     sc[kb4][i] = s;
                 }
             }
