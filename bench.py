@@ -51,10 +51,32 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def timed(fn, steps, warmup, stream):
-    for _ in range(warmup):
+# After an idle spell the MI355X's power management lets the first few
+# milliseconds of a bandwidth-bound load run fast, then throttles hard (a
+# 0.63 ms step takes up to 0.93 ms) and settles over roughly 30-40 ms.  The
+# warm-up therefore runs W steps and at least SETTLE_S seconds of steps, so the
+# timed steps see the sustained clock.
+SETTLE_S = 0.1
+
+
+def warm(fn, warmup):
+    """Run the untimed warm-up; returns the number of steps it took."""
+    fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    fn()
+    torch.cuda.synchronize()
+    est = max(time.perf_counter() - t0, 1e-5)
+    n = max(warmup, int(SETTLE_S / est) + 1)
+    for _ in range(n - 2):
         fn()
     torch.cuda.synchronize()
+    return n
+
+
+def timed(fn, steps, warmup, stream):
+    """Average ms per step over exactly `steps` steps, after the warm-up."""
+    warm(fn, warmup)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
@@ -214,8 +236,8 @@ def copy_calibration(dev, steps):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-paths", action="store_true")
     ap.add_argument("--path", choices=["forward", "gated", "decode", "noncausal"], default=None)

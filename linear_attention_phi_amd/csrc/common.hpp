@@ -59,6 +59,9 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+// Eight bf16 ones (0x3f80): an MFMA operand that turns a product into row or
+// column sums.
+__device__ __forceinline__ bf16x8 bf16_ones8() { return as_bf16x8(make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u)); }
 
 // Streaming (non-temporal) 16-byte global load and store: every input row is
 // read once and every output row written once, so neither should displace
@@ -71,6 +74,18 @@ __device__ __forceinline__ void store_stream16(void *p, uint4 v) {
     __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4 *>(p));
 }
 __device__ __forceinline__ uint4 as_u4(bf16x8 v) { return __builtin_bit_cast(uint4, v); }
+
+// Buffer resource over [base, base + nbytes): raw (stride 0) buffer loads at a
+// byte offset at or past nbytes return zero instead of touching memory.  The
+// last descriptor word is the gfx9 default data format (32-bit, no swizzle).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t chunk_rsrc(const void *base, int nbytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, nbytes, 0x00020000);
+}
+// 16-byte non-temporal buffer load at byte offset voff (bounds-checked).
+__device__ __forceinline__ uint4 buffer_load_stream16(rsrc_t rs, int voff) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 2));
+}
 
 // ---------------------------------------------------------------- cross-lane
 __device__ __forceinline__ float xor_shfl(float v, int mask) {

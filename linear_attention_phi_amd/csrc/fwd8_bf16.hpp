@@ -56,7 +56,7 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint16_t *tile, int klo, int 
 
 // phi of 8 packed bf16 values.  Rows past the end of the sequence are not
 // masked here: their V rows are zero and causality hides their keys from every
-// valid query; only the z column sums skip them (ZSum).
+// valid query; only z takes them back out (state8_update).
 __device__ __forceinline__ uint4 phi_pack8(uint4 raw, int phi_mode) {
     const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
     uint4 o;
@@ -80,59 +80,47 @@ __device__ __forceinline__ void phi_pack8x2(uint4 raw, int phi_mode, float scale
 }
 
 // Per-thread share of a 64 x D chunk: units of 8 columns of one row, unit
-// u = tid + 512 r -> row u / (D / 8), column group u % (D / 8).
+// u = tid + 512 r -> row u / (D / 8), column group u % (D / 8).  A chunk is
+// contiguous (rows of D elements), so unit u sits at byte 16 u of it.
 template <int D>
 struct Units {
     static constexpr int CG = D / 8;
     static constexpr int N = kChunk * CG / kThreads8;
     uint4 r[N];
-    // Per-row guard, not a branch around the whole load: a branch would make
-    // the compiler wait for every outstanding load where the paths join.
+    // Buffer loads bounded to the chunk's valid rows: rows past the end read
+    // as zero with no per-row compare, select or branch, and the descriptor
+    // (base, size) lives in scalar registers.
     __device__ __forceinline__ void load(const uint16_t *__restrict__ base, int rows_valid, int tid) {
+        const rsrc_t rs = chunk_rsrc(base, rows_valid * D * 2);
 #pragma unroll
-        for (int i = 0; i < N; ++i) {
-            const int u = tid + kThreads8 * i, row = u / CG, cg = u % CG;
-            r[i] = row < rows_valid ? load_stream16(base + (size_t)row * D + cg * 8) : make_uint4(0, 0, 0, 0);
-        }
+        for (int i = 0; i < N; ++i) r[i] = buffer_load_stream16(rs, (tid + kThreads8 * i) * 16);
     }
     __device__ static __forceinline__ int row_of(int tid, int i) { return (tid + kThreads8 * i) / CG; }
     __device__ static __forceinline__ int col_of(int tid, int i) { return ((tid + kThreads8 * i) % CG) * 8; }
 };
 
-// State tiles of one wave: 2 x 4 wave grid over (Dk, Dv).  z lives outside
-// the matrix cores: thread t < Dk owns z[t] (see ZSum).
+// State tiles of one wave: 2 x 4 wave grid over (Dk, Dv).  z is kept as one
+// more 16 x 16 accumulator: wave w with w % 4 below MTW accumulates
+// phi(K)^T 1 for its key-dimension tile mt0 + w % 4, reusing the phi(K)^T
+// operand its state update already holds; every column of that tile then
+// holds z for the tile's 16 key dimensions.
 template <int DK, int DV>
 struct State8 {
     static constexpr int MT = DK / 16, NT = DV / 16;
     static constexpr int MTW = MT / 2, NTW = NT / 4;
     f32x4 s[MTW][NTW];
-};
-
-// z += column sums of a staged chunk of phi(K): thread (dk = tid % Dk,
-// part = tid / Dk) sums its share of the 64 rows, the partial sums meet in LDS
-// and thread dk adds them in a fixed order.
-template <int DK>
-struct ZSum {
-    static constexpr int PARTS = kThreads8 / DK, ROWS = kChunk / PARTS;
-    __device__ static __forceinline__ void partial(const uint16_t *kt, float *zpart, int tid) {
-        const int dk = tid % DK, part = tid / DK;
-        float acc = 0.f;
-#pragma unroll
-        for (int r = 0; r < ROWS; ++r) acc += bf16_bits_to_f32(kt[Tile<DK>::off(part * ROWS + r, dk)]);
-        zpart[part * DK + dk] = acc;
-    }
-    // Rows past the end hold phi(0) (the raw rows are zero, gate 1): exactly
-    // 1 for elu + 1 and 0 for the identity map; they are taken back out here.
-    __device__ static __forceinline__ float gather(const float *zpart, int tid, int rows_valid, int phi_mode) {
-        float acc = 0.f;
-#pragma unroll
-        for (int p = 0; p < PARTS; ++p) acc += zpart[p * DK + tid];
-        return phi_mode ? acc : acc - (float)(kChunk - rows_valid);
+    f32x4 z;
+    __device__ static __forceinline__ int zmi(int w) { return w & 3; }
+    __device__ static __forceinline__ bool has_z(int w) { return (w & 3) < MTW; }
+    // first key dimension of this lane's four z values (elements 0..3)
+    __device__ static __forceinline__ int z_dk(int w, int lane) {
+        return 16 * ((w >> 2) * MTW + (w & 3)) + 4 * (lane >> 4);
     }
 };
 
+// s: [Dk][Dv] (or null for zeros); z: [Dk] (or null for zeros).
 template <int DK, int DV>
-__device__ __forceinline__ void state8_load(State8<DK, DV> &st, const float *s, int w, int lane) {
+__device__ __forceinline__ void state8_load(State8<DK, DV> &st, const float *s, const float *z, int w, int lane) {
     using S = State8<DK, DV>;
     const int l16 = lane & 15, g = lane >> 4, mt0 = (w >> 2) * S::MTW, nt0 = (w & 3) * S::NTW;
 #pragma unroll
@@ -143,6 +131,34 @@ __device__ __forceinline__ void state8_load(State8<DK, DV> &st, const float *s, 
 #pragma unroll
             for (int ni = 0; ni < S::NTW; ++ni) st.s[mi][ni][i] = s ? s[dk * DV + 16 * (nt0 + ni) + l16] : 0.f;
         }
+    }
+    st.z = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (z && S::has_z(w)) {
+        const int dk = S::z_dk(w, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st.z[i] = z[dk + i];
+    }
+}
+
+// z of this wave's tile to z[Dk] (lanes 0, 16, 32, 48 write four each).
+template <int DK, int DV>
+__device__ __forceinline__ void state8_store_z(const State8<DK, DV> &st, float *z, int w, int lane) {
+    using S = State8<DK, DV>;
+    if (S::has_z(w) && (lane & 15) == 0)
+        *reinterpret_cast<float4 *>(z + S::z_dk(w, lane)) = make_float4(st.z[0], st.z[1], st.z[2], st.z[3]);
+}
+
+// z in bf16 into rows row0 + {0, 4, 8, 12} of a Tile<DK> (lanes with
+// lane % 16 in {0, 4, 8, 12} write four key dimensions of one row each).
+template <int DK, int DV>
+__device__ __forceinline__ void state8_z_to_lds(const State8<DK, DV> &st, uint16_t *tile, int row0, int w, int lane) {
+    using S = State8<DK, DV>;
+    const int l16 = lane & 15;
+    if (S::has_z(w) && (l16 & 3) == 0) {
+        uint2 u;
+        u.x = pack_bf16x2(st.z[0], st.z[1]);
+        u.y = pack_bf16x2(st.z[2], st.z[3]);
+        *reinterpret_cast<uint2 *>(tile + Tile<DK>::off(row0 + l16, S::z_dk(w, lane))) = u;
     }
 }
 
@@ -169,15 +185,20 @@ __device__ __forceinline__ void state8_scale(State8<DK, DV> &st, float d) {
 #pragma unroll
         for (int ni = 0; ni < S::NTW; ++ni) st.s[mi][ni] *= d;
     }
+    st.z *= d;
 }
 
-// S += phi(K)^T V over one chunk for this wave's tiles.
-// kt: phi(K) rows (decayed to the chunk end when gated), vt: V rows.
+// S += phi(K)^T V and z += phi(K)^T 1 over one chunk for this wave's tiles.
+// kt: phi(K) rows (decayed to the chunk end when gated), vt: V rows.  Rows
+// past the end of the sequence hold phi(0) in kt and zeros in vt: they add
+// nothing to S, and pad (their number times phi(0): 1 under elu + 1, 0 under
+// the identity map) is taken back out of z.
 template <int DK, int DV>
 __device__ __forceinline__ void state8_update(State8<DK, DV> &st, const uint16_t *kt, const uint16_t *vt, int w,
-                                              int lane) {
+                                              int lane, bf16x8 ones, float pad) {
     using S = State8<DK, DV>;
     const int G = lane >> 4, q = lane & 3, mt0 = (w >> 2) * S::MTW, nt0 = (w & 3) * S::NTW;
+    const int zmi = S::zmi(w);
 #pragma unroll
     for (int ks = 0; ks < kChunk / 32; ++ks) {
         const int klo = 32 * ks + 8 * G, khi = klo + 4;
@@ -190,8 +211,10 @@ __device__ __forceinline__ void state8_update(State8<DK, DV> &st, const uint16_t
         for (int mi = 0; mi < S::MTW; ++mi) {
 #pragma unroll
             for (int ni = 0; ni < S::NTW; ++ni) st.s[mi][ni] = mfma16x16x32(a[mi], b[ni], st.s[mi][ni]);
+            if (mi == zmi) st.z = mfma16x16x32(a[mi], ones, st.z);
         }
     }
+    st.z -= pad;
 }
 
 // bf16 S^T [dv][dk] (swizzled rows of Dk) into LDS.
@@ -222,7 +245,6 @@ __global__ __launch_bounds__(kThreads8, 4) void seg_state8_bf16(const uint16_t *
                                                                 int P, int P_run, int seg_len, int phi_mode) {
     __shared__ __attribute__((aligned(16))) uint16_t sK[kChunk * Tile<DK>::RS];
     __shared__ __attribute__((aligned(16))) uint16_t sV[kChunk * Tile<DV>::RS];
-    __shared__ __attribute__((aligned(16))) float zpart[kThreads8];
 
     const int seg = blockIdx.x % P_run, bh = blockIdx.x / P_run;
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
@@ -234,8 +256,8 @@ __global__ __launch_bounds__(kThreads8, 4) void seg_state8_bf16(const uint16_t *
     const float *ab = GATED ? alpha + (size_t)bh * N + t_begin : nullptr;
 
     State8<DK, DV> st;
-    state8_load<DK, DV>(st, nullptr, w, lane);
-    float zr = 0.f; // z[tid] for tid < DK
+    state8_load<DK, DV>(st, nullptr, nullptr, w, lane);
+    const bf16x8 ones = bf16_ones8();
     float seg_lsum = 0.f;
     int seg_zeros = 0;
 
@@ -280,10 +302,8 @@ __global__ __launch_bounds__(kThreads8, 4) void seg_state8_bf16(const uint16_t *
         if (c + 1 < nch) issue(b, c + 1);
         __syncthreads();
         if (GATED) state8_scale<DK, DV>(st, dC);
-        state8_update<DK, DV>(st, sK, sV, w, lane);
-        ZSum<DK>::partial(sK, zpart, tid);
+        state8_update<DK, DV>(st, sK, sV, w, lane, ones, phi_mode ? 0.f : (float)(kChunk - valid));
         __syncthreads();
-        if (tid < DK) zr = fmaf(dC, zr, ZSum<DK>::gather(zpart, tid, valid, phi_mode));
     };
     // Two workgroups share a compute unit, so one chunk of loads in flight
     // per workgroup (refilled as soon as it is staged) keeps both fed.
@@ -292,7 +312,7 @@ __global__ __launch_bounds__(kThreads8, 4) void seg_state8_bf16(const uint16_t *
     for (int c = 0; c < nch; ++c) step(b0, c);
     float *dst = ws + ((size_t)bh * P + seg) * (size_t)(DK * DV + DK);
     state8_store<DK, DV>(st, dst, w, lane);
-    if (tid < DK) dst[DK * DV + tid] = zr;
+    state8_store_z<DK, DV>(st, dst + DK * DV, w, lane);
     if (GATED && tid == 0) gam[(size_t)bh * P + seg] = seg_zeros > 0 ? 0.f : __builtin_amdgcn_exp2f(seg_lsum);
 }
 
@@ -317,7 +337,6 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd_out8_bf16(
     // elsewhere, so one extra MFMA tile of the summary read yields phi(q).z in
     // element 0 of every lane.
     __shared__ __attribute__((aligned(16))) uint16_t sSt[(DV + 16) * TK::RS];
-    __shared__ __attribute__((aligned(16))) float zpart[kThreads8];
     // gated: the chunk's inclusive gate prefix (log2 sum, zero count) per token
     __shared__ __attribute__((aligned(16))) float sGl[GATED ? kChunk : 4];
     __shared__ __attribute__((aligned(16))) int sGz[GATED ? kChunk : 4];
@@ -328,9 +347,7 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd_out8_bf16(
     // Query block per wave: waves w and w + 4 share a SIMD, so blocks (0, 3) and
     // (1, 2) -- light and heavy ends of the causal triangle -- are paired.
     const int qblk = w < 4 ? (w >> 1) : 5 - (w >> 1), dh = w & 1;
-    bf16x8 ones;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) ones[i] = (__bf16)1.0f;
+    const bf16x8 ones = bf16_ones8();
     const int t_begin = seg * seg_len;
     const int t_end = min(N, t_begin + seg_len);
     const int nch = (t_end - t_begin + kChunk - 1) / kChunk;
@@ -342,22 +359,13 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd_out8_bf16(
     const float *ab = GATED ? alpha + row0 : nullptr;
 
     State8<DK, DV> st;
-    float zr = 0.f; // z[tid] for tid < DK
-    auto z_rows_to_lds = [&](float zv) {
-        const uint16_t zb = (uint16_t)f32_to_bf16_bits(zv);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sSt[TK::off(DV + 4 * r, tid)] = zb;
-    };
     {
         const float *s0 = start ? start + bh * start_stride_bh + seg * start_stride_seg : nullptr;
         const float *z0 = start_z ? start_z + bh * start_z_stride_bh + seg * start_stride_seg : nullptr;
-        state8_load<DK, DV>(st, s0, w, lane);
+        state8_load<DK, DV>(st, s0, z0, w, lane);
         for (int e = tid; e < 16 * TK::RS; e += kThreads8) sSt[DV * TK::RS + e] = 0;
         __syncthreads();
-        if (tid < DK) {
-            zr = z0 ? z0[tid] : 0.f;
-            z_rows_to_lds(zr);
-        }
+        state8_z_to_lds<DK, DV>(st, sSt, DV, w, lane);
     }
     state8_to_lds<DK, DV>(st, sSt, w, lane);
 
@@ -529,14 +537,12 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd_out8_bf16(
 
         // ---- carry the state across the chunk
         if (GATED) state8_scale<DK, DV>(st, dC);
-        state8_update<DK, DV>(st, GATED ? sKs : sK, sV, w, lane);
-        ZSum<DK>::partial(GATED ? sKs : sK, zpart, tid);
+        state8_update<DK, DV>(st, GATED ? sKs : sK, sV, w, lane, ones, phi_mode ? 0.f : (float)(kChunk - valid));
         __syncthreads();
-        if (tid < DK) {
-            zr = fmaf(dC, zr, ZSum<DK>::gather(zpart, tid, valid, phi_mode));
-            z_rows_to_lds(zr);
+        if (c + 1 < nch) {
+            state8_z_to_lds<DK, DV>(st, sSt, DV, w, lane);
+            state8_to_lds<DK, DV>(st, sSt, w, lane);
         }
-        if (c + 1 < nch) state8_to_lds<DK, DV>(st, sSt, w, lane);
     };
 
     qbuf.load(qbp, rows_in(0), tid);
@@ -555,7 +561,7 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd_out8_bf16(
     }
     if (s_final && seg == P - 1) {
         state8_store<DK, DV>(st, s_final + (size_t)bh * DK * DV, w, lane);
-        if (tid < DK) z_final[(size_t)bh * DK + tid] = zr;
+        state8_store_z<DK, DV>(st, z_final + (size_t)bh * DK, w, lane);
     }
 }
 
