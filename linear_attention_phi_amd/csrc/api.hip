@@ -1,6 +1,7 @@
 // api.hip -- the C ABI of include/linattn.h: argument checks, the segment
 // plan, kernel dispatch and the optional per-kernel timing.
 #include <hip/hip_runtime.h>
+#include <type_traits>
 
 #include <cmath>
 #include <cstdint>
@@ -145,6 +146,15 @@ int check_common(int B, int H, int N, int Dk, int Dv, int dtype, int phi, float 
 // the four-wave ones.
 template <int DK, int DV> constexpr bool kEight = DK >= 64 && DV >= 64;
 
+// Runs f(std::integral_constant<int, PHI>) for the feature map in use, for
+// kernels that take it as a template parameter.
+template <typename F> void with_phi(int phi, F &&f) {
+    if (phi == LINATTN_PHI_IDENTITY)
+        f(std::integral_constant<int, LINATTN_PHI_IDENTITY>{});
+    else
+        f(std::integral_constant<int, LINATTN_PHI_ELU1>{});
+}
+
 template <int DK, int DV, bool GATED>
 int run_mfma_causal(const Plan &pl, const void *q, const void *k, const void *v, const float *alpha, void *o,
                     const float *s_init, const float *z_init, float *s_final, float *z_final, int BH, int N,
@@ -158,8 +168,10 @@ int run_mfma_causal(const Plan &pl, const void *q, const void *k, const void *v,
         const int P_run = (pl.P - 1) * pl.R;
         LA_TRY(launch("seg_state_bf16", st, [&] {
             if constexpr (kEight<DK, DV>)
-                seg_state8_bf16<DK, DV, GATED><<<dim3(P_run * BH), dim3(kThreads8), 0, st>>>(
-                    (const uint16_t *)k, (const uint16_t *)v, alpha, states, gam, N, pl.Ps, P_run, pl.sub_len, phi);
+                with_phi(phi, [&](auto PH) {
+                    seg_state8_bf16<DK, DV, GATED, PH()><<<dim3(P_run * BH), dim3(kThreads8), 0, st>>>(
+                        (const uint16_t *)k, (const uint16_t *)v, alpha, states, gam, N, pl.Ps, P_run, pl.sub_len);
+                });
             else
                 seg_state_bf16<DK, DV, GATED><<<dim3(P_run * BH), dim3(kThreads), 0, st>>>(
                     (const uint16_t *)k, (const uint16_t *)v, alpha, states, gam, N, pl.Ps, P_run, pl.sub_len, phi);
@@ -177,9 +189,11 @@ int run_mfma_causal(const Plan &pl, const void *q, const void *k, const void *v,
     }
     return launch(GATED ? "fwd_out_bf16_gated" : "fwd_out_bf16", st, [&] {
         if constexpr (kEight<DK, DV>)
-            fwd_out8_bf16<DK, DV, GATED><<<dim3(pl.P * BH), dim3(kThreads8), 0, st>>>(
-                (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, alpha, (uint16_t *)o, start, sbh, sseg,
-                start_z, zbh, s_final, z_final, N, pl.P, pl.seg_len, phi, eps);
+            with_phi(phi, [&](auto PH) {
+                fwd_out8_bf16<DK, DV, GATED, PH()><<<dim3(pl.P * BH), dim3(kThreads8), 0, st>>>(
+                    (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, alpha, (uint16_t *)o, start, sbh,
+                    sseg, start_z, zbh, s_final, z_final, N, pl.P, pl.seg_len, eps);
+            });
         else
             fwd_out_bf16<DK, DV, GATED><<<dim3(pl.P * BH), dim3(kThreads), 0, st>>>(
                 (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, alpha, (uint16_t *)o, start, sbh, sseg,
@@ -194,8 +208,10 @@ int run_mfma_noncausal(const Plan &pl, const void *q, const void *k, const void 
     float *total = reinterpret_cast<float *>(ws + pl.ws_states + pl.ws_gam);
     LA_TRY(launch("seg_state_bf16", st, [&] {
         if constexpr (kEight<DK, DV>)
-            seg_state8_bf16<DK, DV, false><<<dim3(pl.Ps * BH), dim3(kThreads8), 0, st>>>(
-                (const uint16_t *)k, (const uint16_t *)v, nullptr, states, nullptr, N, pl.Ps, pl.Ps, pl.sub_len, phi);
+            with_phi(phi, [&](auto PH) {
+                seg_state8_bf16<DK, DV, false, PH()><<<dim3(pl.Ps * BH), dim3(kThreads8), 0, st>>>(
+                    (const uint16_t *)k, (const uint16_t *)v, nullptr, states, nullptr, N, pl.Ps, pl.Ps, pl.sub_len);
+            });
         else
             seg_state_bf16<DK, DV, false><<<dim3(pl.Ps * BH), dim3(kThreads), 0, st>>>(
                 (const uint16_t *)k, (const uint16_t *)v, nullptr, states, nullptr, N, pl.Ps, pl.Ps, pl.sub_len, phi);
@@ -210,8 +226,10 @@ int run_mfma_noncausal(const Plan &pl, const void *q, const void *k, const void 
     if (cpb < 1) cpb = 1;
     const int blocks = (nch + cpb - 1) / cpb;
     return launch("noncausal_apply_bf16", st, [&] {
-        noncausal_apply_bf16<DK, DV><<<dim3(blocks * BH), dim3(kThreads), 0, st>>>(
-            (const uint16_t *)q, (uint16_t *)o, total, N, blocks, cpb, phi, eps);
+        with_phi(phi, [&](auto PH) {
+            noncausal_apply_bf16<DK, DV, PH()><<<dim3(blocks * BH), dim3(kThreads), 0, st>>>(
+                (const uint16_t *)q, (uint16_t *)o, total, N, blocks, cpb, eps);
+        });
     });
 }
 

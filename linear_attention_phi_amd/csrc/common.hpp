@@ -82,9 +82,11 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 __device__ __forceinline__ rsrc_t chunk_rsrc(const void *base, int nbytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, nbytes, 0x00020000);
 }
-// 16-byte non-temporal buffer load at byte offset voff (bounds-checked).
-__device__ __forceinline__ uint4 buffer_load_stream16(rsrc_t rs, int voff) {
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 2));
+// 16-byte buffer load at byte offset voff (bounds-checked).  STREAM marks it
+// non-temporal (cache-policy bit 1).
+template <bool STREAM>
+__device__ __forceinline__ uint4 buffer_load16(rsrc_t rs, int voff) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, STREAM ? 2 : 0));
 }
 
 // ---------------------------------------------------------------- cross-lane

@@ -89,11 +89,20 @@ struct Units {
     uint4 r[N];
     // Buffer loads bounded to the chunk's valid rows: rows past the end read
     // as zero with no per-row compare, select or branch, and the descriptor
-    // (base, size) lives in scalar registers.
-    __device__ __forceinline__ void load(const uint16_t *__restrict__ base, int rows_valid, int tid) {
+    // (base, size) lives in scalar registers.  The state pass streams its
+    // reads past the caches (load_stream); the output pass reads with the
+    // default policy (load), which measured faster there.
+    template <bool STREAM>
+    __device__ __forceinline__ void load_policy(const uint16_t *__restrict__ base, int rows_valid, int tid) {
         const rsrc_t rs = chunk_rsrc(base, rows_valid * D * 2);
 #pragma unroll
-        for (int i = 0; i < N; ++i) r[i] = buffer_load_stream16(rs, (tid + kThreads8 * i) * 16);
+        for (int i = 0; i < N; ++i) r[i] = buffer_load16<STREAM>(rs, (tid + kThreads8 * i) * 16);
+    }
+    __device__ __forceinline__ void load(const uint16_t *base, int rows_valid, int tid) {
+        load_policy<false>(base, rows_valid, tid);
+    }
+    __device__ __forceinline__ void load_stream(const uint16_t *base, int rows_valid, int tid) {
+        load_policy<true>(base, rows_valid, tid);
     }
     __device__ static __forceinline__ int row_of(int tid, int i) { return (tid + kThreads8 * i) / CG; }
     __device__ static __forceinline__ int col_of(int tid, int i) { return ((tid + kThreads8 * i) % CG) * 8; }
@@ -237,12 +246,15 @@ __device__ __forceinline__ void state8_to_lds(const State8<DK, DV> &st, uint16_t
 // ====================================================================== kernels
 // Segment-state pass (see seg_state_bf16): dS = phi(K)^T V and dz over one
 // state sub-segment, plus the segment's gate product.
-template <int DK, int DV, bool GATED>
+// PHI: the feature map (0: elu + 1, 1: identity), fixed at compile time so
+// that phi costs no per-element select.
+template <int DK, int DV, bool GATED, int PHI>
 __global__ __launch_bounds__(kThreads8, 4) void seg_state8_bf16(const uint16_t *__restrict__ k,
                                                                 const uint16_t *__restrict__ v,
                                                                 const float *__restrict__ alpha,
                                                                 float *__restrict__ ws, float *__restrict__ gam, int N,
-                                                                int P, int P_run, int seg_len, int phi_mode) {
+                                                                int P, int P_run, int seg_len) {
+    constexpr int phi_mode = PHI;
     __shared__ __attribute__((aligned(16))) uint16_t sK[kChunk * Tile<DK>::RS];
     __shared__ __attribute__((aligned(16))) uint16_t sV[kChunk * Tile<DV>::RS];
 
@@ -269,8 +281,8 @@ __global__ __launch_bounds__(kThreads8, 4) void seg_state8_bf16(const uint16_t *
     auto rows_in = [&](int c) { return min(kChunk, t_end - t_begin - c * kChunk); };
     auto issue = [&](Buf &b, int c) {
         const int nv = rows_in(c);
-        b.k.load(kb + (size_t)c * kChunk * DK, nv, tid);
-        b.v.load(vb + (size_t)c * kChunk * DV, nv, tid);
+        b.k.load_stream(kb + (size_t)c * kChunk * DK, nv, tid);
+        b.v.load_stream(vb + (size_t)c * kChunk * DV, nv, tid);
         if (GATED) b.a = lane < nv ? ab[c * kChunk + lane] : 1.f;
     };
     auto step = [&](Buf &b, int c) {
@@ -318,12 +330,13 @@ __global__ __launch_bounds__(kThreads8, 4) void seg_state8_bf16(const uint16_t *
 
 // Causal output pass (see fwd_out_bf16): wave w serves query block w / 2 and
 // half w % 2 of the value columns; the state tiles are split 2 x 4.
-template <int DK, int DV, bool GATED>
+template <int DK, int DV, bool GATED, int PHI>
 __global__ __launch_bounds__(kThreads8, 1) void fwd_out8_bf16(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const float *__restrict__ alpha, uint16_t *__restrict__ o, const float *__restrict__ start, size_t start_stride_bh,
     size_t start_stride_seg, const float *__restrict__ start_z, size_t start_z_stride_bh, float *__restrict__ s_final,
-    float *__restrict__ z_final, int N, int P, int seg_len, int phi_mode, float eps) {
+    float *__restrict__ z_final, int N, int P, int seg_len, float eps) {
+    constexpr int phi_mode = PHI;
     using TK = Tile<DK>;
     using TV = Tile<DV>;
     constexpr int KS = DK / 32;

@@ -575,12 +575,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_out_bf16(
 
 // Non-causal read: every query of (b, h) reads the one global state.
 // Grid: one workgroup per (block of chunks, bh), block index fastest.
-template <int DK, int DV>
+template <int DK, int DV, int PHI>
 __global__ __launch_bounds__(kThreads, 2) void noncausal_apply_bf16(const uint16_t *__restrict__ q,
                                                                     uint16_t *__restrict__ o,
                                                                     const float *__restrict__ total, int N,
                                                                     int blocks_per_bh, int chunks_per_block,
-                                                                    int phi_mode, float eps) {
+                                                                    float eps) {
+    constexpr int phi_mode = PHI; // 0: elu + 1, 1: identity (compile-time)
     using L = FwdLayout<DK, DV>;
     __shared__ __attribute__((aligned(16))) uint16_t sSt[DV * L::SS];
     __shared__ __attribute__((aligned(16))) float sZ[DK];

@@ -27,10 +27,26 @@ __global__ __launch_bounds__(256) void seg_prefix(float *__restrict__ ws, const 
     float run = 0.f;
     if (s_init) run = e < DK * DV ? s_init[(size_t)bh * DK * DV + e] : z_init[(size_t)bh * DK + (e - DK * DV)];
     float *cell = ws + (size_t)bh * P * E + e;
-    for (int p = 0; p + 1 < cells; ++p) {
-        const float d = cell[(size_t)p * E];
-        cell[(size_t)p * E] = run;
-        run = gam ? fmaf(gam[(size_t)bh * P + p], run, d) : run + d;
+    const float *gb = gam ? gam + (size_t)bh * P : nullptr;
+    // Eight segments' loads are issued before their stores: the loop is a
+    // chain of dependent adds, and a load placed after a store to the same
+    // array would otherwise wait a full memory latency per segment.
+    constexpr int kBatch = 8;
+    for (int p0 = 0; p0 + 1 < cells; p0 += kBatch) {
+        const int nb = min(kBatch, cells - 1 - p0);
+        float d[kBatch], gm[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            d[j] = j < nb ? cell[(size_t)(p0 + j) * E] : 0.f;
+            gm[j] = gb && j < nb ? gb[p0 + j] : 1.f;
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            if (j < nb) {
+                cell[(size_t)(p0 + j) * E] = run;
+                run = gb ? fmaf(gm[j], run, d[j]) : run + d[j];
+            }
+        }
     }
     cell[(size_t)(cells - 1) * E] = run;
 }
@@ -46,6 +62,7 @@ __global__ __launch_bounds__(256) void seg_total(const float *__restrict__ ws, f
     if (e >= E) return;
     const float *cell = ws + (size_t)bh * P * E + e;
     float run = 0.f;
+#pragma unroll 8
     for (int p = 0; p < P; ++p) run += cell[(size_t)p * E];
     total[(size_t)bh * E + e] = run;
     if (s_out) {
