@@ -35,6 +35,28 @@ struct Tile {
     }
 };
 
+// The bf16 copy of the state S in LDS: [dk][dv], Dv elements per row, no
+// padding, its 8-byte groups of 4 elements XOR-swizzled by a GF(2)-linear map
+// of row bits 0..3 (images 1, C1, 2, C3).  It is written 8 bytes per lane from
+// the S^T accumulators (16 consecutive rows per group of 16 lanes) and read
+// with the transposing load as the S^T operand of the summary read, whose
+// value columns are permuted as in perm_dv.  With 32 LDS banks serving each
+// 16-lane group of a 64-bit write and 64 banks each half-wave of a 64-bit
+// read, the map puts both patterns on distinct banks (for Dv = 128 and 64).
+template <int DV>
+struct TileS {
+    static_assert(DV == 64 || DV == 128, "TileS covers Dv = 64 and 128");
+    static constexpr int G = DV / 4;
+    static constexpr int C1 = DV == 128 ? 8 : 5, C3 = DV == 128 ? 20 : 8;
+    __device__ static __forceinline__ int sw(int r) {
+        return (r & 1) ^ ((r & 2) ? C1 : 0) ^ ((r & 4) ? 2 : 0) ^ ((r & 8) ? C3 : 0);
+    }
+    // element offset of (r, c); c % 4 is kept, so 4-element groups stay contiguous
+    __device__ static __forceinline__ int off(int r, int c) {
+        return r * DV + ((((c >> 2) ^ sw(r)) & (G - 1)) << 2) + (c & 3);
+    }
+};
+
 // ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
 // (i % 4) of the 4-element segments addressed by lanes 4j + i/4, j = 0..3.
 __device__ __forceinline__ uint2 lds_tr16(const uint16_t *p) {
@@ -46,12 +68,16 @@ __device__ __forceinline__ uint2 lds_tr16(const uint16_t *p) {
 // lane (G = lane >> 4, i = lane & 15) receives M[klo + j][col_i] (j = 0..3)
 // then M[khi + j][col_i] (j = 0..3), where col_i = colq(i / 4) + i % 4.  Each
 // lane passes klo / khi of its own group and colq of its own quad (lane & 3).
+template <typename L>
+__device__ __forceinline__ bf16x8 tr_operand_in(const uint16_t *tile, int klo, int khi, int colq, int lane) {
+    const int src = lane & 15;
+    const uint2 a = lds_tr16(tile + L::off(klo + (src >> 2), colq));
+    const uint2 b = lds_tr16(tile + L::off(khi + (src >> 2), colq));
+    return as_bf16x8(make_uint4(a.x, a.y, b.x, b.y));
+}
 template <int D>
 __device__ __forceinline__ bf16x8 tr_operand(const uint16_t *tile, int klo, int khi, int colq, int lane) {
-    const int src = lane & 15;
-    const uint2 a = lds_tr16(tile + Tile<D>::off(klo + (src >> 2), colq));
-    const uint2 b = lds_tr16(tile + Tile<D>::off(khi + (src >> 2), colq));
-    return as_bf16x8(make_uint4(a.x, a.y, b.x, b.y));
+    return tr_operand_in<Tile<D>>(tile, klo, khi, colq, lane);
 }
 
 // phi of 8 packed bf16 values.  Rows past the end of the sequence are not
@@ -108,11 +134,13 @@ struct Units {
     __device__ static __forceinline__ int col_of(int tid, int i) { return ((tid + kThreads8 * i) % CG) * 8; }
 };
 
-// State tiles of one wave: 2 x 4 wave grid over (Dk, Dv).  z is kept as one
-// more 16 x 16 accumulator: wave w with w % 4 below MTW accumulates
-// phi(K)^T 1 for its key-dimension tile mt0 + w % 4, reusing the phi(K)^T
-// operand its state update already holds; every column of that tile then
-// holds z for the tile's 16 key dimensions.
+// State tiles of one wave: 2 x 4 wave grid over (Dk, Dv), held transposed:
+// the accumulator of tile (mi, ni) is S^T over value rows 16 nt + 4 g + i and
+// key columns 16 mt + l16, so lane (g, l16) holds S[dk][dv .. dv + 3] with
+// dk = 16 mt + l16, dv = 16 nt + 4 g.  z is one more accumulator: wave w with
+// w % 4 below MTW accumulates 1^T phi(K) for its key-dimension tile
+// mt0 + w % 4 (reusing the phi(K) operand its state update already holds), so
+// every element of lane l16 holds z[16 (mt0 + w % 4) + l16].
 template <int DK, int DV>
 struct State8 {
     static constexpr int MT = DK / 16, NT = DV / 16;
@@ -121,10 +149,8 @@ struct State8 {
     f32x4 z;
     __device__ static __forceinline__ int zmi(int w) { return w & 3; }
     __device__ static __forceinline__ bool has_z(int w) { return (w & 3) < MTW; }
-    // first key dimension of this lane's four z values (elements 0..3)
-    __device__ static __forceinline__ int z_dk(int w, int lane) {
-        return 16 * ((w >> 2) * MTW + (w & 3)) + 4 * (lane >> 4);
-    }
+    // the key dimension whose z this lane holds
+    __device__ static __forceinline__ int z_dk(int w, int lane) { return 16 * ((w >> 2) * MTW + (w & 3)) + (lane & 15); }
 };
 
 // s: [Dk][Dv] (or null for zeros); z: [Dk] (or null for zeros).
@@ -135,40 +161,14 @@ __device__ __forceinline__ void state8_load(State8<DK, DV> &st, const float *s, 
 #pragma unroll
     for (int mi = 0; mi < S::MTW; ++mi) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int dk = 16 * (mt0 + mi) + 4 * g + i;
+        for (int ni = 0; ni < S::NTW; ++ni) {
+            const float *p = s ? s + (size_t)(16 * (mt0 + mi) + l16) * DV + 16 * (nt0 + ni) + 4 * g : nullptr;
 #pragma unroll
-            for (int ni = 0; ni < S::NTW; ++ni) st.s[mi][ni][i] = s ? s[dk * DV + 16 * (nt0 + ni) + l16] : 0.f;
+            for (int i = 0; i < 4; ++i) st.s[mi][ni][i] = p ? p[i] : 0.f;
         }
     }
-    st.z = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (z && S::has_z(w)) {
-        const int dk = S::z_dk(w, lane);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) st.z[i] = z[dk + i];
-    }
-}
-
-// z of this wave's tile to z[Dk] (lanes 0, 16, 32, 48 write four each).
-template <int DK, int DV>
-__device__ __forceinline__ void state8_store_z(const State8<DK, DV> &st, float *z, int w, int lane) {
-    using S = State8<DK, DV>;
-    if (S::has_z(w) && (lane & 15) == 0)
-        *reinterpret_cast<float4 *>(z + S::z_dk(w, lane)) = make_float4(st.z[0], st.z[1], st.z[2], st.z[3]);
-}
-
-// z in bf16 into rows row0 + {0, 4, 8, 12} of a Tile<DK> (lanes with
-// lane % 16 in {0, 4, 8, 12} write four key dimensions of one row each).
-template <int DK, int DV>
-__device__ __forceinline__ void state8_z_to_lds(const State8<DK, DV> &st, uint16_t *tile, int row0, int w, int lane) {
-    using S = State8<DK, DV>;
-    const int l16 = lane & 15;
-    if (S::has_z(w) && (l16 & 3) == 0) {
-        uint2 u;
-        u.x = pack_bf16x2(st.z[0], st.z[1]);
-        u.y = pack_bf16x2(st.z[2], st.z[3]);
-        *reinterpret_cast<uint2 *>(tile + Tile<DK>::off(row0 + l16, S::z_dk(w, lane))) = u;
-    }
+    const float zv = z && S::has_z(w) ? z[S::z_dk(w, lane)] : 0.f;
+    st.z = f32x4{zv, zv, zv, zv};
 }
 
 template <int DK, int DV>
@@ -178,12 +178,26 @@ __device__ __forceinline__ void state8_store(const State8<DK, DV> &st, float *s,
 #pragma unroll
     for (int mi = 0; mi < S::MTW; ++mi) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int dk = 16 * (mt0 + mi) + 4 * g + i;
+        for (int ni = 0; ni < S::NTW; ++ni) {
+            float *p = s + (size_t)(16 * (mt0 + mi) + l16) * DV + 16 * (nt0 + ni) + 4 * g;
 #pragma unroll
-            for (int ni = 0; ni < S::NTW; ++ni) s[dk * DV + 16 * (nt0 + ni) + l16] = st.s[mi][ni][i];
+            for (int i = 0; i < 4; ++i) p[i] = st.s[mi][ni][i];
         }
     }
+}
+
+// z of this wave's tile to z[Dk] (lanes 0..15 of the waves holding z).
+template <int DK, int DV>
+__device__ __forceinline__ void state8_store_z(const State8<DK, DV> &st, float *z, int w, int lane) {
+    using S = State8<DK, DV>;
+    if (S::has_z(w) && lane < 16) z[S::z_dk(w, lane)] = st.z[0];
+}
+
+// z in bf16 into a plain row of Dk elements (lanes 0..15 of the z waves).
+template <int DK, int DV>
+__device__ __forceinline__ void state8_z_to_lds(const State8<DK, DV> &st, uint16_t *zrow, int w, int lane) {
+    using S = State8<DK, DV>;
+    if (S::has_z(w) && lane < 16) zrow[S::z_dk(w, lane)] = (uint16_t)f32_to_bf16_bits(st.z[0]);
 }
 
 template <int DK, int DV>
@@ -197,7 +211,8 @@ __device__ __forceinline__ void state8_scale(State8<DK, DV> &st, float d) {
     st.z *= d;
 }
 
-// S += phi(K)^T V and z += phi(K)^T 1 over one chunk for this wave's tiles.
+// S += phi(K)^T V and z += phi(K)^T 1 over one chunk for this wave's tiles
+// (as S^T += V^T phi(K): the V operand supplies the rows, phi(K) the columns).
 // kt: phi(K) rows (decayed to the chunk end when gated), vt: V rows.  Rows
 // past the end of the sequence hold phi(0) in kt and zeros in vt: they add
 // nothing to S, and pad (their number times phi(0): 1 under elu + 1, 0 under
@@ -219,16 +234,17 @@ __device__ __forceinline__ void state8_update(State8<DK, DV> &st, const uint16_t
 #pragma unroll
         for (int mi = 0; mi < S::MTW; ++mi) {
 #pragma unroll
-            for (int ni = 0; ni < S::NTW; ++ni) st.s[mi][ni] = mfma16x16x32(a[mi], b[ni], st.s[mi][ni]);
-            if (mi == zmi) st.z = mfma16x16x32(a[mi], ones, st.z);
+            for (int ni = 0; ni < S::NTW; ++ni) st.s[mi][ni] = mfma16x16x32(b[ni], a[mi], st.s[mi][ni]);
+            if (mi == zmi) st.z = mfma16x16x32(ones, a[mi], st.z);
         }
     }
     st.z -= pad;
 }
 
-// bf16 S^T [dv][dk] (swizzled rows of Dk) into LDS.
+// bf16 S [dk][dv] into LDS (TileS layout): each lane writes the four values
+// dv .. dv + 3 of row dk of each of its tiles.
 template <int DK, int DV>
-__device__ __forceinline__ void state8_to_lds(const State8<DK, DV> &st, uint16_t *sSt, int w, int lane) {
+__device__ __forceinline__ void state8_to_lds(const State8<DK, DV> &st, uint16_t *sS, int w, int lane) {
     using S = State8<DK, DV>;
     const int l16 = lane & 15, g = lane >> 4, mt0 = (w >> 2) * S::MTW, nt0 = (w & 3) * S::NTW;
 #pragma unroll
@@ -238,7 +254,7 @@ __device__ __forceinline__ void state8_to_lds(const State8<DK, DV> &st, uint16_t
             uint2 u;
             u.x = pack_bf16x2(st.s[mi][ni][0], st.s[mi][ni][1]);
             u.y = pack_bf16x2(st.s[mi][ni][2], st.s[mi][ni][3]);
-            *reinterpret_cast<uint2 *>(sSt + Tile<DK>::off(16 * (nt0 + ni) + l16, 16 * (mt0 + mi) + 4 * g)) = u;
+            *reinterpret_cast<uint2 *>(sS + TileS<DV>::off(16 * (mt0 + mi) + l16, 16 * (nt0 + ni) + 4 * g)) = u;
         }
     }
 }
@@ -346,10 +362,10 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd_out8_bf16(
     __shared__ __attribute__((aligned(16))) uint16_t sK[kChunk * TK::RS];
     __shared__ __attribute__((aligned(16))) uint16_t sKs[GATED ? kChunk * TK::RS : 8];
     __shared__ __attribute__((aligned(16))) uint16_t sV[kChunk * TV::RS];
-    // S^T in bf16, then 16 more rows: z in rows Dv, Dv+4, Dv+8, Dv+12, zeros
-    // elsewhere, so one extra MFMA tile of the summary read yields phi(q).z in
-    // element 0 of every lane.
-    __shared__ __attribute__((aligned(16))) uint16_t sSt[(DV + 16) * TK::RS];
+    // S in bf16 (TileS, rows dk), and z in bf16 as one row that every lane of
+    // the denominator tile reads (a broadcast), so that tile holds phi(q).z.
+    __shared__ __attribute__((aligned(16))) uint16_t sS[DK * DV];
+    __shared__ __attribute__((aligned(16))) uint16_t sZr[DK];
     // gated: the chunk's inclusive gate prefix (log2 sum, zero count) per token
     __shared__ __attribute__((aligned(16))) float sGl[GATED ? kChunk : 4];
     __shared__ __attribute__((aligned(16))) int sGz[GATED ? kChunk : 4];
@@ -376,22 +392,22 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd_out8_bf16(
         const float *s0 = start ? start + bh * start_stride_bh + seg * start_stride_seg : nullptr;
         const float *z0 = start_z ? start_z + bh * start_z_stride_bh + seg * start_stride_seg : nullptr;
         state8_load<DK, DV>(st, s0, z0, w, lane);
-        for (int e = tid; e < 16 * TK::RS; e += kThreads8) sSt[DV * TK::RS + e] = 0;
-        __syncthreads();
-        state8_z_to_lds<DK, DV>(st, sSt, DV, w, lane);
+        state8_z_to_lds<DK, DV>(st, sZr, w, lane);
     }
-    state8_to_lds<DK, DV>(st, sSt, w, lane);
+    state8_to_lds<DK, DV>(st, sS, w, lane);
 
-    // K, V (and gates) are loaded two chunks ahead (one with gates, where the
-    // decay bookkeeping needs the registers), Q one chunk ahead.
-    constexpr int DEPTH = 2;
+    auto rows_in = [&](int c) { return min(kChunk, t_end - t_begin - c * kChunk); };
+
+    // K, V (and gates) are loaded two chunks ahead without gates and one with
+    // them (where the decay bookkeeping needs the registers), Q one chunk ahead;
+    // each buffer is refilled as soon as it is staged.
+    constexpr int DEPTH = GATED ? 1 : 2;
     struct Buf {
         Units<DK> k;
         Units<DV> v;
         float a;
     };
     Units<DK> qbuf;
-    auto rows_in = [&](int c) { return min(kChunk, t_end - t_begin - c * kChunk); };
     auto issue = [&](Buf &b, int c) {
         const int nv = rows_in(c);
         b.k.load(kbp + (size_t)c * kChunk * DK, nv, tid);
@@ -435,7 +451,6 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd_out8_bf16(
         if (c + 1 < nch) qbuf.load(qbp + (size_t)(c + 1) * kChunk * DK, rows_in(c + 1), tid);
         if (c + DEPTH < nch) issue(b, c + DEPTH);
         __syncthreads();
-
         // ---- phi(Q) operands of this wave's query block
         bf16x8 qa[KS];
 #pragma unroll
@@ -485,22 +500,24 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd_out8_bf16(
         }
 
         // ---- summary read: O^T = S^T phi(Q)^T for this wave's value columns
+        // (S^T rows in the permuted value order, read transposed from S)
         f32x4 oacc[NTO];
 #pragma unroll
         for (int j = 0; j < NTO; ++j) {
             oacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const int dvr = perm_dv(dh * NTO + j, l16);
+            const int nt = dh * NTO + j;
+            const int colq = 32 * (nt >> 1) + 8 * qd + 4 * (nt & 1);
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(sSt + TK::off(dvr, 32 * ks + 8 * g));
-                oacc[j] = mfma16x16x32(a, qa[ks], oacc[j]);
+                const int klo = 32 * ks + 8 * g;
+                oacc[j] = mfma16x16x32(tr_operand_in<TileS<DV>>(sS, klo, klo + 4, colq, lane), qa[ks], oacc[j]);
             }
         }
-        // denominator tile: phi(q).z from the z rows (element 0 of every lane)
+        // denominator tile: every A row is z, so every element is phi(q).z
         f32x4 dt = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(sSt + TK::off(DV + l16, 32 * ks + 8 * g));
+            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(sZr + 32 * ks + 8 * g);
             dt = mfma16x16x32(a, qa[ks], dt);
         }
         if (GATED) {
@@ -548,13 +565,13 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd_out8_bf16(
             }
         }
 
-        // ---- carry the state across the chunk
+        // ---- carry the state across the chunk, stage S (and z) for the next
         if (GATED) state8_scale<DK, DV>(st, dC);
         state8_update<DK, DV>(st, GATED ? sKs : sK, sV, w, lane, ones, phi_mode ? 0.f : (float)(kChunk - valid));
         __syncthreads();
         if (c + 1 < nch) {
-            state8_z_to_lds<DK, DV>(st, sSt, DV, w, lane);
-            state8_to_lds<DK, DV>(st, sSt, w, lane);
+            state8_z_to_lds<DK, DV>(st, sZr, w, lane);
+            state8_to_lds<DK, DV>(st, sS, w, lane);
         }
     };
 
