@@ -375,7 +375,7 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd_out8_bf16(
     const int l16 = lane & 15, g = lane >> 4, qd = lane & 3;
     // Query block per wave: waves w and w + 4 share a SIMD, so blocks (0, 3) and
     // (1, 2) -- light and heavy ends of the causal triangle -- are paired.
-    const int qblk = w < 4 ? (w >> 1) : 5 - (w >> 1), dh = w & 1;
+    const int qblk_w = w < 4 ? (w >> 1) : 5 - (w >> 1), dh = w & 1;
     const bf16x8 ones = bf16_ones8();
     const int t_begin = seg * seg_len;
     const int t_end = min(N, t_begin + seg_len);
@@ -451,118 +451,132 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd_out8_bf16(
         if (c + 1 < nch) qbuf.load(qbp + (size_t)(c + 1) * kChunk * DK, rows_in(c + 1), tid);
         if (c + DEPTH < nch) issue(b, c + DEPTH);
         __syncthreads();
-        // ---- phi(Q) operands of this wave's query block
-        bf16x8 qa[KS];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            qa[ks] = *reinterpret_cast<const bf16x8 *>(sQ + TK::off(16 * qblk + l16, 32 * ks + 8 * g));
+        // The chunk's matrix work is specialized on the wave's query block, so
+        // the causal triangle (which key blocks are scored, which one is
+        // masked) is fixed at compile time: no per-block branches and no
+        // zero-filled skipped tiles.
+        auto chunk_work = [&](auto qblk_c) {
+            constexpr int qblk = decltype(qblk_c)::value;
+            // ---- phi(Q) operands of this wave's query block
+            bf16x8 qa[KS];
+    #pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                qa[ks] = *reinterpret_cast<const bf16x8 *>(sQ + TK::off(16 * qblk + l16, 32 * ks + 8 * g));
 
-        // ---- scores A^T[key][query], key blocks 0..qblk
-        f32x4 sc[4];
-#pragma unroll
-        for (int kb4 = 0; kb4 < 4; ++kb4) {
-            sc[kb4] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (kb4 <= qblk) {
-#pragma unroll
+            // ---- scores A^T[key][query], key blocks 0..qblk
+            f32x4 sc[4];
+    #pragma unroll
+            for (int kb4 = 0; kb4 < 4; ++kb4) {
+                sc[kb4] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (kb4 <= qblk) {
+    #pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) {
+                        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(sK + TK::off(16 * kb4 + l16, 32 * ks + 8 * g));
+                        sc[kb4] = mfma16x16x32(a, qa[ks], sc[kb4]);
+                    }
+                }
+            }
+            const int tq = 16 * qblk + l16;
+            float lq = 0.f;
+            int zq = 0;
+            if (GATED) {
+                lq = sGl[tq];
+                zq = sGz[tq];
+            }
+    #pragma unroll
+            for (int kb4 = 0; kb4 < 4; ++kb4) {
+                if (kb4 <= qblk) {
+                    float4 lk = make_float4(0.f, 0.f, 0.f, 0.f);
+                    int4 zk = make_int4(0, 0, 0, 0);
+                    if (GATED) {
+                        lk = *reinterpret_cast<const float4 *>(sGl + 16 * kb4 + 4 * g);
+                        zk = *reinterpret_cast<const int4 *>(sGz + 16 * kb4 + 4 * g);
+                    }
+                    const float lka[4] = {lk.x, lk.y, lk.z, lk.w};
+                    const int zka[4] = {zk.x, zk.y, zk.z, zk.w};
+    #pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int tk = 16 * kb4 + 4 * g + i;
+                        float s = sc[kb4][i];
+                        if (kb4 == qblk && tk > tq) s = 0.f;
+                        if (GATED) s *= decay_between(lq, zq, lka[i], zka[i]);
+                        sc[kb4][i] = s;
+                    }
+                }
+            }
+
+            // ---- summary read: O^T = S^T phi(Q)^T for this wave's value columns
+            // (S^T rows in the permuted value order, read transposed from S)
+            f32x4 oacc[NTO];
+    #pragma unroll
+            for (int j = 0; j < NTO; ++j) {
+                oacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+                const int nt = dh * NTO + j;
+                const int colq = 32 * (nt >> 1) + 8 * qd + 4 * (nt & 1);
+    #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(sK + TK::off(16 * kb4 + l16, 32 * ks + 8 * g));
-                    sc[kb4] = mfma16x16x32(a, qa[ks], sc[kb4]);
+                    const int klo = 32 * ks + 8 * g;
+                    oacc[j] = mfma16x16x32(tr_operand_in<TileS<DV>>(sS, klo, klo + 4, colq, lane), qa[ks], oacc[j]);
                 }
             }
-        }
-        const int tq = 16 * qblk + l16;
-        float lq = 0.f;
-        int zq = 0;
-        if (GATED) {
-            lq = sGl[tq];
-            zq = sGz[tq];
-        }
-#pragma unroll
-        for (int kb4 = 0; kb4 < 4; ++kb4) {
-            if (kb4 <= qblk) {
-                float4 lk = make_float4(0.f, 0.f, 0.f, 0.f);
-                int4 zk = make_int4(0, 0, 0, 0);
-                if (GATED) {
-                    lk = *reinterpret_cast<const float4 *>(sGl + 16 * kb4 + 4 * g);
-                    zk = *reinterpret_cast<const int4 *>(sGz + 16 * kb4 + 4 * g);
-                }
-                const float lka[4] = {lk.x, lk.y, lk.z, lk.w};
-                const int zka[4] = {zk.x, zk.y, zk.z, zk.w};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int tk = 16 * kb4 + 4 * g + i;
-                    float s = sc[kb4][i];
-                    if (kb4 == qblk && tk > tq) s = 0.f;
-                    if (GATED) s *= decay_between(lq, zq, lka[i], zka[i]);
-                    sc[kb4][i] = s;
-                }
-            }
-        }
-
-        // ---- summary read: O^T = S^T phi(Q)^T for this wave's value columns
-        // (S^T rows in the permuted value order, read transposed from S)
-        f32x4 oacc[NTO];
-#pragma unroll
-        for (int j = 0; j < NTO; ++j) {
-            oacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const int nt = dh * NTO + j;
-            const int colq = 32 * (nt >> 1) + 8 * qd + 4 * (nt & 1);
-#pragma unroll
+            // denominator tile: every A row is z, so every element is phi(q).z
+            f32x4 dt = {0.f, 0.f, 0.f, 0.f};
+    #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const int klo = 32 * ks + 8 * g;
-                oacc[j] = mfma16x16x32(tr_operand_in<TileS<DV>>(sS, klo, klo + 4, colq, lane), qa[ks], oacc[j]);
+                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(sZr + 32 * ks + 8 * g);
+                dt = mfma16x16x32(a, qa[ks], dt);
             }
-        }
-        // denominator tile: every A row is z, so every element is phi(q).z
-        f32x4 dt = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(sZr + 32 * ks + 8 * g);
-            dt = mfma16x16x32(a, qa[ks], dt);
-        }
-        if (GATED) {
-            const float dq = decay_between(lq, zq, 0.f, 0);
-            dt *= dq;
-#pragma unroll
-            for (int j = 0; j < NTO; ++j) oacc[j] *= dq;
-        }
+            if (GATED) {
+                const float dq = decay_between(lq, zq, 0.f, 0);
+                dt *= dq;
+    #pragma unroll
+                for (int j = 0; j < NTO; ++j) oacc[j] *= dq;
+            }
 
-        // ---- in-chunk part: O^T += V^T A^T (keys permuted within 32-key steps)
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-            if (2 * s2 <= qblk) {
-                uint4 bu;
-                bu.x = pack_bf16x2(sc[2 * s2][0], sc[2 * s2][1]);
-                bu.y = pack_bf16x2(sc[2 * s2][2], sc[2 * s2][3]);
-                bu.z = pack_bf16x2(sc[2 * s2 + 1][0], sc[2 * s2 + 1][1]);
-                bu.w = pack_bf16x2(sc[2 * s2 + 1][2], sc[2 * s2 + 1][3]);
-                const bf16x8 bop = as_bf16x8(bu);
-                // row sums of the scores into the denominator tile
-                dt = mfma16x16x32(ones, bop, dt);
-                const int klo = 32 * s2 + 4 * g, khi = klo + 16;
-#pragma unroll
-                for (int j = 0; j < NTO; ++j) {
-                    const int nt = dh * NTO + j;
-                    const int colq = 32 * (nt >> 1) + 8 * qd + 4 * (nt & 1);
-                    oacc[j] = mfma16x16x32(tr_operand<DV>(sV, klo, khi, colq, lane), bop, oacc[j]);
+            // ---- in-chunk part: O^T += V^T A^T (keys permuted within 32-key steps)
+    #pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                if (2 * s2 <= qblk) {
+                    uint4 bu;
+                    bu.x = pack_bf16x2(sc[2 * s2][0], sc[2 * s2][1]);
+                    bu.y = pack_bf16x2(sc[2 * s2][2], sc[2 * s2][3]);
+                    bu.z = pack_bf16x2(sc[2 * s2 + 1][0], sc[2 * s2 + 1][1]);
+                    bu.w = pack_bf16x2(sc[2 * s2 + 1][2], sc[2 * s2 + 1][3]);
+                    const bf16x8 bop = as_bf16x8(bu);
+                    // row sums of the scores into the denominator tile
+                    dt = mfma16x16x32(ones, bop, dt);
+                    const int klo = 32 * s2 + 4 * g, khi = klo + 16;
+    #pragma unroll
+                    for (int j = 0; j < NTO; ++j) {
+                        const int nt = dh * NTO + j;
+                        const int colq = 32 * (nt >> 1) + 8 * qd + 4 * (nt & 1);
+                        oacc[j] = mfma16x16x32(tr_operand<DV>(sV, klo, khi, colq, lane), bop, oacc[j]);
+                    }
                 }
             }
-        }
 
-        // ---- normalize and store: 16 rows x this wave's half of Dv
-        if (tq < valid) {
-            const float inv = __builtin_amdgcn_rcpf(dt[0] + eps); // 1 ulp; the result is rounded to bf16
-            uint16_t *orow = obp + ((size_t)c * kChunk + tq) * DV;
-#pragma unroll
-            for (int pp = 0; pp < NTO / 2; ++pp) {
-                const int p = dh * (NTO / 2) + pp;
-                uint4 u;
-                u.x = pack_bf16x2(oacc[2 * pp][0] * inv, oacc[2 * pp][1] * inv);
-                u.y = pack_bf16x2(oacc[2 * pp][2] * inv, oacc[2 * pp][3] * inv);
-                u.z = pack_bf16x2(oacc[2 * pp + 1][0] * inv, oacc[2 * pp + 1][1] * inv);
-                u.w = pack_bf16x2(oacc[2 * pp + 1][2] * inv, oacc[2 * pp + 1][3] * inv);
-                *reinterpret_cast<uint4 *>(orow + 32 * p + 8 * g) = u;
+            // ---- normalize and store: 16 rows x this wave's half of Dv
+            if (tq < valid) {
+                const float inv = __builtin_amdgcn_rcpf(dt[0] + eps); // 1 ulp; the result is rounded to bf16
+                uint16_t *orow = obp + ((size_t)c * kChunk + tq) * DV;
+    #pragma unroll
+                for (int pp = 0; pp < NTO / 2; ++pp) {
+                    const int p = dh * (NTO / 2) + pp;
+                    uint4 u;
+                    u.x = pack_bf16x2(oacc[2 * pp][0] * inv, oacc[2 * pp][1] * inv);
+                    u.y = pack_bf16x2(oacc[2 * pp][2] * inv, oacc[2 * pp][3] * inv);
+                    u.z = pack_bf16x2(oacc[2 * pp + 1][0] * inv, oacc[2 * pp + 1][1] * inv);
+                    u.w = pack_bf16x2(oacc[2 * pp + 1][2] * inv, oacc[2 * pp + 1][3] * inv);
+                    *reinterpret_cast<uint4 *>(orow + 32 * p + 8 * g) = u;
+                }
             }
+
+        };
+        switch (qblk_w) {
+        case 0: chunk_work(std::integral_constant<int, 0>{}); break;
+        case 1: chunk_work(std::integral_constant<int, 1>{}); break;
+        case 2: chunk_work(std::integral_constant<int, 2>{}); break;
+        default: chunk_work(std::integral_constant<int, 3>{}); break;
         }
 
         // ---- carry the state across the chunk, stage S (and z) for the next
