@@ -597,13 +597,31 @@ __global__ __launch_bounds__(kThreads, 2) void noncausal_apply_bf16(const uint16
     __syncthreads();
     const int c0 = blk * chunks_per_block;
     const int c1 = min((N + kChunk - 1) / kChunk, c0 + chunks_per_block);
-    QueryRows<DK> qr;
-    for (int c = c0; c < c1; ++c) {
-        const int valid = min(kChunk, N - c * kChunk);
-        const uint16_t *qb = q + ((size_t)bh * N + (size_t)c * kChunk) * DK;
-        qr.load(qb, valid, w, lane);
+    const int t = 16 * w + l16; // this lane's query row within a chunk
+    const uint16_t *qh = q + (size_t)bh * N * DK;
+    // The next chunk's Q rows are loaded while this one is computed.  The loads
+    // are bounded to the chunk's valid rows (rows past the end read as zero and
+    // their outputs are not stored); past the block's last chunk the range is
+    // empty, so the loop needs no branch around them.
+    auto rows_in = [&](int c) { return c < c1 ? min(kChunk, N - c * kChunk) : 0; };
+    auto qload = [&](uint4 (&r)[L::KS], int c) {
+        const rsrc_t rs = chunk_rsrc(qh + (size_t)c * kChunk * DK, rows_in(c) * DK * 2);
+#pragma unroll
+        for (int ks = 0; ks < L::KS; ++ks) r[ks] = buffer_load16<true>(rs, (t * DK + 32 * ks + 8 * g) * 2);
+    };
+    auto process = [&](const uint4 (&r)[L::KS], int c) {
+        const int valid = rows_in(c);
         bf16x8 qa[L::KS];
-        qr.to_operands(qa, valid, w, lane, phi_mode);
+#pragma unroll
+        for (int ks = 0; ks < L::KS; ++ks) {
+            const uint32_t w4[4] = {r[ks].x, r[ks].y, r[ks].z, r[ks].w};
+            uint4 o4;
+            uint32_t *ow = reinterpret_cast<uint32_t *>(&o4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                ow[e] = pack_bf16x2(phi_fast(bf_lo(w4[e]), phi_mode), phi_fast(bf_hi(w4[e]), phi_mode));
+            qa[ks] = as_bf16x8(o4);
+        }
         f32x4 oacc[L::NT];
 #pragma unroll
         for (int nt = 0; nt < L::NT; ++nt) {
@@ -625,10 +643,9 @@ __global__ __launch_bounds__(kThreads, 2) void noncausal_apply_bf16(const uint16
             den += bf_lo(u.z) * z1.x + bf_hi(u.z) * z1.y + bf_lo(u.w) * z1.z + bf_hi(u.w) * z1.w;
         }
         den = sum_over_groups(den);
-        const int tq = 16 * w + l16;
-        if (tq < valid) {
+        if (t < valid) {
             const float inv = __builtin_amdgcn_rcpf(den + eps); // 1 ulp; the result is rounded to bf16
-            uint16_t *orow = o + ((size_t)bh * N + (size_t)c * kChunk + tq) * DV;
+            uint16_t *orow = o + ((size_t)bh * N + (size_t)c * kChunk + t) * DV;
 #pragma unroll
             for (int p = 0; p < DV / 32; ++p) {
                 uint4 u;
@@ -639,6 +656,15 @@ __global__ __launch_bounds__(kThreads, 2) void noncausal_apply_bf16(const uint16
                 *reinterpret_cast<uint4 *>(orow + 32 * p + 8 * g) = u;
             }
         }
+    };
+    uint4 r0[L::KS], r1[L::KS];
+    qload(r0, c0);
+    for (int c = c0; c < c1; c += 2) {
+        qload(r1, c + 1);
+        process(r0, c);
+        if (c + 1 >= c1) break;
+        qload(r0, c + 2);
+        process(r1, c + 1);
     }
 }
 
