@@ -10,7 +10,7 @@ Three independent routes to the same quantities live here:
 
 * ``forward`` / ``forward_gated`` / ``noncausal`` / ``decode_step`` call the
   plain per-token recurrence in ``linattn_oracle.c`` (fp64, one token at a
-  time, OpenMP over (batch, head) pairs only).
+  time, OpenMP over (batch, head) pairs only); ``backward`` calls its adjoint.
 * ``quadratic_forward`` (in ``quadratic.py``) is the masked N x N form written
   with NumPy, for tiny inputs.
 * ``state_from_prefix`` sums the outer products with a library matrix product
@@ -30,7 +30,7 @@ import threading
 
 import numpy as np
 
-from .quadratic import quadratic_forward  # noqa: F401
+from .quadratic import quadratic_backward, quadratic_forward  # noqa: F401
 
 PHI_ELU1 = 0
 PHI_IDENTITY = 1
@@ -69,6 +69,8 @@ def _load():
             lib.oracle_noncausal.restype = i32
             lib.oracle_decode_step.argtypes = [P] * 7 + [i64, i32, i32, i32, f64, i32]
             lib.oracle_decode_step.restype = i32
+            lib.oracle_backward.argtypes = [P] * 12 + [i64, i64, i32, i32, i32, f64, i32]
+            lib.oracle_backward.restype = i32
             lib.oracle_phi.argtypes = [P, P, i64, i32]
             lib.oracle_phi.restype = None
             _lib = lib
@@ -164,6 +166,32 @@ def decode_step(q, k, v, s, z, *, alpha=None, eps=1e-6, phi_mode=PHI_ELU1, nthre
     if rc != 0:
         raise RuntimeError("oracle_decode_step failed")
     return o, s, z
+
+
+def backward(q, k, v, dout, s_init=None, z_init=None, *, alpha=None, eps=1e-6, phi_mode=PHI_ELU1,
+             nthreads=None):
+    """Gradients of a loss L through the causal forward, given dout = dL/dO.
+
+    Returns (dq, dk, dv, ds_init, dz_init) in fp64; the gates ``alpha`` are
+    constants.  The adjoint of the per-token recurrence in ``linattn_oracle.c``.
+    """
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, H, N, Dk = q.shape
+    Dv = v.shape[-1]
+    assert k.shape == (B, H, N, Dk) and v.shape == (B, H, N, Dv) and dout.shape == (B, H, N, Dv)
+    a = _f64(alpha)
+    si, zi = _f64(s_init), _f64(z_init)
+    dq = np.empty((B, H, N, Dk))
+    dk = np.empty((B, H, N, Dk))
+    dv = np.empty((B, H, N, Dv))
+    ds = np.empty((B, H, Dk, Dv))
+    dz = np.empty((B, H, Dk))
+    rc = _load().oracle_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(si), _ptr(zi), _ptr(dout),
+                                 _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ds), _ptr(dz), B * H, N, Dk, Dv,
+                                 phi_mode, float(eps), nthreads or _threads(B * H))
+    if rc != 0:
+        raise RuntimeError("oracle_backward failed")
+    return dq, dk, dv, ds, dz
 
 
 def state_from_prefix(k, v, phi_mode=PHI_ELU1):

@@ -26,7 +26,8 @@
  *             state-space-models page, section 3).
  *
  * The read uses the state *after* token t was added, so token t's own key and
- * value take part in o_t (inclusive diagonal).  eps is added after the dot
+ * value take part in o_t (inclusive diagonal).  oracle_backward is the adjoint
+ * of the same recurrence (the gradients of a loss L given dL/dO).  eps is added after the dot
  * product.  parity pinned: see tests/test_oracle.py.
  *
  * Layout (row-major, contiguous, one (batch, head) pair after another):
@@ -227,6 +228,156 @@ int oracle_decode_step(const double *q, const double *k, const double *v,
 }
 
 /* The feature map alone, elementwise, for the closed-form pins. */
+/* Derivative of phi: 1 on x >= 0 and exp(x) on x < 0 for elu + 1 (elu's
+ * derivative, the +1 offset drops out); 1 everywhere for the identity map. */
+static double dphi(double x, int mode)
+{
+    if (mode == PHI_IDENTITY)
+        return 1.0;
+    return (x >= 0.0) ? 1.0 : exp(x);
+}
+
+/* Backward of the causal forward for one (batch, head) pair: given
+ * dout = dL/dO, the gradients of L with respect to q, k, v and the initial
+ * state.  The gates (alpha == NULL means a_t = 1) are constants here.
+ *
+ * It is the adjoint of the recurrence above, written out from its definition:
+ *   forward in time, with num_t = phi(q_t)^T S_t, den_t = phi(q_t)^T z_t + eps,
+ *     dy_t  = dout_t / den_t                 (dL/dnum_t)
+ *     dd_t  = -(dout_t . o_t) / den_t        (dL/dden_t)
+ *     dq_t  = (S_t dy_t + dd_t z_t) * phi'(q_t)
+ *   backward in time, with G_t = dL/dS_t and g_t = dL/dz_t over all later reads,
+ *     G_t   = a_{t+1} G_{t+1} + phi(q_t) dy_t^T
+ *     g_t   = a_{t+1} g_{t+1} + dd_t phi(q_t)
+ *     dk_t  = (G_t v_t + g_t) * phi'(k_t)
+ *     dv_t  = G_t^T phi(k_t)
+ *   and the initial state enters S_0 with factor a_0:
+ *     ds_init = a_0 G_0,  dz_init = a_0 g_0. */
+static void backward_one(const double *q, const double *k, const double *v,
+                         const double *alpha, const double *s_init,
+                         const double *z_init, const double *dout, double *dq,
+                         double *dk, double *dv, double *ds_init,
+                         double *dz_init, int64_t N, int Dk, int Dv, int mode,
+                         double eps, double *s, double *z, double *dy,
+                         double *dd, double *fq, double *fk, double *num)
+{
+    /* forward sweep */
+    for (int i = 0; i < Dk; ++i) {
+        z[i] = z_init ? z_init[i] : 0.0;
+        for (int j = 0; j < Dv; ++j)
+            s[(int64_t)i * Dv + j] = s_init ? s_init[(int64_t)i * Dv + j] : 0.0;
+    }
+    for (int64_t t = 0; t < N; ++t) {
+        const double *qt = q + t * Dk, *kt = k + t * Dk, *vt = v + t * Dv;
+        const double *go = dout + t * Dv;
+        for (int i = 0; i < Dk; ++i) {
+            fq[i] = phi(qt[i], mode);
+            fk[i] = phi(kt[i], mode);
+        }
+        const double a = alpha ? alpha[t] : 1.0;
+        for (int i = 0; i < Dk; ++i) {
+            z[i] = a * z[i] + fk[i];
+            for (int j = 0; j < Dv; ++j)
+                s[(int64_t)i * Dv + j] = a * s[(int64_t)i * Dv + j] + fk[i] * vt[j];
+        }
+        double den = eps;
+        for (int j = 0; j < Dv; ++j)
+            num[j] = 0.0;
+        for (int i = 0; i < Dk; ++i) {
+            den += fq[i] * z[i];
+            for (int j = 0; j < Dv; ++j)
+                num[j] += fq[i] * s[(int64_t)i * Dv + j];
+        }
+        double go_dot_o = 0.0;
+        for (int j = 0; j < Dv; ++j) {
+            dy[t * Dv + j] = go[j] / den;
+            go_dot_o += go[j] * (num[j] / den);
+        }
+        dd[t] = -go_dot_o / den;
+        for (int i = 0; i < Dk; ++i) {
+            double acc = dd[t] * z[i];
+            for (int j = 0; j < Dv; ++j)
+                acc += s[(int64_t)i * Dv + j] * dy[t * Dv + j];
+            dq[t * Dk + i] = acc * dphi(qt[i], mode);
+        }
+    }
+    /* backward sweep: s, z now hold G and g */
+    memset(s, 0, sizeof(double) * (size_t)Dk * Dv);
+    memset(z, 0, sizeof(double) * (size_t)Dk);
+    double a_next = 1.0;
+    for (int64_t t = N - 1; t >= 0; --t) {
+        const double *qt = q + t * Dk, *kt = k + t * Dk, *vt = v + t * Dv;
+        for (int i = 0; i < Dk; ++i) {
+            fq[i] = phi(qt[i], mode);
+            fk[i] = phi(kt[i], mode);
+        }
+        for (int i = 0; i < Dk; ++i) {
+            z[i] = a_next * z[i] + dd[t] * fq[i];
+            for (int j = 0; j < Dv; ++j)
+                s[(int64_t)i * Dv + j] = a_next * s[(int64_t)i * Dv + j] + fq[i] * dy[t * Dv + j];
+        }
+        for (int i = 0; i < Dk; ++i) {
+            double acc = z[i];
+            for (int j = 0; j < Dv; ++j)
+                acc += s[(int64_t)i * Dv + j] * vt[j];
+            dk[t * Dk + i] = acc * dphi(kt[i], mode);
+        }
+        for (int j = 0; j < Dv; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < Dk; ++i)
+                acc += s[(int64_t)i * Dv + j] * fk[i];
+            dv[t * Dv + j] = acc;
+        }
+        a_next = alpha ? alpha[t] : 1.0;
+    }
+    if (ds_init)
+        for (int64_t e = 0; e < (int64_t)Dk * Dv; ++e)
+            ds_init[e] = a_next * s[e];
+    if (dz_init)
+        for (int i = 0; i < Dk; ++i)
+            dz_init[i] = a_next * z[i];
+}
+
+/* Backward over BH (batch, head) pairs; see backward_one.  alpha, s_init,
+ * z_init, ds_init, dz_init may be NULL.  Returns 0, or -1 on a bad argument /
+ * allocation failure. */
+int oracle_backward(const double *q, const double *k, const double *v,
+                    const double *alpha, const double *s_init,
+                    const double *z_init, const double *dout, double *dq,
+                    double *dk, double *dv, double *ds_init, double *dz_init,
+                    int64_t BH, int64_t N, int Dk, int Dv, int mode, double eps,
+                    int nthreads)
+{
+    if (!q || !k || !v || !dout || !dq || !dk || !dv || BH < 0 || N < 0 || Dk < 1 || Dv < 1)
+        return -1;
+    int err = 0;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads > 0 ? nthreads : 1)
+    for (int64_t bh = 0; bh < BH; ++bh) {
+        double *s = malloc(sizeof(double) * (size_t)Dk * Dv);
+        double *z = malloc(sizeof(double) * (size_t)Dk);
+        double *dy = malloc(sizeof(double) * (size_t)(N > 0 ? N : 1) * Dv);
+        double *dd = malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+        double *fq = malloc(sizeof(double) * Dk);
+        double *fk = malloc(sizeof(double) * Dk);
+        double *num = malloc(sizeof(double) * Dv);
+        if (!s || !z || !dy || !dd || !fq || !fk || !num) {
+#pragma omp atomic write
+            err = 1;
+        } else {
+            backward_one(q + bh * N * Dk, k + bh * N * Dk, v + bh * N * Dv,
+                         alpha ? alpha + bh * N : NULL,
+                         s_init ? s_init + bh * Dk * Dv : NULL,
+                         z_init ? z_init + bh * Dk : NULL, dout + bh * N * Dv,
+                         dq + bh * N * Dk, dk + bh * N * Dk, dv + bh * N * Dv,
+                         ds_init ? ds_init + bh * Dk * Dv : NULL,
+                         dz_init ? dz_init + bh * Dk : NULL, N, Dk, Dv, mode,
+                         eps, s, z, dy, dd, fq, fk, num);
+        }
+        free(s); free(z); free(dy); free(dd); free(fq); free(fk); free(num);
+    }
+    return err ? -1 : 0;
+}
+
 void oracle_phi(const double *x, double *y, int64_t n, int mode)
 {
     for (int64_t i = 0; i < n; ++i)

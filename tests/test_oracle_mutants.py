@@ -26,11 +26,22 @@ MUTANTS = {
     "gate_index_shifted": ("double a = alpha[t];", "double a = alpha[t > 0 ? t - 1 : 0];"),
     "value_scaled_by_query": ("s[(int64_t)i * Dv + j] += fk[i] * vt[j];", "s[(int64_t)i * Dv + j] += fq[i] * vt[j];"),
 }
+# Mistakes in the backward (the adjoint), caught by its own pins.
+BACKWARD_MUTANTS = {
+    "bwd_dd_sign": ("dd[t] = -go_dot_o / den;", "dd[t] = go_dot_o / den;"),
+    "bwd_dphi_is_one": ("return (x >= 0.0) ? 1.0 : exp(x);", "return 1.0;"),
+    "bwd_g_not_decayed": ("z[i] = a_next * z[i] + dd[t] * fq[i];", "z[i] = z[i] + dd[t] * fq[i];"),
+    "bwd_dv_uses_query": ("acc += s[(int64_t)i * Dv + j] * fk[i];", "acc += s[(int64_t)i * Dv + j] * fq[i];"),
+    "bwd_dq_drops_den_term": ("double acc = dd[t] * z[i];", "double acc = 0.0;"),
+    "bwd_dk_drops_den_term": ("double acc = z[i];", "double acc = 0.0;"),
+    "bwd_init_grad_undecayed": ("ds_init[e] = a_next * s[e];", "ds_init[e] = s[e];"),
+}
 
 
-@pytest.mark.parametrize("name", sorted(MUTANTS))
+@pytest.mark.parametrize("name", sorted(MUTANTS) + sorted(BACKWARD_MUTANTS))
 def test_mutant_is_caught(name, tmp_path):
-    old, new = MUTANTS[name]
+    old, new = MUTANTS.get(name) or BACKWARD_MUTANTS[name]
+    pins = "test_oracle_backward.py" if name in BACKWARD_MUTANTS else "test_oracle.py"
     src = open(SRC).read()
     assert src.count(old) >= 1, f"mutation site for {name} not found"
     mutated = src.replace(old, new, 1)
@@ -41,6 +52,6 @@ def test_mutant_is_caught(name, tmp_path):
                     str(csrc), "-lm"], check=True)
     env = dict(os.environ, LINATTN_ORACLE_LIB=str(lib))
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle.py")],
+                        os.path.join(ROOT, "tests", pins)],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
     assert r.returncode != 0, f"mutant {name} passed every pin:\n{r.stdout[-2000:]}"
