@@ -55,11 +55,16 @@
 extern "C" {
 #endif
 
-#define LINATTN_ABI_VERSION 1
+#define LINATTN_ABI_VERSION 2
 
 enum linattn_dtype { LINATTN_F32 = 0, LINATTN_BF16 = 1 };
 enum linattn_phi { LINATTN_PHI_ELU1 = 0, LINATTN_PHI_IDENTITY = 1 };
-enum linattn_kind { LINATTN_KIND_FORWARD = 0, LINATTN_KIND_GATED = 1, LINATTN_KIND_NONCAUSAL = 2 };
+enum linattn_kind {
+    LINATTN_KIND_FORWARD = 0,
+    LINATTN_KIND_GATED = 1,
+    LINATTN_KIND_NONCAUSAL = 2,
+    LINATTN_KIND_BACKWARD = 3
+};
 
 enum linattn_status {
     LINATTN_OK = 0,
@@ -113,6 +118,58 @@ int linattn_forward_gated(const void *q, const void *k, const void *v,
                           int B, int H, int N, int Dk, int Dv, int dtype,
                           int phi, float eps, void *workspace,
                           size_t workspace_bytes, void *hip_stream);
+
+/*
+ * Causal forward for training: linattn_forward that also keeps, for the
+ * backward, each token's denominator den_t = phi(q_t)^T z_t + eps.
+ *
+ *   den       output [B][H][N] fp32.
+ * o and den are required; den must not overlap q, k, v or o.
+ * Restricted to the chunked bf16 path: dtype LINATTN_BF16 with Dk and Dv in
+ * {64, 128} (LINATTN_ESHAPE / LINATTN_EDTYPE otherwise).  Other arguments and
+ * the workspace (kind LINATTN_KIND_FORWARD) as linattn_forward; o is
+ * identical to what linattn_forward writes.
+ */
+int linattn_forward_train(const void *q, const void *k, const void *v, void *o,
+                          float *den, const float *s_init, const float *z_init,
+                          float *s_final, float *z_final,
+                          int B, int H, int N, int Dk, int Dv, int dtype,
+                          int phi, float eps, void *workspace,
+                          size_t workspace_bytes, void *hip_stream);
+
+/*
+ * Backward of the causal forward (ungated): given dout = dL/dO for a loss L,
+ * the gradients dq, dk, dv of L.  They are the derivative of the forward's
+ * definition above (the pages give no backward formula; the quantities are
+ * those of reverse-mode differentiation of the recurrence, with
+ * dY_t = dout_t / den_t, dd_t = -(dout_t . o_t) / den_t:
+ *   dq_t = (S_t dY_t + dd_t z_t) * phi'(q_t)
+ *   dk_t = (R_t v_t + r_t) * phi'(k_t),  dv_t = R_t^T phi(k_t),
+ *   R_t = sum_{u >= t} phi(q_u) dY_u^T,  r_t = sum_{u >= t} dd_u phi(q_u)).
+ *
+ *   q, k, v   the forward's inputs; den its output from linattn_forward_train
+ *             ([B][H][N] fp32) on the same inputs and initial state.
+ *   dout      [B][H][N][Dv], dtype `dtype`.
+ *   dq, dk    outputs [B][H][N][Dk]; dv output [B][H][N][Dv]; dtype `dtype`
+ *             (bf16 round-to-nearest-even).  Must not overlap any input or
+ *             each other.
+ *   s_init,   the forward's initial state (both NULL for a zero start).  Its
+ *   z_init    gradient is not returned.
+ *   eps       the forward's eps.
+ * dY is dout / den rounded to bf16 once.  dd_t is formed from the state the
+ * backward carries, as -phi(q_t) . (S_t dY_t) / (phi(q_t) . z_t + eps),
+ * rather than from the forward's rounded o (dq is a small difference of
+ * large terms, and o's rounding would show in it).
+ * Restricted like linattn_forward_train (bf16, Dk and Dv in {64, 128}).
+ * Workspace kind LINATTN_KIND_BACKWARD (always needed: it holds dd).
+ */
+int linattn_backward(const void *q, const void *k, const void *v,
+                     const float *den, const void *dout,
+                     void *dq, void *dk, void *dv,
+                     const float *s_init, const float *z_init,
+                     int B, int H, int N, int Dk, int Dv, int dtype, int phi,
+                     float eps, void *workspace, size_t workspace_bytes,
+                     void *hip_stream);
 
 /*
  * Non-causal form: S = sum_t phi(k_t) v_t^T and z = sum_t phi(k_t) over the

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "liblinattn.so")
 
 F32, BF16 = 0, 1
 PHI_ELU1, PHI_IDENTITY = 0, 1
-KIND_FORWARD, KIND_GATED, KIND_NONCAUSAL = 0, 1, 2
+KIND_FORWARD, KIND_GATED, KIND_NONCAUSAL, KIND_BACKWARD = 0, 1, 2, 3
 
 _lib = None
 _lock = threading.Lock()
@@ -32,6 +32,8 @@ _SZ = ctypes.c_size_t
 SIGNATURES = {
     "linattn_forward": ([_P] * 8 + [_I] * 7 + [_F, _P, _SZ, _P], _I),
     "linattn_forward_gated": ([_P] * 9 + [_I] * 7 + [_F, _P, _SZ, _P], _I),
+    "linattn_forward_train": ([_P] * 9 + [_I] * 7 + [_F, _P, _SZ, _P], _I),
+    "linattn_backward": ([_P] * 10 + [_I] * 7 + [_F, _P, _SZ, _P], _I),
     "linattn_forward_noncausal": ([_P] * 6 + [_I] * 7 + [_F, _P, _SZ, _P], _I),
     "linattn_decode_step": ([_P] * 7 + [_I] * 6 + [_F, _P], _I),
     "linattn_workspace_size": ([_I] * 7, _SZ),
@@ -158,6 +160,70 @@ def _forward(gated, q, k, v, alpha, s_init, z_init, eps, phi, want_state, out, s
                                _stream(q))
     _check(rc, "linattn_forward_gated" if gated else "linattn_forward")
     return o, s_final, z_final
+
+
+def linattn_forward_train(q, k, v, s_init=None, z_init=None, *, eps=1e-6, phi=PHI_ELU1, workspace=None):
+    """Causal forward that also keeps each token's denominator -> (o, den, s_final, z_final).
+
+    bf16 with Dk, Dv in {64, 128}; den [B, H, N] fp32 feeds linattn_backward.
+    """
+    _dev(q, "q")
+    code = _dtype_code(q)
+    _dev(k, "k", q.dtype)
+    _dev(v, "v", q.dtype)
+    B, H, N, Dk = q.shape
+    Dv = v.shape[-1]
+    if tuple(k.shape) != (B, H, N, Dk) or tuple(v.shape[:3]) != (B, H, N):
+        raise ValueError("q, k, v shapes do not match")
+    if (s_init is None) != (z_init is None):
+        raise ValueError("pass both s_init and z_init or neither")
+    _dev(s_init, "s_init", torch.float32)
+    _dev(z_init, "z_init", torch.float32)
+    o = torch.empty((B, H, N, Dv), dtype=q.dtype, device=q.device)
+    den = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    s_final = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device)
+    z_final = torch.empty((B, H, Dk), dtype=torch.float32, device=q.device)
+    ws, _ = _workspace(KIND_FORWARD, B, H, N, Dk, Dv, code, q.device, workspace)
+    rc = lib().linattn_forward_train(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(den), _ptr(s_init), _ptr(z_init),
+                                     _ptr(s_final), _ptr(z_final), B, H, N, Dk, Dv, code, phi, float(eps), _ptr(ws),
+                                     ws.numel(), _stream(q))
+    _check(rc, "linattn_forward_train")
+    return o, den, s_final, z_final
+
+
+def linattn_backward(q, k, v, den, dout, s_init=None, z_init=None, *, eps=1e-6, phi=PHI_ELU1, out=None,
+                     workspace=None):
+    """Gradients of a loss through the causal forward, given dout = dL/dO -> (dq, dk, dv).
+
+    den is the output of linattn_forward_train on the same q, k, v (and
+    initial state, eps, phi).  ``out`` may pass preallocated (dq, dk, dv).
+    """
+    _dev(q, "q")
+    code = _dtype_code(q)
+    for name, t in (("k", k), ("v", v), ("dout", dout)):
+        _dev(t, name, q.dtype)
+    _dev(den, "den", torch.float32)
+    B, H, N, Dk = q.shape
+    Dv = v.shape[-1]
+    if (tuple(k.shape) != (B, H, N, Dk) or tuple(v.shape) != (B, H, N, Dv) or tuple(dout.shape) != (B, H, N, Dv)
+            or tuple(den.shape) != (B, H, N)):
+        raise ValueError("q, k, v, den, dout shapes do not match")
+    if (s_init is None) != (z_init is None):
+        raise ValueError("pass both s_init and z_init or neither")
+    _dev(s_init, "s_init", torch.float32)
+    _dev(z_init, "z_init", torch.float32)
+    if out is None:
+        out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    dq, dk, dv = out
+    _dev(dq, "dq", q.dtype)
+    _dev(dk, "dk", q.dtype)
+    _dev(dv, "dv", q.dtype)
+    ws, _ = _workspace(KIND_BACKWARD, B, H, N, Dk, Dv, code, q.device, workspace)
+    rc = lib().linattn_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(den), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                                _ptr(s_init), _ptr(z_init), B, H, N, Dk, Dv, code, phi, float(eps), _ptr(ws),
+                                ws.numel(), _stream(q))
+    _check(rc, "linattn_backward")
+    return dq, dk, dv
 
 
 def linattn_forward_noncausal(q, k, v, *, eps=1e-6, phi=PHI_ELU1, want_state=True, out=None, workspace=None):

@@ -13,6 +13,7 @@
 #include "../../include/linattn.h"
 #include "fwd_bf16.hpp"
 #include "fwd8_bf16.hpp"
+#include "bwd8_bf16.hpp"
 #include "recur.hpp"
 #include "scan_decode.hpp"
 
@@ -38,7 +39,8 @@ struct Plan {
     int sub_len = 0;  // tokens per state sub-segment
     int nvb = 1;      // 64-column value blocks (recurrence path)
     size_t E = 0;     // floats of one state (Dk * Dv + Dk)
-    size_t ws_states = 0, ws_gam = 0, ws_total = 0, ws_bytes = 0;
+    size_t Eb = 0;    // backward: a forward state cell with the column sums of V (E + Dv)
+    size_t ws_states = 0, ws_gam = 0, ws_total = 0, ws_rev = 0, ws_dd = 0, ws_bytes = 0;
 };
 
 bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
@@ -70,11 +72,17 @@ Plan make_plan(int kind, int B, int H, int N, int Dk, int Dv, int dtype) {
     p.Ps = p.P * p.R;
     p.sub_len = p.seg_len / p.R;
     p.E = (size_t)Dk * Dv + Dk;
+    p.Eb = p.E + Dv;
+    const bool backward = kind == LINATTN_KIND_BACKWARD;
     const bool need_states = kind == LINATTN_KIND_NONCAUSAL || p.P > 1;
-    if (need_states) p.ws_states = align256((size_t)BH * p.Ps * p.E * sizeof(float));
+    // the backward keeps the forward's segment states (cells of Eb floats),
+    // then the reverse sums of the later segments, then dd of every token
+    if (need_states) p.ws_states = align256((size_t)BH * p.Ps * (backward ? p.Eb : p.E) * sizeof(float));
+    if (backward && p.P > 1) p.ws_rev = align256((size_t)BH * p.Ps * p.E * sizeof(float));
+    if (backward) p.ws_dd = align256((size_t)BH * N * sizeof(float));
     if (kind == LINATTN_KIND_GATED && p.P > 1) p.ws_gam = align256((size_t)BH * p.Ps * sizeof(float));
     if (kind == LINATTN_KIND_NONCAUSAL) p.ws_total = align256((size_t)BH * p.E * sizeof(float));
-    p.ws_bytes = p.ws_states + p.ws_gam + p.ws_total;
+    p.ws_bytes = p.ws_states + p.ws_gam + p.ws_total + p.ws_rev + p.ws_dd;
     return p;
 }
 
@@ -157,8 +165,8 @@ template <typename F> void with_phi(int phi, F &&f) {
 
 template <int DK, int DV, bool GATED>
 int run_mfma_causal(const Plan &pl, const void *q, const void *k, const void *v, const float *alpha, void *o,
-                    const float *s_init, const float *z_init, float *s_final, float *z_final, int BH, int N,
-                    int phi, float eps, char *ws, hipStream_t st) {
+                    const float *s_init, const float *z_init, float *s_final, float *z_final, float *den,
+                    int BH, int N, int phi, float eps, char *ws, hipStream_t st) {
     const float *start = s_init, *start_z = z_init;
     size_t sbh = (size_t)DK * DV, sseg = 0, zbh = DK;
     if (pl.P > 1) {
@@ -177,8 +185,8 @@ int run_mfma_causal(const Plan &pl, const void *q, const void *k, const void *v,
                     (const uint16_t *)k, (const uint16_t *)v, alpha, states, gam, N, pl.Ps, P_run, pl.sub_len, phi);
         }));
         LA_TRY(launch("seg_prefix", st, [&] {
-            seg_prefix<<<dim3((unsigned)((pl.E + 255) / 256), BH), dim3(256), 0, st>>>(states, gam, s_init, z_init,
-                                                                                       pl.Ps, P_run + 1, DK, DV);
+            seg_prefix<<<dim3((unsigned)((pl.E + 255) / 256), BH), dim3(256), 0, st>>>(
+                states, gam, s_init, z_init, pl.Ps, P_run + 1, DK, DV, (int)pl.E);
         }));
         // output segment p starts from the prefix before state cell p * R
         start = states;
@@ -190,9 +198,15 @@ int run_mfma_causal(const Plan &pl, const void *q, const void *k, const void *v,
     return launch(GATED ? "fwd_out_bf16_gated" : "fwd_out_bf16", st, [&] {
         if constexpr (kEight<DK, DV>)
             with_phi(phi, [&](auto PH) {
-                fwd_out8_bf16<DK, DV, GATED, PH()><<<dim3(pl.P * BH), dim3(kThreads8), 0, st>>>(
-                    (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, alpha, (uint16_t *)o, start, sbh,
-                    sseg, start_z, zbh, s_final, z_final, N, pl.P, pl.seg_len, eps);
+                // the training forward (den given) is its own instantiation
+                if (den)
+                    fwd_out8_bf16<DK, DV, GATED, PH(), true><<<dim3(pl.P * BH), dim3(kThreads8), 0, st>>>(
+                        (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, alpha, (uint16_t *)o, start,
+                        sbh, sseg, start_z, zbh, s_final, z_final, N, pl.P, pl.seg_len, eps, den);
+                else
+                    fwd_out8_bf16<DK, DV, GATED, PH()><<<dim3(pl.P * BH), dim3(kThreads8), 0, st>>>(
+                        (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, alpha, (uint16_t *)o, start,
+                        sbh, sseg, start_z, zbh, s_final, z_final, N, pl.P, pl.seg_len, eps, nullptr);
             });
         else
             fwd_out_bf16<DK, DV, GATED><<<dim3(pl.P * BH), dim3(kThreads), 0, st>>>(
@@ -233,6 +247,81 @@ int run_mfma_noncausal(const Plan &pl, const void *q, const void *k, const void 
     });
 }
 
+// Backward (ungated, bf16, Dk and Dv in {64, 128}): the forward state at
+// segment starts (for elu + 1 as sums of elu(k) v^T, elu(k) and v), dQ (and
+// dd) forward in time, reverse segment sums, dK / dV backward in time.
+template <int DK, int DV>
+int run_mfma_backward(const Plan &pl, const void *q, const void *k, const void *v, const float *den,
+                      const void *dout, void *dq, void *dk, void *dv, const float *s_init, const float *z_init,
+                      int BH, int N, int phi, float eps, char *ws, hipStream_t st) {
+    if constexpr (!kEight<DK, DV>) {
+        return LINATTN_ESHAPE;
+    } else {
+        const uint16_t *q16 = (const uint16_t *)q, *k16 = (const uint16_t *)k, *v16 = (const uint16_t *)v;
+        const uint16_t *g16 = (const uint16_t *)dout;
+        float *dd = reinterpret_cast<float *>(ws + pl.ws_states + pl.ws_rev);
+        const float *start = s_init, *start_z = z_init, *start_vb = nullptr;
+        size_t sbh = (size_t)DK * DV, sseg = 0, zbh = DK;
+        float *rev = nullptr;
+        if (pl.P > 1) {
+            float *states = reinterpret_cast<float *>(ws);
+            rev = reinterpret_cast<float *>(ws + pl.ws_states);
+            const int P_run = (pl.P - 1) * pl.R;
+            LA_TRY(launch("seg_state_bf16", st, [&] {
+                with_phi(phi, [&](auto PH) {
+                    constexpr int FEAT = PH() == LINATTN_PHI_ELU1 ? kFeatElu : PH();
+                    seg_state8_bf16<DK, DV, false, FEAT, true><<<dim3(P_run * BH), dim3(kThreads8), 0, st>>>(
+                        k16, v16, nullptr, states, nullptr, N, pl.Ps, P_run, pl.sub_len);
+                });
+            }));
+            LA_TRY(launch("seg_prefix", st, [&] {
+                seg_prefix<<<dim3((unsigned)((pl.Eb + 255) / 256), BH), dim3(256), 0, st>>>(
+                    states, nullptr, s_init, z_init, pl.Ps, P_run + 1, DK, DV, (int)pl.Eb);
+            }));
+            start = states;
+            start_z = states + (size_t)DK * DV;
+            start_vb = states + (size_t)DK * DV + DK;
+            sbh = (size_t)pl.Ps * pl.Eb;
+            sseg = (size_t)pl.R * pl.Eb;
+            zbh = (size_t)pl.Ps * pl.Eb;
+        }
+        LA_TRY(launch("bwd_dq_bf16", st, [&] {
+            with_phi(phi, [&](auto PH) {
+                bwd_dq8_bf16<DK, DV, PH()><<<dim3(pl.P * BH), dim3(kThreads8), 0, st>>>(
+                    q16, k16, v16, den, g16, (uint16_t *)dq, dd, start, sbh, sseg, start_z, zbh, start_vb, N, pl.P,
+                    pl.seg_len, eps);
+            });
+        }));
+        if (pl.P > 1) {
+            // cell j: state sub-segment R + j (the first segment's are never needed)
+            const int cells = (pl.P - 1) * pl.R;
+            LA_TRY(launch("bwd_rstate_bf16", st, [&] {
+                with_phi(phi, [&](auto PH) {
+                    bwd_rstate8_bf16<DK, DV, PH()><<<dim3(cells * BH), dim3(kThreads8), 0, st>>>(
+                        q16, den, dd, g16, rev, N, cells, pl.Ps, pl.R, pl.sub_len);
+                });
+            }));
+            LA_TRY(launch("seg_suffix", st, [&] {
+                seg_suffix<<<dim3((unsigned)((pl.E + 255) / 256), BH), dim3(256), 0, st>>>(rev, pl.Ps, cells,
+                                                                                          (int)pl.E);
+            }));
+        }
+        // output segment p < P - 1 starts (going backward) from the sum over
+        // cells j >= p * R; the last segment starts from zero
+        return launch("bwd_dkv_bf16", st, [&] {
+            with_phi(phi, [&](auto PH) {
+                bwd_dkv8_bf16<DK, DV, PH()><<<dim3(pl.P * BH), dim3(kThreads8), 0, st>>>(
+                    q16, k16, v16, den, dd, g16, (uint16_t *)dk, (uint16_t *)dv, rev, (size_t)pl.Ps * pl.E,
+                    (size_t)pl.R * pl.E, N, pl.P, pl.seg_len);
+            });
+        });
+    }
+}
+
+template <int DK, int DV> struct MfmaBackward {
+    template <typename... A> static int run(A &&...a) { return run_mfma_backward<DK, DV>(a...); }
+};
+
 template <typename T, int DK, bool GATED>
 int run_recur_causal(const Plan &pl, const void *q, const void *k, const void *v, const float *alpha, void *o,
                      const float *s_init, const float *z_init, float *s_final, float *z_final, int BH, int N, int Dv,
@@ -252,7 +341,7 @@ int run_recur_causal(const Plan &pl, const void *q, const void *k, const void *v
         }));
         LA_TRY(launch("seg_prefix", st, [&] {
             seg_prefix<<<dim3((unsigned)((E + 255) / 256), BH), dim3(256), 0, st>>>(states, gam, s_init, z_init, pl.P,
-                                                                                    pl.P, DK, Dv);
+                                                                                    pl.P, DK, Dv, (int)E);
         }));
         start = states;
         start_z = states + (size_t)DK * Dv;
@@ -332,7 +421,7 @@ template <typename T, typename... A> int recur_noncausal_dk(int Dk, A &&...a) {
 int forward_impl(bool gated, const void *q, const void *k, const void *v, const float *alpha, void *o,
                  const float *s_init, const float *z_init, float *s_final, float *z_final, int B, int H, int N,
                  int Dk, int Dv, int dtype, int phi, float eps, void *workspace, size_t workspace_bytes,
-                 void *hip_stream) {
+                 void *hip_stream, float *den = nullptr) {
     LA_TRY(check_common(B, H, N, Dk, Dv, dtype, phi, eps));
     if (!q || !k || !v || !o || (gated && !alpha)) return LINATTN_EINVAL;
     if ((s_init == nullptr) != (z_init == nullptr)) return LINATTN_EINVAL;
@@ -348,9 +437,9 @@ int forward_impl(bool gated, const void *q, const void *k, const void *v, const 
     if (pl.mfma) {
         if (gated)
             return by_dims_mfma<MfmaCausal<true>::F>(Dk, Dv, pl, q, k, v, alpha, o, s_init, z_init, s_final, z_final,
-                                                    BH, N, phi, eps, ws, st);
-        return by_dims_mfma<MfmaCausal<false>::F>(Dk, Dv, pl, q, k, v, alpha, o, s_init, z_init, s_final, z_final, BH,
-                                                 N, phi, eps, ws, st);
+                                                    den, BH, N, phi, eps, ws, st);
+        return by_dims_mfma<MfmaCausal<false>::F>(Dk, Dv, pl, q, k, v, alpha, o, s_init, z_init, s_final, z_final,
+                                                 den, BH, N, phi, eps, ws, st);
     }
     if (dtype == LINATTN_BF16) {
         if (gated)
@@ -409,6 +498,52 @@ int linattn_forward_gated(const void *q, const void *k, const void *v, const flo
                         workspace, workspace_bytes, hip_stream);
 }
 
+// The training forward and the backward run the chunked bf16 kernels only.
+int check_train(int Dk, int Dv, int dtype) {
+    if (dtype != LINATTN_BF16) return LINATTN_EDTYPE;
+    if ((Dk != 64 && Dk != 128) || (Dv != 64 && Dv != 128)) return LINATTN_ESHAPE;
+    return LINATTN_OK;
+}
+
+int linattn_forward_train(const void *q, const void *k, const void *v, void *o, float *den, const float *s_init,
+                          const float *z_init, float *s_final, float *z_final, int B, int H, int N, int Dk, int Dv,
+                          int dtype, int phi, float eps, void *workspace, size_t workspace_bytes,
+                          void *hip_stream) {
+    LA_TRY(check_common(B, H, N, Dk, Dv, dtype, phi, eps));
+    LA_TRY(check_train(Dk, Dv, dtype));
+    if (!o || !den) return LINATTN_EINVAL;
+    const size_t nq = (size_t)B * H * N * Dk * 2, nv = (size_t)B * H * N * Dv * 2, nd = (size_t)B * H * N * 4;
+    if (overlaps(den, nd, q, nq) || overlaps(den, nd, k, nq) || overlaps(den, nd, v, nv) || overlaps(den, nd, o, nv))
+        return LINATTN_EINVAL;
+    return forward_impl(false, q, k, v, nullptr, o, s_init, z_init, s_final, z_final, B, H, N, Dk, Dv, dtype, phi,
+                        eps, workspace, workspace_bytes, hip_stream, den);
+}
+
+int linattn_backward(const void *q, const void *k, const void *v, const float *den, const void *dout, void *dq,
+                     void *dk, void *dv, const float *s_init, const float *z_init, int B, int H, int N, int Dk,
+                     int Dv, int dtype, int phi, float eps, void *workspace, size_t workspace_bytes,
+                     void *hip_stream) {
+    LA_TRY(check_common(B, H, N, Dk, Dv, dtype, phi, eps));
+    LA_TRY(check_train(Dk, Dv, dtype));
+    if (!q || !k || !v || !den || !dout || !dq || !dk || !dv) return LINATTN_EINVAL;
+    if ((s_init == nullptr) != (z_init == nullptr)) return LINATTN_EINVAL;
+    const size_t nq = (size_t)B * H * N * Dk * 2, nv = (size_t)B * H * N * Dv * 2, nd = (size_t)B * H * N * 4;
+    const void *ins[5] = {q, k, v, den, dout};
+    const size_t insz[5] = {nq, nq, nv, nd, nv};
+    void *outs[3] = {dq, dk, dv};
+    const size_t outsz[3] = {nq, nq, nv};
+    for (int a = 0; a < 3; ++a) {
+        for (int b = 0; b < 5; ++b)
+            if (overlaps(outs[a], outsz[a], ins[b], insz[b])) return LINATTN_EINVAL;
+        for (int b = a + 1; b < 3; ++b)
+            if (overlaps(outs[a], outsz[a], outs[b], outsz[b])) return LINATTN_EINVAL;
+    }
+    const Plan pl = make_plan(LINATTN_KIND_BACKWARD, B, H, N, Dk, Dv, dtype);
+    if (!workspace || workspace_bytes < pl.ws_bytes) return LINATTN_EWORKSPACE;
+    return by_dims_mfma<MfmaBackward>(Dk, Dv, pl, q, k, v, den, dout, dq, dk, dv, s_init, z_init, B * H, N, phi,
+                                      eps, (char *)workspace, (hipStream_t)hip_stream);
+}
+
 int linattn_forward_noncausal(const void *q, const void *k, const void *v, void *o, float *s_out, float *z_out,
                               int B, int H, int N, int Dk, int Dv, int dtype, int phi, float eps, void *workspace,
                               size_t workspace_bytes, void *hip_stream) {
@@ -448,7 +583,7 @@ int linattn_decode_step(const void *q, const void *k, const void *v, float *s, f
 }
 
 size_t linattn_workspace_size(int kind, int B, int H, int N, int Dk, int Dv, int dtype) {
-    if (kind < LINATTN_KIND_FORWARD || kind > LINATTN_KIND_NONCAUSAL) return 0;
+    if (kind < LINATTN_KIND_FORWARD || kind > LINATTN_KIND_BACKWARD) return 0;
     if (check_common(B, H, N, Dk, Dv, dtype, LINATTN_PHI_ELU1, 0.f) != LINATTN_OK) return 0;
     return make_plan(kind, B, H, N, Dk, Dv, dtype).ws_bytes;
 }

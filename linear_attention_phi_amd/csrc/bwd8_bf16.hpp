@@ -1,0 +1,679 @@
+// bwd8_bf16.hpp -- backward of the chunked causal linear attention (ungated),
+// eight waves per workgroup, head dims Dk, Dv in {64, 128}, bf16 in and out,
+// fp32 state.
+//
+// With dY_t = dO_t / den_t and dd_t = -(dO_t . o_t) / den_t (den_t = phi(q_t).z_t
+// + eps), the gradients of the forward of fwd8_bf16.hpp are, with S_t, z_t
+// the forward state after token t and
+// R_t = sum_{u >= t} phi(q_u) dY_u^T, r_t = sum_{u >= t} dd_u phi(q_u):
+//   dphi(q_t) = S_t dY_t + dd_t z_t
+//   dphi(k_t) = R_t v_t + r_t
+//   dv_t      = R_t^T phi(k_t)
+// and dq = dphi(q) phi'(q), dk = dphi(k) phi'(k), where phi'(x) = min(1, phi(x))
+// for elu + 1 (1 on x >= 0 where phi(x) = x + 1 >= 1, exp(x) = phi(x) < 1 below)
+// and 1 for the identity map.  Chunked like the forward (64 tokens):
+//   dphi(Q)_c = dY_c S_{c-1}^T + dd_c z_{c-1}^T + tril(dY_c V_c^T + dd_c 1^T) phi(K)_c
+//   dphi(K)_c = V_c R_{c+1}^T + 1 r_{c+1}^T + triu(V_c dY_c^T + 1 dd_c^T) phi(Q)_c
+//   dV_c      = phi(K)_c R_{c+1} + triu(phi(K)_c phi(Q)_c^T) dY_c
+// (tril / triu over (query, key) with the diagonal included).  Passes: the
+// state pass gives the forward state at segment starts; bwd_dq8_bf16 runs
+// each segment forward in time and also writes dd; bwd_rstate8_bf16 sums R
+// and r over state sub-segments for a suffix over segments; bwd_dkv8_bf16
+// runs each segment backward in time.  dY is dO over the forward's saved
+// denominator, rounded to bf16 once; every pass uses that same dY.
+//
+// Precision of dq.  dphi(q_t) = sum_j phi(k_j) (v_j - o_t) . dY_t satisfies
+// phi(q_t) . dphi(q_t) = 0 up to eps: for elu + 1 its part along the all-ones
+// direction cancels, and for inputs of small spread the result is far smaller
+// than its terms.  A bf16 phi(k) = 1 + elu(k) keeps elu(k) only to 2^-8
+// absolute, and an o rounded anywhere on its way (a bf16 score or output in
+// the forward) moves the cancelling terms by 2^-9 of their size; either alone
+// leaves percent-level errors in dq.  The dq pass therefore
+//  * writes phi = 1 + elu and carries the constant part in fp32:
+//      S_t = E_t + 1 Vbar_t^T,  z_t = zeta_t + n_t 1,
+//      dphi(q_t) = E_t dY_t + dd_t zeta_t + (Vbar_t . dY_t + n_t dd_t) 1,
+//    with E = sum elu(k) v^T and zeta = sum elu(k) (bf16 operands of full
+//    relative precision), Vbar = sum v and n the token count (fp32), and the
+//    in-chunk sums over keys taken from the fp32 accumulators;
+//  * forms dd from its own state rather than from the forward's o:
+//      dd_t = -phi(q_t) . (S_t dY_t) / (phi(q_t) . z_t + eps),
+//    the same S_t, z_t that the gradient uses, so that the cancellation is
+//    exact in the arithmetic the pass carries out.  dd goes to the workspace
+//    for the reverse passes.
+#pragma once
+
+#include "fwd8_bf16.hpp"
+
+namespace linattn {
+
+// 4-byte buffer load (bounds-checked: 0 past the range).
+__device__ __forceinline__ float buffer_load_f32(rsrc_t rs, int voff) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, voff, 0, 0));
+}
+
+// 1 / den for dY = dO / den; rows past the end (den read as 0) get 0.
+__device__ __forceinline__ float dy_inv(float den) { return den != 0.f ? 1.f / den : 0.f; }
+
+// Eight elements of dY = dO / den, rounded to bf16 as every pass uses them.
+__device__ __forceinline__ uint4 dy_pack8(uint4 g, float inv) {
+    return make_uint4(pack_bf16x2(bf_lo(g.x) * inv, bf_hi(g.x) * inv), pack_bf16x2(bf_lo(g.y) * inv, bf_hi(g.y) * inv),
+                      pack_bf16x2(bf_lo(g.z) * inv, bf_hi(g.z) * inv), pack_bf16x2(bf_lo(g.w) * inv, bf_hi(g.w) * inv));
+}
+
+// Per-thread loads of one chunk for the backward: Q, K, V, dO rows, and the
+// saved denominators (and, with DD, dd) of this thread's dO rows.
+template <int DK, int DV, bool DD = true>
+struct BwdBuf {
+    Units<DK> q, k;
+    Units<DV> v, g;
+    float den[Units<DV>::N], dd[Units<DV>::N];
+    __device__ __forceinline__ void load(const uint16_t *qb, const uint16_t *kb, const uint16_t *vb, const uint16_t *gb,
+                                         const float *db, const float *ddb, int rows_valid, int tid) {
+        q.load(qb, rows_valid, tid);
+        k.load(kb, rows_valid, tid);
+        v.load(vb, rows_valid, tid);
+        g.load(gb, rows_valid, tid);
+        const rsrc_t rs = chunk_rsrc(db, rows_valid * 4);
+#pragma unroll
+        for (int i = 0; i < Units<DV>::N; ++i) den[i] = buffer_load_f32(rs, Units<DV>::row_of(tid, i) * 4);
+        if constexpr (DD) {
+            const rsrc_t rd = chunk_rsrc(ddb, rows_valid * 4);
+#pragma unroll
+            for (int i = 0; i < Units<DV>::N; ++i) dd[i] = buffer_load_f32(rd, Units<DV>::row_of(tid, i) * 4);
+        }
+    }
+};
+
+// Stage dY = dO / den (bf16, Tile<DV>) and, when sDD is given, dd (fp32 per
+// row).  Rows past the end read den = 0 and dd = 0 and get dY = 0.
+template <int DV>
+__device__ __forceinline__ void stage_dy(const Units<DV> &g, const float (&den)[Units<DV>::N],
+                                         const float (&dd)[Units<DV>::N], uint16_t *sDY, float *sDD, int tid) {
+#pragma unroll
+    for (int i = 0; i < Units<DV>::N; ++i) {
+        const int row = Units<DV>::row_of(tid, i), col = Units<DV>::col_of(tid, i);
+        *reinterpret_cast<uint4 *>(sDY + Tile<DV>::off(row, col)) = dy_pack8(g.r[i], dy_inv(den[i]));
+        if (sDD && col == 0) sDD[row] = dd[i];
+    }
+}
+
+// Row sums of phi(Q) in fp32 from the raw rows (sum over the DK / 8
+// consecutive lanes of a row), into sSq[row].
+template <int DK, int PHI>
+__device__ __forceinline__ void stage_phi_rowsum(const Units<DK> &q, float *sSq, int tid) {
+    constexpr int CG = Units<DK>::CG;
+#pragma unroll
+    for (int i = 0; i < Units<DK>::N; ++i) {
+        const uint32_t wv[4] = {q.r[i].x, q.r[i].y, q.r[i].z, q.r[i].w};
+        float x = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x += phi_fast(bf_lo(wv[e]), PHI) + phi_fast(bf_hi(wv[e]), PHI);
+#pragma unroll
+        for (int m = 1; m < CG; m <<= 1) x += __shfl_xor(x, m, 64);
+        if (Units<DK>::col_of(tid, i) == 0) sSq[Units<DK>::row_of(tid, i)] = x;
+    }
+}
+
+// The staged Q and K rows into their tiles through feature map QF / KF
+// (phi_fast modes, or kRaw for the inputs as they are), and V as is.
+constexpr int kRaw = -1;
+template <int F>
+__device__ __forceinline__ uint4 feat8(uint4 raw) {
+    if constexpr (F == kRaw) return raw;
+    else return phi_pack8(raw, F);
+}
+template <int DK, int DV, int QF, int KF, bool DD>
+__device__ __forceinline__ void stage_qkv(const BwdBuf<DK, DV, DD> &b, uint16_t *sQ, uint16_t *sK, uint16_t *sV,
+                                          int tid) {
+#pragma unroll
+    for (int i = 0; i < Units<DK>::N; ++i) {
+        const int row = Units<DK>::row_of(tid, i), col = Units<DK>::col_of(tid, i);
+        *reinterpret_cast<uint4 *>(sQ + Tile<DK>::off(row, col)) = feat8<QF>(b.q.r[i]);
+        *reinterpret_cast<uint4 *>(sK + Tile<DK>::off(row, col)) = feat8<KF>(b.k.r[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < Units<DV>::N; ++i)
+        *reinterpret_cast<uint4 *>(sV + Tile<DV>::off(Units<DV>::row_of(tid, i), Units<DV>::col_of(tid, i))) =
+            b.v.r[i];
+}
+
+// A operand rows m -> row index perm_dv(nt, m) (k along the row) from a TileS
+// [rows][Dv] tile: two 8-byte reads per lane.
+template <int DV>
+__device__ __forceinline__ bf16x8 tiles_row_operand(const uint16_t *t, int row, int col) {
+    const uint2 lo = *reinterpret_cast<const uint2 *>(t + TileS<DV>::off(row, col));
+    const uint2 hi = *reinterpret_cast<const uint2 *>(t + TileS<DV>::off(row, col + 4));
+    return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
+// phi'(x) for elu + 1 (1 for the identity map): 1 on x >= 0, exp(x) below,
+// from phi(x) = exp(x) < 1 there (kScalePhi) or from x itself (kScaleRaw).
+constexpr int kScaleNone = 0, kScalePhi = 1, kScaleRaw = 2;
+template <int PHI, int MODE>
+__device__ __forceinline__ float dphi_of(float f) {
+    if (PHI || MODE == kScaleNone) return 1.f;
+    if (MODE == kScalePhi) return fminf(1.f, f);
+    return f >= 0.f ? 1.f : __builtin_amdgcn_exp2f(f * 1.4426950408889634f);
+}
+
+// Store 16 rows x (2 * NTW) permuted tiles of a gradient, scaled by phi'
+// (from the staged tile given, per MODE): lane (g, l16) holds, for tile pair
+// p, the 8 consecutive columns 32 p + 8 g .. + 7 of row l16.
+template <int D, int NTW, int MODE, int PHI>
+__device__ __forceinline__ void store_grad_rows(const f32x4 (&acc)[NTW], int nt0, const uint16_t *phi_tile,
+                                                int tile_row, uint16_t *out_row, bool ok, int g) {
+    constexpr bool SCALE = MODE != kScaleNone && !PHI;
+#pragma unroll
+    for (int pp = 0; pp < NTW / 2; ++pp) {
+        const int p = (nt0 >> 1) + pp;
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[i] = acc[2 * pp][i];
+            x[4 + i] = acc[2 * pp + 1][i];
+        }
+        if (SCALE) {
+            const uint4 f = *reinterpret_cast<const uint4 *>(phi_tile + Tile<D>::off(tile_row, 32 * p + 8 * g));
+            const uint32_t fw[4] = {f.x, f.y, f.z, f.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                x[2 * e] *= dphi_of<PHI, MODE>(bf_lo(fw[e]));
+                x[2 * e + 1] *= dphi_of<PHI, MODE>(bf_hi(fw[e]));
+            }
+        }
+        if (ok) {
+            uint4 u;
+            u.x = pack_bf16x2(x[0], x[1]);
+            u.y = pack_bf16x2(x[2], x[3]);
+            u.z = pack_bf16x2(x[4], x[5]);
+            u.w = pack_bf16x2(x[6], x[7]);
+            *reinterpret_cast<uint4 *>(out_row + 32 * p + 8 * g) = u;
+        }
+    }
+}
+
+// Eight dd values of tokens 32 ks + 8 G .. + 7 (the state update's operand
+// order for lane group G) as a bf16 MFMA operand.
+__device__ __forceinline__ bf16x8 dd_operand(const float *sDD, int ks, int G) {
+    const float4 a = *reinterpret_cast<const float4 *>(sDD + 32 * ks + 8 * G);
+    const float4 b = *reinterpret_cast<const float4 *>(sDD + 32 * ks + 8 * G + 4);
+    return as_bf16x8(make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y),
+                                pack_bf16x2(b.z, b.w)));
+}
+
+// ============================================================== dQ pass
+// Per output segment, forward in time from the segment's prefix state.  Wave
+// w serves query block qblk (light and heavy blocks paired per SIMD as in the
+// forward) and half w % 2 of the key dims.  For elu + 1 the state is carried
+// as E = sum elu(k) v^T, zeta = sum elu(k), Vbar = sum v and the token count
+// (start: E, zeta and Vbar of the segment's prefix cell; Vbar sits after zeta
+// and start_vb may be null for zero); for the identity map E, zeta are S, z.
+// Writes dq and dd_out (dd of every token, for the reverse passes).
+template <int DK, int DV, int PHI>
+__global__ __launch_bounds__(kThreads8, 1) void bwd_dq8_bf16(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    const float *__restrict__ den, const uint16_t *__restrict__ dout, uint16_t *__restrict__ dq,
+    float *__restrict__ dd_out, const float *__restrict__ start, size_t start_stride_bh, size_t start_stride_seg,
+    const float *__restrict__ start_z, size_t start_z_stride_bh, const float *__restrict__ start_vb, int N, int P,
+    int seg_len, float eps) {
+    using TK = Tile<DK>;
+    using TV = Tile<DV>;
+    constexpr bool KAPPA = PHI == 0; // elu + 1: the constant part is carried apart
+    constexpr float kap = KAPPA ? 1.f : 0.f;
+    constexpr int FEAT = KAPPA ? kFeatElu : PHI;
+    constexpr int KSV = DV / 32;     // k-steps over value dims
+    constexpr int NTK = DK / 16 / 2; // key-dim tiles per wave
+    __shared__ __attribute__((aligned(16))) uint16_t sQ[kChunk * TK::RS]; // raw q
+    __shared__ __attribute__((aligned(16))) uint16_t sK[kChunk * TK::RS]; // features of k (elu for elu + 1)
+    __shared__ __attribute__((aligned(16))) uint16_t sV[kChunk * TV::RS];
+    __shared__ __attribute__((aligned(16))) uint16_t sDY[kChunk * TV::RS];
+    __shared__ __attribute__((aligned(16))) float sSq[kChunk];      // sum_i phi(q_i) per row
+    __shared__ __attribute__((aligned(16))) float sRed[2 * 2 * kChunk]; // per key-dim half: phi(q).(S dY), phi(q).zeta
+    __shared__ __attribute__((aligned(16))) uint16_t sS[DK * DV];
+    __shared__ __attribute__((aligned(16))) float sZf[DK];
+    __shared__ __attribute__((aligned(16))) float sVb[KAPPA ? DV : 4];     // Vbar before the chunk
+    __shared__ __attribute__((aligned(16))) float sVp[KAPPA ? 8 * DV : 4]; // the chunk's per-wave column sums
+
+    const int seg = blockIdx.x % P, bh = blockIdx.x / P;
+    const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
+    const int l16 = lane & 15, g = lane >> 4, qd = lane & 3;
+    const int qblk_w = w < 4 ? (w >> 1) : 5 - (w >> 1), dh = w & 1;
+    const bf16x8 ones = bf16_ones8();
+    const int t_begin = seg * seg_len;
+    const int t_end = min(N, t_begin + seg_len);
+    const int nch = (t_end - t_begin + kChunk - 1) / kChunk;
+    const size_t row0 = (size_t)bh * N + t_begin;
+
+    State8<DK, DV> st;
+    {
+        const float *s0 = start ? start + bh * start_stride_bh + seg * start_stride_seg : nullptr;
+        const float *z0 = start_z ? start_z + bh * start_z_stride_bh + seg * start_stride_seg : nullptr;
+        state8_load<DK, DV>(st, s0, z0, w, lane);
+        if (KAPPA && tid < DV) {
+            const float *vb0 = start_vb ? start_vb + bh * start_z_stride_bh + seg * start_stride_seg : nullptr;
+            sVb[tid] = vb0 ? vb0[tid] : 0.f;
+        }
+    }
+    auto state_to_lds = [&] {
+        state8_to_lds<DK, DV>(st, sS, w, lane);
+        if (State8<DK, DV>::has_z(w) && lane < 16) sZf[State8<DK, DV>::z_dk(w, lane)] = st.z[0];
+    };
+    state_to_lds();
+
+    // never negative: a sub-segment may start past the end of a ragged sequence
+    auto rows_in = [&](int c) { return max(0, min(kChunk, t_end - t_begin - c * kChunk)); };
+    auto issue = [&](BwdBuf<DK, DV, false> &b, int c) {
+        const size_t r = row0 + (size_t)c * kChunk;
+        b.load(q + r * DK, k + r * DK, v + r * DV, dout + r * DV, den + r, nullptr, rows_in(c), tid);
+    };
+    BwdBuf<DK, DV, false> buf;
+    if (nch > 0) issue(buf, 0);
+    for (int c = 0; c < nch; ++c) {
+        const int valid = rows_in(c);
+        float vsum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (KAPPA) {
+#pragma unroll
+            for (int i = 0; i < Units<DV>::N; ++i) add_bf16x8(vsum, buf.v.r[i]);
+        }
+        stage_qkv<DK, DV, kRaw, FEAT>(buf, sQ, sK, sV, tid);
+        stage_phi_rowsum<DK, PHI>(buf.q, sSq, tid);
+        stage_dy<DV>(buf.g, buf.den, buf.dd, sDY, nullptr, tid);
+        if (c + 1 < nch) issue(buf, c + 1);
+        __syncthreads();
+        // tokens before this chunk (the constant part's count)
+        const float n_prev = (float)(t_begin + c * kChunk);
+
+        auto chunk_work = [&](auto qblk_c) {
+            constexpr int qblk = decltype(qblk_c)::value;
+            const int tq = 16 * qblk + l16;
+            // dY rows of this wave's query block: B operand over value dims
+            bf16x8 dya[KSV];
+#pragma unroll
+            for (int ks = 0; ks < KSV; ++ks)
+                dya[ks] = *reinterpret_cast<const bf16x8 *>(sDY + TV::off(tq, 32 * ks + 8 * g));
+            // G^T[key][query] = v_key . dY_query for key blocks 0..qblk, zero
+            // above the diagonal; mk: the causal mask itself
+            f32x4 gt[4], mk[4];
+#pragma unroll
+            for (int kb4 = 0; kb4 < 4; ++kb4) {
+                gt[kb4] = f32x4{0.f, 0.f, 0.f, 0.f};
+                mk[kb4] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (kb4 <= qblk) {
+#pragma unroll
+                    for (int ks = 0; ks < KSV; ++ks)
+                        gt[kb4] = mfma16x16x32(
+                            *reinterpret_cast<const bf16x8 *>(sV + TV::off(16 * kb4 + l16, 32 * ks + 8 * g)), dya[ks],
+                            gt[kb4]);
+                    // rounded to bf16 here, so that the sum over keys below and
+                    // the feat(K)^T G product use the same values (at the first
+                    // token the two cancel exactly)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const bool keep = kb4 < qblk || 4 * g + i <= l16;
+                        gt[kb4][i] = keep ? bf16_round(gt[kb4][i]) : 0.f;
+                        mk[kb4][i] = keep ? 1.f : 0.f;
+                    }
+                }
+            }
+            // Vbar_t . dY_t = Vbar_{c-1} . dY_t + sum_{j <= t} v_j . dY_t, in fp32
+            float vdy = 0.f;
+#pragma unroll
+            for (int kb4 = 0; kb4 < 4; ++kb4) {
+                if (kb4 <= qblk) vdy += (gt[kb4][0] + gt[kb4][1]) + (gt[kb4][2] + gt[kb4][3]);
+            }
+            if (KAPPA) {
+#pragma unroll
+                for (int ks = 0; ks < KSV; ++ks) {
+                    const float4 a = *reinterpret_cast<const float4 *>(sVb + 32 * ks + 8 * g);
+                    const float4 b = *reinterpret_cast<const float4 *>(sVb + 32 * ks + 8 * g + 4);
+                    const float vb[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) vdy = fmaf((float)dya[ks][e], vb[e], vdy);
+                }
+            }
+            vdy += __shfl_xor(vdy, 16, 64);
+            vdy += __shfl_xor(vdy, 32, 64);
+
+            // A = E_t dY_t and zeta_t over this wave's key dims (tiles permuted as perm_dv)
+            f32x4 acc[NTK], zt[NTK];
+#pragma unroll
+            for (int j = 0; j < NTK; ++j) {
+                acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+                const int nt = dh * NTK + j;
+                const int dkr = perm_dv(nt, l16);
+#pragma unroll
+                for (int ks = 0; ks < KSV; ++ks)
+                    acc[j] = mfma16x16x32(tiles_row_operand<DV>(sS, dkr, 32 * ks + 8 * g), dya[ks], acc[j]);
+                const float4 zf = *reinterpret_cast<const float4 *>(sZf + 32 * (nt >> 1) + 8 * g + 4 * (nt & 1));
+                zt[j] = f32x4{zf.x, zf.y, zf.z, zf.w};
+            }
+            auto pack_b = [&](const f32x4(&x)[4], int s2) {
+                uint4 u;
+                u.x = pack_bf16x2(x[2 * s2][0], x[2 * s2][1]);
+                u.y = pack_bf16x2(x[2 * s2][2], x[2 * s2][3]);
+                u.z = pack_bf16x2(x[2 * s2 + 1][0], x[2 * s2 + 1][1]);
+                u.w = pack_bf16x2(x[2 * s2 + 1][2], x[2 * s2 + 1][3]);
+                return as_bf16x8(u);
+            };
+            // in-chunk: feat(K)^T Gm^T and feat(K)^T M over key steps of 32
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                if (2 * s2 <= qblk) {
+                    const bf16x8 bop = pack_b(gt, s2), mop = pack_b(mk, s2);
+                    const int klo = 32 * s2 + 4 * g, khi = klo + 16;
+#pragma unroll
+                    for (int j = 0; j < NTK; ++j) {
+                        const int nt = dh * NTK + j;
+                        const int colq = 32 * (nt >> 1) + 8 * qd + 4 * (nt & 1);
+                        const bf16x8 ka = tr_operand<DK>(sK, klo, khi, colq, lane);
+                        acc[j] = mfma16x16x32(ka, bop, acc[j]);
+                        zt[j] = mfma16x16x32(ka, mop, zt[j]);
+                    }
+                }
+            }
+            // phi(q_t) of this lane's key dims: for tile pair p, columns 32 p + 8 g .. + 7
+            float fq[NTK][4];
+#pragma unroll
+            for (int pp = 0; pp < NTK / 2; ++pp) {
+                const uint4 r = *reinterpret_cast<const uint4 *>(sQ + TK::off(tq, 32 * (dh * (NTK / 2) + pp) + 8 * g));
+                const uint32_t rw[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    fq[2 * pp][2 * e] = phi_fast(bf_lo(rw[e]), PHI);
+                    fq[2 * pp][2 * e + 1] = phi_fast(bf_hi(rw[e]), PHI);
+                    fq[2 * pp + 1][2 * e] = phi_fast(bf_lo(rw[2 + e]), PHI);
+                    fq[2 * pp + 1][2 * e + 1] = phi_fast(bf_hi(rw[2 + e]), PHI);
+                }
+            }
+            // phi(q) . A and phi(q) . zeta over this half of the key dims
+            float pa = 0.f, pz = 0.f;
+#pragma unroll
+            for (int j = 0; j < NTK; ++j) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    pa = fmaf(fq[j][i], acc[j][i], pa);
+                    pz = fmaf(fq[j][i], zt[j][i], pz);
+                }
+            }
+            pa += __shfl_xor(pa, 16, 64);
+            pa += __shfl_xor(pa, 32, 64);
+            pz += __shfl_xor(pz, 16, 64);
+            pz += __shfl_xor(pz, 32, 64);
+            if (g == 0) {
+                sRed[(dh * 2 + 0) * kChunk + tq] = pa;
+                sRed[(dh * 2 + 1) * kChunk + tq] = pz;
+            }
+            __syncthreads();
+            // dd_t = -phi(q).(S_t dY_t) / (phi(q).z_t + eps) with S = E + 1 Vbar^T,
+            // z = zeta + n 1 (kap = 0: S = E, z = zeta)
+            const float sq = sSq[tq];
+            const float n_t = n_prev + (float)(tq + 1);
+            const float num = (sRed[0 * kChunk + tq] + sRed[2 * kChunk + tq]) + kap * sq * vdy;
+            const float dnm = (sRed[1 * kChunk + tq] + sRed[3 * kChunk + tq]) + kap * n_t * sq + eps;
+            const float ddq = dnm != 0.f ? -num / dnm : 0.f;
+            // dphi(q) = A + dd zeta + (Vbar . dY + n dd) 1
+            const float cpart = kap * fmaf(n_t, ddq, vdy);
+#pragma unroll
+            for (int j = 0; j < NTK; ++j) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[j][i] = fmaf(ddq, zt[j][i], acc[j][i]) + cpart;
+            }
+            const bool ok = tq < valid;
+            if (ok && dh == 0 && g == 0) dd_out[row0 + (size_t)c * kChunk + tq] = ddq;
+            store_grad_rows<DK, NTK, kScaleRaw, PHI>(acc, dh * NTK, sQ, tq,
+                                                     dq + (row0 + (size_t)c * kChunk + tq) * DK, ok, g);
+        };
+        switch (qblk_w) {
+        case 0: chunk_work(std::integral_constant<int, 0>{}); break;
+        case 1: chunk_work(std::integral_constant<int, 1>{}); break;
+        case 2: chunk_work(std::integral_constant<int, 2>{}); break;
+        default: chunk_work(std::integral_constant<int, 3>{}); break;
+        }
+        if (KAPPA) colsum_to_lds<DV>(vsum, sVp, w, lane);
+
+        // carry the state across the chunk (elu(0) = 0: rows past the end add nothing)
+        state8_update<DK, DV>(st, sK, sV, w, lane, ones, 0.f);
+        __syncthreads();
+        if (c + 1 < nch) {
+            state_to_lds();
+            if (KAPPA && tid < DV) sVb[tid] += colsum_from_lds<DV>(sVp, tid);
+        }
+    }
+}
+
+// ============================================================== reverse state pass
+// Per state sub-segment s (the first output segment's sub-segments are
+// skipped, cell j holds sub-segment R + j): dR = phi(Q)^T dY and
+// dr = phi(Q)^T dd, in the layout of the forward's segment states.
+template <int DK, int DV, int PHI>
+__global__ __launch_bounds__(kThreads8, 2) void bwd_rstate8_bf16(
+    const uint16_t *__restrict__ q, const float *__restrict__ den, const float *__restrict__ dd,
+    const uint16_t *__restrict__ dout, float *__restrict__ ws, int N, int cells_per_bh, int cell_stride,
+    int first_sub, int sub_len) {
+    __shared__ __attribute__((aligned(16))) uint16_t sQ[kChunk * Tile<DK>::RS];
+    __shared__ __attribute__((aligned(16))) uint16_t sDY[kChunk * Tile<DV>::RS];
+    __shared__ __attribute__((aligned(16))) float sDD[kChunk];
+
+    const int cell = blockIdx.x % cells_per_bh, bh = blockIdx.x / cells_per_bh;
+    const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
+    const int t_begin = (first_sub + cell) * sub_len;
+    const int t_end = min(N, t_begin + sub_len);
+    const int nch = (t_end - t_begin + kChunk - 1) / kChunk;
+    const size_t row0 = (size_t)bh * N + t_begin;
+
+    State8<DK, DV> st;
+    state8_load<DK, DV>(st, nullptr, nullptr, w, lane);
+    struct Buf {
+        Units<DK> q;
+        Units<DV> g;
+        float den[Units<DV>::N], dd[Units<DV>::N];
+    };
+    // never negative: a sub-segment may start past the end of a ragged sequence
+    auto rows_in = [&](int c) { return max(0, min(kChunk, t_end - t_begin - c * kChunk)); };
+    auto issue = [&](Buf &b, int c) {
+        const size_t r = row0 + (size_t)c * kChunk;
+        const int nv = rows_in(c);
+        b.q.load_stream(q + r * DK, nv, tid);
+        b.g.load_stream(dout + r * DV, nv, tid);
+        const rsrc_t rs = chunk_rsrc(den + r, nv * 4), rd = chunk_rsrc(dd + r, nv * 4);
+#pragma unroll
+        for (int i = 0; i < Units<DV>::N; ++i) {
+            b.den[i] = buffer_load_f32(rs, Units<DV>::row_of(tid, i) * 4);
+            b.dd[i] = buffer_load_f32(rd, Units<DV>::row_of(tid, i) * 4);
+        }
+    };
+    Buf b;
+    if (nch > 0) issue(b, 0);
+    for (int c = 0; c < nch; ++c) {
+#pragma unroll
+        for (int i = 0; i < Units<DK>::N; ++i)
+            *reinterpret_cast<uint4 *>(sQ + Tile<DK>::off(Units<DK>::row_of(tid, i), Units<DK>::col_of(tid, i))) =
+                phi_pack8(b.q.r[i], PHI);
+        stage_dy<DV>(b.g, b.den, b.dd, sDY, sDD, tid);
+        if (c + 1 < nch) issue(b, c + 1);
+        __syncthreads();
+        const bf16x8 wop[kChunk / 32] = {dd_operand(sDD, 0, lane >> 4), dd_operand(sDD, 1, lane >> 4)};
+        // rows past the end have dY = 0 and dd = 0: nothing to take back out
+        state8_update_w<DK, DV>(st, sQ, sDY, w, lane, wop, 0.f);
+        __syncthreads();
+    }
+    float *dst = ws + ((size_t)bh * cell_stride + cell) * (size_t)(DK * DV + DK);
+    state8_store<DK, DV>(st, dst, w, lane);
+    state8_store_z<DK, DV>(st, dst + DK * DV, w, lane);
+}
+
+// ============================================================== dK, dV pass
+// Per output segment, backward in time from R, r summed over the later
+// segments (zero for the last one).  Wave w serves key block kblk and half
+// w % 2 of the key dims (dK) and of the value dims (dV).
+template <int DK, int DV, int PHI>
+__global__ __launch_bounds__(kThreads8, 1) void bwd_dkv8_bf16(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    const float *__restrict__ den, const float *__restrict__ dd, const uint16_t *__restrict__ dout,
+    uint16_t *__restrict__ dk, uint16_t *__restrict__ dv, const float *__restrict__ rstart, size_t rstart_stride_bh,
+    size_t rstart_stride_seg, int N, int P, int seg_len) {
+    using TK = Tile<DK>;
+    using TV = Tile<DV>;
+    constexpr int KSK = DK / 32, KSV = DV / 32;
+    constexpr int NTK = DK / 16 / 2, NTV = DV / 16 / 2;
+    __shared__ __attribute__((aligned(16))) uint16_t sQ[kChunk * TK::RS];
+    __shared__ __attribute__((aligned(16))) uint16_t sK[kChunk * TK::RS];
+    __shared__ __attribute__((aligned(16))) uint16_t sV[kChunk * TV::RS];
+    __shared__ __attribute__((aligned(16))) uint16_t sDY[kChunk * TV::RS];
+    __shared__ __attribute__((aligned(16))) float sDD[kChunk];
+    __shared__ __attribute__((aligned(16))) uint16_t sR[DK * DV];
+    __shared__ __attribute__((aligned(16))) float sRf[DK];
+
+    const int seg = blockIdx.x % P, bh = blockIdx.x / P;
+    const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
+    const int l16 = lane & 15, g = lane >> 4, qd = lane & 3;
+    // key block per wave; blocks 0 (heaviest: every query block follows it)
+    // and 3 share a SIMD, as do 1 and 2
+    const int kblk_w = w < 4 ? (w >> 1) : 5 - (w >> 1), dh = w & 1;
+    const int t_begin = seg * seg_len;
+    const int t_end = min(N, t_begin + seg_len);
+    const int nch = (t_end - t_begin + kChunk - 1) / kChunk;
+    const size_t row0 = (size_t)bh * N + t_begin;
+
+    State8<DK, DV> st; // R^T tiles and r
+    {
+        const float *r0 = (rstart && seg + 1 < P) ? rstart + bh * rstart_stride_bh + seg * rstart_stride_seg : nullptr;
+        state8_load<DK, DV>(st, r0, r0 ? r0 + DK * DV : nullptr, w, lane);
+    }
+    auto state_to_lds = [&] {
+        state8_to_lds<DK, DV>(st, sR, w, lane);
+        if (State8<DK, DV>::has_z(w) && lane < 16) sRf[State8<DK, DV>::z_dk(w, lane)] = st.z[0];
+    };
+    state_to_lds();
+
+    // never negative: a sub-segment may start past the end of a ragged sequence
+    auto rows_in = [&](int c) { return max(0, min(kChunk, t_end - t_begin - c * kChunk)); };
+    auto issue = [&](BwdBuf<DK, DV> &b, int c) {
+        const size_t r = row0 + (size_t)c * kChunk;
+        b.load(q + r * DK, k + r * DK, v + r * DV, dout + r * DV, den + r, dd + r, rows_in(c), tid);
+    };
+    BwdBuf<DK, DV> buf;
+    if (nch > 0) issue(buf, nch - 1);
+    for (int c = nch - 1; c >= 0; --c) {
+        const int valid = rows_in(c);
+        stage_qkv<DK, DV, PHI, PHI>(buf, sQ, sK, sV, tid);
+        stage_dy<DV>(buf.g, buf.den, buf.dd, sDY, sDD, tid);
+        if (c > 0) issue(buf, c - 1);
+        __syncthreads();
+
+        auto chunk_work = [&](auto kblk_c) {
+            constexpr int kblk = decltype(kblk_c)::value;
+            const int tk = 16 * kblk + l16;
+            // B operands with n = this wave's keys: V^T (over value dims), phi(K)^T (over key dims)
+            bf16x8 va[KSV], ka[KSK];
+#pragma unroll
+            for (int ks = 0; ks < KSV; ++ks) va[ks] = *reinterpret_cast<const bf16x8 *>(sV + TV::off(tk, 32 * ks + 8 * g));
+#pragma unroll
+            for (int ks = 0; ks < KSK; ++ks) ka[ks] = *reinterpret_cast<const bf16x8 *>(sK + TK::off(tk, 32 * ks + 8 * g));
+            // G[query][key] = dY_query . v_key + dd_query and P[query][key] =
+            // phi(q).phi(k), for query blocks kblk..3, zero below the diagonal
+            f32x4 gq[4], pq[4];
+#pragma unroll
+            for (int qb = 0; qb < 4; ++qb) {
+                gq[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                pq[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (qb >= kblk) {
+#pragma unroll
+                    for (int ks = 0; ks < KSV; ++ks)
+                        gq[qb] = mfma16x16x32(
+                            *reinterpret_cast<const bf16x8 *>(sDY + TV::off(16 * qb + l16, 32 * ks + 8 * g)), va[ks],
+                            gq[qb]);
+#pragma unroll
+                    for (int ks = 0; ks < KSK; ++ks)
+                        pq[qb] = mfma16x16x32(
+                            *reinterpret_cast<const bf16x8 *>(sQ + TK::off(16 * qb + l16, 32 * ks + 8 * g)), ka[ks],
+                            pq[qb]);
+                    const float4 dd4 = *reinterpret_cast<const float4 *>(sDD + 16 * qb + 4 * g);
+                    const float dda[4] = {dd4.x, dd4.y, dd4.z, dd4.w};
+                    // dY . v rounded to bf16 before dd is added: dd was formed
+                    // (dQ pass) from these same rounded in-chunk products, and at
+                    // the first token dY . v + dd cancels only with them
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const bool keep = qb > kblk || 4 * g + i >= l16;
+                        gq[qb][i] = keep ? bf16_round(gq[qb][i]) + dda[i] : 0.f;
+                        pq[qb][i] = keep ? pq[qb][i] : 0.f;
+                    }
+                }
+            }
+            f32x4 ak[NTK], av[NTV];
+            // dphi(K)^T: R v^T + r, then phi(Q)^T Gm
+#pragma unroll
+            for (int j = 0; j < NTK; ++j) {
+                ak[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+                const int nt = dh * NTK + j;
+                const int dkr = perm_dv(nt, l16);
+#pragma unroll
+                for (int ks = 0; ks < KSV; ++ks)
+                    ak[j] = mfma16x16x32(tiles_row_operand<DV>(sR, dkr, 32 * ks + 8 * g), va[ks], ak[j]);
+                const float4 rf = *reinterpret_cast<const float4 *>(sRf + 32 * (nt >> 1) + 8 * g + 4 * (nt & 1));
+                ak[j][0] += rf.x;
+                ak[j][1] += rf.y;
+                ak[j][2] += rf.z;
+                ak[j][3] += rf.w;
+            }
+            // dV^T: R^T phi(k), then dY^T P
+#pragma unroll
+            for (int j = 0; j < NTV; ++j) {
+                av[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+                const int nt = dh * NTV + j;
+                const int colq = 32 * (nt >> 1) + 8 * qd + 4 * (nt & 1);
+#pragma unroll
+                for (int ks = 0; ks < KSK; ++ks) {
+                    const int klo = 32 * ks + 8 * g;
+                    av[j] = mfma16x16x32(tr_operand_in<TileS<DV>>(sR, klo, klo + 4, colq, lane), ka[ks], av[j]);
+                }
+            }
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                if (2 * s2 + 1 >= kblk) {
+                    uint4 gu, pu;
+                    gu.x = pack_bf16x2(gq[2 * s2][0], gq[2 * s2][1]);
+                    gu.y = pack_bf16x2(gq[2 * s2][2], gq[2 * s2][3]);
+                    gu.z = pack_bf16x2(gq[2 * s2 + 1][0], gq[2 * s2 + 1][1]);
+                    gu.w = pack_bf16x2(gq[2 * s2 + 1][2], gq[2 * s2 + 1][3]);
+                    pu.x = pack_bf16x2(pq[2 * s2][0], pq[2 * s2][1]);
+                    pu.y = pack_bf16x2(pq[2 * s2][2], pq[2 * s2][3]);
+                    pu.z = pack_bf16x2(pq[2 * s2 + 1][0], pq[2 * s2 + 1][1]);
+                    pu.w = pack_bf16x2(pq[2 * s2 + 1][2], pq[2 * s2 + 1][3]);
+                    const bf16x8 gop = as_bf16x8(gu), pop = as_bf16x8(pu);
+                    const int klo = 32 * s2 + 4 * g, khi = klo + 16;
+#pragma unroll
+                    for (int j = 0; j < NTK; ++j) {
+                        const int nt = dh * NTK + j;
+                        const int colq = 32 * (nt >> 1) + 8 * qd + 4 * (nt & 1);
+                        ak[j] = mfma16x16x32(tr_operand<DK>(sQ, klo, khi, colq, lane), gop, ak[j]);
+                    }
+#pragma unroll
+                    for (int j = 0; j < NTV; ++j) {
+                        const int nt = dh * NTV + j;
+                        const int colq = 32 * (nt >> 1) + 8 * qd + 4 * (nt & 1);
+                        av[j] = mfma16x16x32(tr_operand<DV>(sDY, klo, khi, colq, lane), pop, av[j]);
+                    }
+                }
+            }
+            const size_t orow = row0 + (size_t)c * kChunk + tk;
+            store_grad_rows<DK, NTK, kScalePhi, PHI>(ak, dh * NTK, sK, tk, dk + orow * DK, tk < valid, g);
+            store_grad_rows<DV, NTV, kScaleNone, PHI>(av, dh * NTV, nullptr, tk, dv + orow * DV, tk < valid, g);
+        };
+        switch (kblk_w) {
+        case 0: chunk_work(std::integral_constant<int, 0>{}); break;
+        case 1: chunk_work(std::integral_constant<int, 1>{}); break;
+        case 2: chunk_work(std::integral_constant<int, 2>{}); break;
+        default: chunk_work(std::integral_constant<int, 3>{}); break;
+        }
+
+        // carry R, r back across the chunk: R += phi(Q)^T dY, r += phi(Q)^T dd
+        const bf16x8 wop[kChunk / 32] = {dd_operand(sDD, 0, lane >> 4), dd_operand(sDD, 1, lane >> 4)};
+        state8_update_w<DK, DV>(st, sQ, sDY, w, lane, wop, 0.f);
+        __syncthreads();
+        if (c > 0) state_to_lds();
+    }
+}
+
+} // namespace linattn

@@ -18,12 +18,18 @@ constexpr int kThreads = 256; // four 64-wide waves per workgroup
 // ---------------------------------------------------------------- feature map
 // phi(x) = elu(x) + 1: x + 1 for x >= 0 and exp(x) for x < 0 (elu's exp(x) - 1,
 // plus one).  Mode 1 is the identity map used for the post-feature-map worked
-// examples.
+// examples.  Mode 2 (kFeatElu) is elu itself, phi - 1: the backward writes
+// phi(x) = 1 + elu(x) and carries the constant part separately, so that the
+// bf16 copy of a feature keeps its varying part at full relative precision
+// (bf16 of 1 + x keeps only the bits of x above 2^-8).
+constexpr int kFeatElu = 2;
 __device__ __forceinline__ float phi_fast(float x, int mode) {
-    if (mode) return x;
+    if (mode == 1) return x;
     // exp(x) = 2^(x log2 e) on the hardware exp2; relative error ~1e-7 for the
     // |x| seen here, far below the bf16 rounding that follows.
-    return x >= 0.f ? x + 1.f : __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+    const float e = __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+    if (mode == kFeatElu) return x >= 0.f ? x : e - 1.f;
+    return x >= 0.f ? x + 1.f : e;
 }
 __device__ __forceinline__ float phi_exact(float x, int mode) {
     if (mode) return x;
@@ -42,6 +48,8 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
     __bf16 b = static_cast<__bf16>(f);
     return (uint32_t)__builtin_bit_cast(unsigned short, b);
 }
+// x rounded to the nearest bf16 (ties to even), as a float.
+__device__ __forceinline__ float bf16_round(float x) { return __uint_as_float(f32_to_bf16_bits(x) << 16); }
 // Two floats -> packed bf16 pair (one v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     typedef float f32x2 __attribute__((ext_vector_type(2)));

@@ -211,15 +211,16 @@ __device__ __forceinline__ void state8_scale(State8<DK, DV> &st, float d) {
     st.z *= d;
 }
 
-// S += phi(K)^T V and z += phi(K)^T 1 over one chunk for this wave's tiles
+// S += phi(K)^T V and z += phi(K)^T w over one chunk for this wave's tiles
 // (as S^T += V^T phi(K): the V operand supplies the rows, phi(K) the columns).
-// kt: phi(K) rows (decayed to the chunk end when gated), vt: V rows.  Rows
-// past the end of the sequence hold phi(0) in kt and zeros in vt: they add
-// nothing to S, and pad (their number times phi(0): 1 under elu + 1, 0 under
-// the identity map) is taken back out of z.
+// kt: phi(K) rows (decayed to the chunk end when gated), vt: V rows; wop[ks]:
+// the per-token weights of z for the 32 tokens of step ks in this lane's
+// operand order (all ones for z itself).  Rows past the end of the sequence
+// hold phi(0) in kt and zeros in vt: they add nothing to S, and pad (their
+// weighted count times phi(0)) is taken back out of z.
 template <int DK, int DV>
-__device__ __forceinline__ void state8_update(State8<DK, DV> &st, const uint16_t *kt, const uint16_t *vt, int w,
-                                              int lane, bf16x8 ones, float pad) {
+__device__ __forceinline__ void state8_update_w(State8<DK, DV> &st, const uint16_t *kt, const uint16_t *vt, int w,
+                                                int lane, const bf16x8 (&wop)[kChunk / 32], float pad) {
     using S = State8<DK, DV>;
     const int G = lane >> 4, q = lane & 3, mt0 = (w >> 2) * S::MTW, nt0 = (w & 3) * S::NTW;
     const int zmi = S::zmi(w);
@@ -235,10 +236,17 @@ __device__ __forceinline__ void state8_update(State8<DK, DV> &st, const uint16_t
         for (int mi = 0; mi < S::MTW; ++mi) {
 #pragma unroll
             for (int ni = 0; ni < S::NTW; ++ni) st.s[mi][ni] = mfma16x16x32(b[ni], a[mi], st.s[mi][ni]);
-            if (mi == zmi) st.z = mfma16x16x32(ones, a[mi], st.z);
+            if (mi == zmi) st.z = mfma16x16x32(wop[ks], a[mi], st.z);
         }
     }
     st.z -= pad;
+}
+
+template <int DK, int DV>
+__device__ __forceinline__ void state8_update(State8<DK, DV> &st, const uint16_t *kt, const uint16_t *vt, int w,
+                                              int lane, bf16x8 ones, float pad) {
+    const bf16x8 wop[kChunk / 32] = {ones, ones};
+    state8_update_w<DK, DV>(st, kt, vt, w, lane, wop, pad);
 }
 
 // bf16 S [dk][dv] into LDS (TileS layout): each lane writes the four values
@@ -259,12 +267,51 @@ __device__ __forceinline__ void state8_to_lds(const State8<DK, DV> &st, uint16_t
     }
 }
 
+// Column sums of staged Units<D> rows: vsum[e] += element e of the unit, in fp32.
+__device__ __forceinline__ void add_bf16x8(float (&vsum)[8], uint4 u) {
+    const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        vsum[2 * e] += bf_lo(wv[e]);
+        vsum[2 * e + 1] += bf_hi(wv[e]);
+    }
+}
+
+// Per-thread column sums of Units<D> (columns 8 (tid % (D / 8)) + e) summed
+// over the wave's lanes with the same columns, then written as this wave's
+// row of red[8][D] (lanes 0 .. D / 8 - 1).
+template <int D>
+__device__ __forceinline__ void colsum_to_lds(float (&vsum)[8], float *red, int w, int lane) {
+    constexpr int CG = D / 8;
+#pragma unroll
+    for (int m = CG; m < 64; m <<= 1) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vsum[e] += __shfl_xor(vsum[e], m, 64);
+    }
+    if (lane < CG) {
+        float4 *r = reinterpret_cast<float4 *>(red + w * D + 8 * lane);
+        r[0] = make_float4(vsum[0], vsum[1], vsum[2], vsum[3]);
+        r[1] = make_float4(vsum[4], vsum[5], vsum[6], vsum[7]);
+    }
+}
+
+// Column col of the eight waves' rows of red[8][D], summed in wave order.
+template <int D>
+__device__ __forceinline__ float colsum_from_lds(const float *red, int col) {
+    float x = 0.f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) x += red[w * D + col];
+    return x;
+}
+
 // ====================================================================== kernels
 // Segment-state pass (see seg_state_bf16): dS = phi(K)^T V and dz over one
 // state sub-segment, plus the segment's gate product.
-// PHI: the feature map (0: elu + 1, 1: identity), fixed at compile time so
-// that phi costs no per-element select.
-template <int DK, int DV, bool GATED, int PHI>
+// PHI: the feature map (0: elu + 1, 1: identity, kFeatElu: elu), fixed at
+// compile time so that phi costs no per-element select.  VBAR: the cell also
+// holds the column sums of V (Dv more floats after z), the constant part of
+// the state when the features are written 1 + elu.
+template <int DK, int DV, bool GATED, int PHI, bool VBAR = false>
 __global__ __launch_bounds__(kThreads8, 4) void seg_state8_bf16(const uint16_t *__restrict__ k,
                                                                 const uint16_t *__restrict__ v,
                                                                 const float *__restrict__ alpha,
@@ -288,6 +335,9 @@ __global__ __launch_bounds__(kThreads8, 4) void seg_state8_bf16(const uint16_t *
     const bf16x8 ones = bf16_ones8();
     float seg_lsum = 0.f;
     int seg_zeros = 0;
+    // VBAR: this thread's V columns are the same in every chunk (the unit
+    // layout repeats every 512 units), so it sums them over the whole range
+    float vsum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 
     struct Buf {
         Units<DK> k;
@@ -324,9 +374,11 @@ __global__ __launch_bounds__(kThreads8, 4) void seg_state8_bf16(const uint16_t *
             *reinterpret_cast<uint4 *>(sK + Tile<DK>::off(row, Units<DK>::col_of(tid, i))) = GATED ? scaled : plain;
         }
 #pragma unroll
-        for (int i = 0; i < Units<DV>::N; ++i)
+        for (int i = 0; i < Units<DV>::N; ++i) {
             *reinterpret_cast<uint4 *>(sV + Tile<DV>::off(Units<DV>::row_of(tid, i), Units<DV>::col_of(tid, i))) =
                 b.v.r[i];
+            if (VBAR) add_bf16x8(vsum, b.v.r[i]);
+        }
         if (c + 1 < nch) issue(b, c + 1);
         __syncthreads();
         if (GATED) state8_scale<DK, DV>(st, dC);
@@ -338,20 +390,30 @@ __global__ __launch_bounds__(kThreads8, 4) void seg_state8_bf16(const uint16_t *
     Buf b0;
     issue(b0, 0);
     for (int c = 0; c < nch; ++c) step(b0, c);
-    float *dst = ws + ((size_t)bh * P + seg) * (size_t)(DK * DV + DK);
+    constexpr size_t E = (size_t)DK * DV + DK + (VBAR ? DV : 0);
+    float *dst = ws + ((size_t)bh * P + seg) * E;
     state8_store<DK, DV>(st, dst, w, lane);
     state8_store_z<DK, DV>(st, dst + DK * DV, w, lane);
+    if (VBAR) {
+        // sK is free after the last chunk's closing barrier
+        float *red = reinterpret_cast<float *>(sK);
+        colsum_to_lds<DV>(vsum, red, w, lane);
+        __syncthreads();
+        if (tid < DV) dst[DK * DV + DK + tid] = colsum_from_lds<DV>(red, tid);
+    }
     if (GATED && tid == 0) gam[(size_t)bh * P + seg] = seg_zeros > 0 ? 0.f : __builtin_amdgcn_exp2f(seg_lsum);
 }
 
 // Causal output pass (see fwd_out_bf16): wave w serves query block w / 2 and
-// half w % 2 of the value columns; the state tiles are split 2 x 4.
-template <int DK, int DV, bool GATED, int PHI>
+// half w % 2 of the value columns; the state tiles are split 2 x 4.  TRAIN:
+// also keep, for the backward, each token's denominator phi(q).z + eps
+// (den_out).
+template <int DK, int DV, bool GATED, int PHI, bool TRAIN = false>
 __global__ __launch_bounds__(kThreads8, 1) void fwd_out8_bf16(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const float *__restrict__ alpha, uint16_t *__restrict__ o, const float *__restrict__ start, size_t start_stride_bh,
     size_t start_stride_seg, const float *__restrict__ start_z, size_t start_z_stride_bh, float *__restrict__ s_final,
-    float *__restrict__ z_final, int N, int P, int seg_len, float eps) {
+    float *__restrict__ z_final, int N, int P, int seg_len, float eps, float *__restrict__ den_out) {
     constexpr int phi_mode = PHI;
     using TK = Tile<DK>;
     using TV = Tile<DV>;
@@ -559,6 +621,7 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd_out8_bf16(
             if (tq < valid) {
                 const float inv = __builtin_amdgcn_rcpf(dt[0] + eps); // 1 ulp; the result is rounded to bf16
                 uint16_t *orow = obp + ((size_t)c * kChunk + tq) * DV;
+                if (TRAIN && dh == 0 && g == 0) den_out[row0 + (size_t)c * kChunk + tq] = dt[0] + eps;
     #pragma unroll
                 for (int pp = 0; pp < NTO / 2; ++pp) {
                     const int p = dh * (NTO / 2) + pp;

@@ -16,16 +16,18 @@ namespace linattn {
 // The order over segments is fixed, so the result is bitwise reproducible.
 // Grid: x = element blocks of 256, y = bh.
 // Cells 0..cells-2 hold segment states on entry; cells 0..cells-1 receive the
-// prefix (cell p gets the state before segment p).  P is the cell stride.
+// prefix (cell p gets the state before segment p).  P is the number of cells
+// per (b, h); a cell is E floats (S, z, then any further sums, which start
+// from zero).
 __global__ __launch_bounds__(256) void seg_prefix(float *__restrict__ ws, const float *__restrict__ gam,
                                                   const float *__restrict__ s_init, const float *__restrict__ z_init,
-                                                  int P, int cells, int DK, int DV) {
-    const int E = DK * DV + DK;
+                                                  int P, int cells, int DK, int DV, int E) {
     const int e = blockIdx.x * 256 + threadIdx.x;
     const int bh = blockIdx.y;
     if (e >= E) return;
     float run = 0.f;
-    if (s_init) run = e < DK * DV ? s_init[(size_t)bh * DK * DV + e] : z_init[(size_t)bh * DK + (e - DK * DV)];
+    if (s_init && e < DK * DV + DK)
+        run = e < DK * DV ? s_init[(size_t)bh * DK * DV + e] : z_init[(size_t)bh * DK + (e - DK * DV)];
     float *cell = ws + (size_t)bh * P * E + e;
     const float *gb = gam ? gam + (size_t)bh * P : nullptr;
     // Eight segments' loads are issued before their stores: the loop is a
@@ -49,6 +51,31 @@ __global__ __launch_bounds__(256) void seg_prefix(float *__restrict__ ws, const 
         }
     }
     cell[(size_t)(cells - 1) * E] = run;
+}
+
+// Inclusive suffix over the cells of each (b, h), in place and in a fixed
+// order: cell j <- sum_{j' >= j} cell j' (the backward's sums over later
+// segments).  P cells of E floats per (b, h).
+__global__ __launch_bounds__(256) void seg_suffix(float *__restrict__ ws, int P, int cells, int E) {
+    const int e = blockIdx.x * 256 + threadIdx.x;
+    const int bh = blockIdx.y;
+    if (e >= E) return;
+    float *cell = ws + (size_t)bh * P * E + e;
+    float run = 0.f;
+    constexpr int kBatch = 8;
+    for (int j1 = cells; j1 > 0; j1 -= kBatch) {
+        const int nb = min(kBatch, j1);
+        float d[kBatch];
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) d[i] = i < nb ? cell[(size_t)(j1 - 1 - i) * E] : 0.f;
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+            if (i < nb) {
+                run += d[i];
+                cell[(size_t)(j1 - 1 - i) * E] = run;
+            }
+        }
+    }
 }
 
 // Non-causal total: S = sum over all segments (fixed order), written to

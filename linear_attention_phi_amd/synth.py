@@ -28,7 +28,7 @@ from dataclasses import dataclass, field
 import numpy as np
 import torch
 
-Q_ID, K_ID, V_ID, G_ID, PK_ID, PV_ID = 0, 1, 2, 3, 4, 5
+Q_ID, K_ID, V_ID, G_ID, PK_ID, PV_ID, DO_ID = 0, 1, 2, 3, 4, 5, 6
 
 
 def _stream(seed: int, tensor_id: int, b: int, h: int) -> np.random.Generator:
@@ -129,6 +129,12 @@ def qkv(w: Workload, heads=None, N=None):
     k = normal_heads(w.seed, K_ID, w.B, w.H, n, w.Dk, w.k_scale, w.dtype, heads)
     v = normal_heads(w.seed, V_ID, w.B, w.H, n, w.Dv, w.v_scale, w.dtype, heads)
     return q, k, v
+
+
+def dout(w: Workload, heads=None, N=None) -> torch.Tensor:
+    """An upstream gradient dL/dO for the backward: N(0, 1) in the workload's dtype, [B, H, N, Dv]."""
+    n = w.N if N is None else N
+    return normal_heads(w.seed, DO_ID, w.B, w.H, n, w.Dv, 1.0, w.dtype, heads)
 
 
 def alpha(w: Workload, heads=None, N=None) -> torch.Tensor:

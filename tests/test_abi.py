@@ -60,8 +60,12 @@ def test_workspace_size_is_host_arithmetic(L):
     assert n >= 16 * 2 * (128 * 128 + 128) * 4
     assert ws(1, 1, 16, 131072, 128, 128, 1) > n  # plus the gate products
     assert ws(2, 1, 1, 64, 16, 16, 0) > 0          # non-causal always needs the total
+    # the backward keeps forward (with the column sums of V) and reverse
+    # segment states, and dd of every token
+    assert ws(3, 1, 16, 131072, 128, 128, 1) >= 2 * n + 16 * 131072 * 4
+    assert ws(3, 1, 1, 64, 64, 64, 1) >= 64 * 4  # dd even with one segment
     # invalid arguments -> 0
-    assert ws(3, 1, 1, 64, 16, 16, 0) == 0
+    assert ws(4, 1, 1, 64, 16, 16, 0) == 0
     assert ws(0, 0, 1, 64, 16, 16, 0) == 0
     assert ws(0, 1, 1, 64, 48, 16, 0) == 0
     assert ws(0, 1, 1, 64, 16, 16, 7) == 0
@@ -135,3 +139,40 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(1, 1, 4, 16)
     with pytest.raises(TypeError):
         b.linattn_forward(x, x, x)
+
+
+def train(L, q=FAKE[0], k=FAKE[1], v=FAKE[2], o=FAKE[3], den=FAKE[4], B=1, H=1, N=64, Dk=64, Dv=64, dtype=1,
+          phi=0, eps=1e-6, ws=None, wsb=0):
+    return L.linattn_forward_train(q, k, v, o, den, None, None, None, None, B, H, N, Dk, Dv, dtype, phi, eps, ws,
+                                   wsb, None)
+
+
+def bwd(L, q=FAKE[0], k=FAKE[1], v=FAKE[2], den=FAKE[4], g=FAKE[5], dq=FAKE[6], dk=FAKE[7], dv=FAKE[8], si=None,
+        zi=None, B=1, H=1, N=64, Dk=64, Dv=64, dtype=1, phi=0, eps=1e-6, ws=FAKE[10], wsb=1 << 20):
+    return L.linattn_backward(q, k, v, den, g, dq, dk, dv, si, zi, B, H, N, Dk, Dv, dtype, phi, eps, ws, wsb, None)
+
+
+def test_training_forward_and_backward_reject_bad_arguments(L):
+    # chunked bf16 path only
+    assert train(L, dtype=0) == EDTYPE
+    assert train(L, Dk=32) == ESHAPE
+    assert train(L, Dv=16) == ESHAPE
+    for name in ("o", "den"):
+        assert train(L, **{name: None}) == EINVAL, name
+    assert train(L, den=FAKE[0]) == EINVAL  # den overlaps q
+    assert train(L, den=FAKE[3]) == EINVAL  # den overlaps o
+    assert bwd(L, dtype=0) == EDTYPE
+    assert bwd(L, Dk=32, Dv=128) == ESHAPE
+    for name in ("q", "k", "v", "den", "g", "dq", "dk", "dv"):
+        assert bwd(L, **{name: None}) == EINVAL, name
+    assert bwd(L, eps=-1.0) == EINVAL
+    assert bwd(L, ws=None, wsb=0) == EWORKSPACE  # dd lives in the workspace
+    assert bwd(L, si=FAKE[9]) == EINVAL           # s_init without z_init
+    assert bwd(L, dq=FAKE[0]) == EINVAL            # output overlaps an input
+    assert bwd(L, dk=FAKE[6]) == EINVAL            # outputs overlap each other
+    assert bwd(L, B=0) == EINVAL
+    assert bwd(L, phi=5) == EDTYPE
+    # long sequence on one head: segment states needed, workspace missing
+    assert bwd(L, N=131072) == EWORKSPACE
+    need = L.linattn_workspace_size(3, 1, 1, 131072, 64, 64, 1)
+    assert bwd(L, N=131072, ws=FAKE[10], wsb=need - 1) == EWORKSPACE

@@ -1,0 +1,105 @@
+"""GPU parity of the backward (dq, dk, dv) against the fp64 oracle's adjoint.
+
+The training forward runs through the C ABI (its o must equal the plain
+forward's bit for bit), the backward takes its den, and every gradient is
+compared with oracle.backward on the same seeded inputs (the oracle uses the
+exact forward, so the comparison includes every rounding of the kernels).  Gradients are compared normwise per head,
+max |got - ref| / max |ref| over each (b, h): single rows can vanish by
+cancellation (at a sequence's first token o = v whatever q is, so the exact
+dq there is of the order of eps, and rounding noise on it has no scale of its
+own); the per-row error is printed as well.  Shapes span several chunks and segments (the
+reverse segment sums), ragged tails, both head dims and their mix.  Sequences
+of one token get their own test: there every row of dq is eps-sized.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linear_attention_phi_amd import binding as la
+from linear_attention_phi_amd import synth
+from parity import TOL, assert_close, row_rel_err
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def make(B, H, N, Dk, Dv, seed, positive=False):
+    w = synth.Workload("t", B, H, N, Dk, Dv, torch.bfloat16, seed, q_scale=Dk ** -0.5, k_scale=Dk ** -0.5)
+    q, k, v = synth.qkv(w)
+    if positive:
+        q, k = ((x.float().abs() + 1.0 / 64).to(torch.bfloat16) for x in (q, k))
+    return q, k, v, synth.dout(w)
+
+
+def run(q, k, v, g, phi=la.PHI_ELU1, s0=None, z0=None):
+    d = [x.to(DEV) for x in (q, k, v, g)]
+    si = None if s0 is None else s0.to(DEV)
+    zi = None if z0 is None else z0.to(DEV)
+    o, den, _, _ = la.linattn_forward_train(d[0], d[1], d[2], si, zi, phi=phi)
+    o_plain, _, _ = la.linattn_forward(d[0], d[1], d[2], si, zi, phi=phi)
+    dq, dk, dv = la.linattn_backward(d[0], d[1], d[2], den, d[3], si, zi, phi=phi)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_plain)
+    return dq.cpu(), dk.cpu(), dv.cpu()
+
+
+def check(q, k, v, g, phi=la.PHI_ELU1, s0=None, z0=None):
+    dq, dk, dv = run(q, k, v, g, phi, s0, z0)
+    rq, rk, rv, _, _ = oracle.backward(q, k, v, g, s0, z0, phi_mode=phi)
+    tol = TOL[torch.bfloat16]
+    for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        print(f"  {name}: per-row error {row_rel_err(got, ref):.3e} (information)")
+        assert_close(name, got, ref, tol, per="head")
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 700, 64, 64), (1, 1, 5000, 128, 128), (2, 2, 1000, 64, 128),
+                                   (1, 3, 777, 128, 64), (1, 1, 64, 128, 128), (1, 1, 2, 64, 64),
+                                   (1, 1, 65, 128, 128), (4, 8, 300, 64, 64), (1, 2, 16385, 128, 128),
+                                   (16, 16, 64, 64, 64)])
+def test_backward(shape):
+    check(*make(*shape, seed=700 + sum(shape)))
+
+
+@pytest.mark.parametrize("Dk,Dv", [(64, 64), (128, 128), (64, 128)])
+def test_backward_one_token(Dk, Dv):
+    # One token: o = v s / (s + eps) with s = phi(q).phi(k), so dq and dk are
+    # (v . dY) eps / (s + eps) times phi(k) phi'(q), resp. phi(q) phi'(k):
+    # eps-sized differences of terms of size |phi| |v . dY|, against which
+    # alone an error bound means anything.  dv is compared as usual.
+    q, k, v, g = make(3, 2, 1, Dk, Dv, seed=750 + Dk + Dv)
+    dq, dk, dv = run(q, k, v, g)
+    rq, rk, rv, _, _ = oracle.backward(q, k, v, g)
+    tol = TOL[torch.bfloat16]
+    assert_close("dv", dv, rv, tol, per="head")
+    q64, k64, v64, g64 = (x.double().numpy() for x in (q, k, v, g))
+    fq, fk = oracle.phi(q64), oracle.phi(k64)
+    s = (fq * fk).sum(-1)
+    vdy = np.abs((v64 * g64).sum(-1)) / (s + 1e-6)  # |v . dY|, [B, H, 1]
+    for name, got, ref, f in (("dq", dq, rq, fk), ("dk", dk, rk, fq)):
+        terms = np.abs(f).max(-1) * vdy
+        err = np.abs(got.double().numpy() - ref).max(-1)
+        print(f"  {name}: max |err| / term size {float((err / terms).max()):.3e} (tol {tol:.0e})")
+        assert (err <= tol * terms).all(), name
+
+
+def test_backward_identity_map():
+    check(*make(1, 2, 900, 128, 128, seed=741, positive=True), phi=la.PHI_IDENTITY)
+
+
+def test_backward_with_initial_state():
+    q, k, v, g = make(1, 2, 3000, 128, 128, seed=742)
+    gen = torch.Generator().manual_seed(3)
+    s0 = torch.randn(1, 2, 128, 128, generator=gen)
+    z0 = torch.rand(1, 2, 128, generator=gen) * 50 + 20
+    check(q, k, v, g, s0=s0, z0=z0)
+
+
+def test_backward_deterministic():
+    q, k, v, g = (x.to(DEV) for x in make(1, 4, 9000, 128, 128, seed=743))
+    _, den, _, _ = la.linattn_forward_train(q, k, v)
+    r1 = la.linattn_backward(q, k, v, den, g)
+    r2 = la.linattn_backward(q, k, v, den, g)
+    torch.cuda.synchronize()
+    for x, y in zip(r1, r2):
+        assert torch.equal(x, y)
