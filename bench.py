@@ -132,8 +132,25 @@ def forward_case(name, dev):
     return w, fn, nbytes, (q, k, v, a)
 
 
+def backward_case(name, dev, inputs=None):
+    """Backward over a forward workload: den from the training forward (untimed), dO seeded N(0, 1)."""
+    w = synth.WORKLOADS[name]
+    q, k, v = inputs if inputs is not None else (x.to(dev) for x in synth.qkv(w))
+    g = synth.dout(w).to(dev)
+    _, den, _, _ = la.linattn_forward_train(q, k, v)
+    ws = torch.empty(la.workspace_size(la.KIND_BACKWARD, w.B, w.H, w.N, w.Dk, w.Dv, la.BF16), dtype=torch.uint8,
+                     device=dev)
+    out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+
+    def fn():
+        la.linattn_backward(q, k, v, den, g, out=out, workspace=ws)
+    return w, fn, rf.backward_bytes(w.B, w.H, w.N, w.Dk, w.Dv, 2)
+
+
 def kernel_bytes(kernel, w):
     """Algorithmic bytes one launch of a library kernel moves on workload w (None if not a whole-pass kernel)."""
+    if kernel.startswith("bwd_"):
+        return rf.backward_kernel_bytes(kernel, w.B, w.H, w.N, w.Dk, w.Dv, 2)
     if kernel.startswith("fwd_out_bf16"):
         return rf.forward_bytes(w.B, w.H, w.N, w.Dk, w.Dv, 2, gated=w.gated)
     if kernel == "decode_step":
@@ -142,6 +159,15 @@ def kernel_bytes(kernel, w):
         # non-causal: the state pass reads every K and V row once; the apply
         # pass reads Q and writes O once
         return w.B * w.H * w.N * (w.Dk + w.Dv) * 2
+    return None
+
+
+def kernel_flops(kernel, w, path_flops):
+    """MFMA-level flops of one launch, where the kernel does the path's contractions."""
+    if kernel.startswith("fwd_out"):
+        return path_flops
+    if kernel.startswith("bwd_"):
+        return rf.backward_kernel_flops(kernel, w.B, w.H, w.N, w.Dk, w.Dv)
     return None
 
 
@@ -240,7 +266,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-paths", action="store_true")
-    ap.add_argument("--path", choices=["forward", "gated", "decode", "noncausal"], default=None)
+    ap.add_argument("--path", choices=["forward", "gated", "decode", "noncausal", "backward"], default=None)
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -254,7 +280,7 @@ def main():
         copy_calibration(dev, args.steps)
         return
 
-    if args.path in ("decode", "gated", "noncausal"):
+    if args.path in ("decode", "gated", "noncausal", "backward"):
         # single-path run (used for counter collection); prints its own line
         run_single_path(args, dev, stream)
         return
@@ -301,7 +327,7 @@ def path_entry(w, fn, nbytes, stream, args, tokens, reset=None, flops=None, key=
     return {"workload": key, "ms_per_step": round(ms, 4), "Mtokens_per_s": round(tokens / (ms * 1e-3) / 1e6, 3),
             "path_roofline_frac": round(rf.hbm_time_s(nbytes) / (ms * 1e-3), 4),
             "roofline": roofline_entry(dom, kt[dom]["avg_ms"], kernel_bytes(dom, w), key,
-                                       flops if dom.startswith("fwd_out") else None),
+                                       kernel_flops(dom, w, flops)),
             "kernels_ms": {n: round(e["avg_ms"], 4) for n, e in kt.items()}}
 
 
@@ -320,6 +346,11 @@ def other_paths(args, dev, stream, headline_inputs):
     log("[bench] non-causal form")
     w, fn, nbytes = noncausal_case(HEADLINE, dev, headline_inputs)
     out["noncausal"] = path_entry(w, fn, nbytes, stream, args, w.B * w.N, key="noncausal_" + w.name)
+    del fn
+    log("[bench] backward")
+    w, fn, nbytes = backward_case(HEADLINE, dev, headline_inputs)
+    out["backward"] = path_entry(w, fn, nbytes, stream, args, w.B * w.N, key="backward_" + w.name,
+                                 flops=rf.backward_flops(w.B, w.H, w.N, w.Dk, w.Dv))
     return out
 
 
@@ -330,6 +361,10 @@ def run_single_path(args, dev, stream):
     elif args.path == "decode":
         w, fn, nbytes, reset = decode_case(dev)
         r = path_entry(w, fn, nbytes, stream, args, w.B, reset=reset)
+    elif args.path == "backward":
+        w, fn, nbytes = backward_case(HEADLINE, dev)
+        r = path_entry(w, fn, nbytes, stream, args, w.B * w.N, key="backward_" + w.name,
+                       flops=rf.backward_flops(w.B, w.H, w.N, w.Dk, w.Dv))
     else:
         w, fn, nbytes = noncausal_case(HEADLINE, dev)
         r = path_entry(w, fn, nbytes, stream, args, w.B * w.N, key="noncausal_" + w.name)

@@ -51,6 +51,15 @@ __device__ __forceinline__ float buffer_load_f32(rsrc_t rs, int voff) {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, voff, 0, 0));
 }
 
+// The lane index, hidden from loop-invariant code motion: the per-lane LDS
+// addresses of a chunk's many operand reads are then recomputed inside the
+// chunk loop (a few VALU ops beside the MFMAs) instead of all being hoisted
+// out of it and held in registers for the whole loop.
+__device__ __forceinline__ int lane_in_loop(int lane) {
+    asm volatile("" : "+v"(lane));
+    return lane;
+}
+
 // 1 / den for dY = dO / den; rows past the end (den read as 0) get 0.
 __device__ __forceinline__ float dy_inv(float den) { return den != 0.f ? 1.f / den : 0.f; }
 
@@ -285,6 +294,8 @@ __global__ __launch_bounds__(kThreads8, 1) void bwd_dq8_bf16(
 
         auto chunk_work = [&](auto qblk_c) {
             constexpr int qblk = decltype(qblk_c)::value;
+            const int lane = lane_in_loop(tid & 63);
+            const int l16 = lane & 15, g = lane >> 4, qd = lane & 3;
             const int tq = 16 * qblk + l16;
             // dY rows of this wave's query block: B operand over value dims
             bf16x8 dya[KSV];
@@ -563,103 +574,131 @@ __global__ __launch_bounds__(kThreads8, 1) void bwd_dkv8_bf16(
 
         auto chunk_work = [&](auto kblk_c) {
             constexpr int kblk = decltype(kblk_c)::value;
+            const int lane = lane_in_loop(tid & 63);
+            const int l16 = lane & 15, g = lane >> 4, qd = lane & 3;
             const int tk = 16 * kblk + l16;
-            // B operands with n = this wave's keys: V^T (over value dims), phi(K)^T (over key dims)
-            bf16x8 va[KSV], ka[KSK];
-#pragma unroll
-            for (int ks = 0; ks < KSV; ++ks) va[ks] = *reinterpret_cast<const bf16x8 *>(sV + TV::off(tk, 32 * ks + 8 * g));
-#pragma unroll
-            for (int ks = 0; ks < KSK; ++ks) ka[ks] = *reinterpret_cast<const bf16x8 *>(sK + TK::off(tk, 32 * ks + 8 * g));
-            // G[query][key] = dY_query . v_key + dd_query and P[query][key] =
-            // phi(q).phi(k), for query blocks kblk..3, zero below the diagonal
-            f32x4 gq[4], pq[4];
-#pragma unroll
-            for (int qb = 0; qb < 4; ++qb) {
-                gq[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-                pq[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (qb >= kblk) {
-#pragma unroll
-                    for (int ks = 0; ks < KSV; ++ks)
-                        gq[qb] = mfma16x16x32(
-                            *reinterpret_cast<const bf16x8 *>(sDY + TV::off(16 * qb + l16, 32 * ks + 8 * g)), va[ks],
-                            gq[qb]);
-#pragma unroll
-                    for (int ks = 0; ks < KSK; ++ks)
-                        pq[qb] = mfma16x16x32(
-                            *reinterpret_cast<const bf16x8 *>(sQ + TK::off(16 * qb + l16, 32 * ks + 8 * g)), ka[ks],
-                            pq[qb]);
-                    const float4 dd4 = *reinterpret_cast<const float4 *>(sDD + 16 * qb + 4 * g);
-                    const float dda[4] = {dd4.x, dd4.y, dd4.z, dd4.w};
-                    // dY . v rounded to bf16 before dd is added: dd was formed
-                    // (dQ pass) from these same rounded in-chunk products, and at
-                    // the first token dY . v + dd cancels only with them
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const bool keep = qb > kblk || 4 * g + i >= l16;
-                        gq[qb][i] = keep ? bf16_round(gq[qb][i]) + dda[i] : 0.f;
-                        pq[qb][i] = keep ? pq[qb][i] : 0.f;
-                    }
-                }
-            }
-            f32x4 ak[NTK], av[NTV];
-            // dphi(K)^T: R v^T + r, then phi(Q)^T Gm
-#pragma unroll
-            for (int j = 0; j < NTK; ++j) {
-                ak[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-                const int nt = dh * NTK + j;
-                const int dkr = perm_dv(nt, l16);
+            const size_t orow = row0 + (size_t)c * kChunk + tk;
+            auto pack_b = [&](const f32x4(&x)[4], int s2) {
+                uint4 u;
+                u.x = pack_bf16x2(x[2 * s2][0], x[2 * s2][1]);
+                u.y = pack_bf16x2(x[2 * s2][2], x[2 * s2][3]);
+                u.z = pack_bf16x2(x[2 * s2 + 1][0], x[2 * s2 + 1][1]);
+                u.w = pack_bf16x2(x[2 * s2 + 1][2], x[2 * s2 + 1][3]);
+                return as_bf16x8(u);
+            };
+            // ---- dK: G[query][key] = dY_query . v_key + dd_query (query >= key),
+            // then dphi(K)^T = R v^T + r + phi(Q)^T G
+            {
+                bf16x8 va[KSV];
 #pragma unroll
                 for (int ks = 0; ks < KSV; ++ks)
-                    ak[j] = mfma16x16x32(tiles_row_operand<DV>(sR, dkr, 32 * ks + 8 * g), va[ks], ak[j]);
-                const float4 rf = *reinterpret_cast<const float4 *>(sRf + 32 * (nt >> 1) + 8 * g + 4 * (nt & 1));
-                ak[j][0] += rf.x;
-                ak[j][1] += rf.y;
-                ak[j][2] += rf.z;
-                ak[j][3] += rf.w;
-            }
-            // dV^T: R^T phi(k), then dY^T P
+                    va[ks] = *reinterpret_cast<const bf16x8 *>(sV + TV::off(tk, 32 * ks + 8 * g));
+                f32x4 gq[4];
 #pragma unroll
-            for (int j = 0; j < NTV; ++j) {
-                av[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-                const int nt = dh * NTV + j;
-                const int colq = 32 * (nt >> 1) + 8 * qd + 4 * (nt & 1);
+                for (int qb = 0; qb < 4; ++qb) {
+                    gq[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    if (qb >= kblk) {
 #pragma unroll
-                for (int ks = 0; ks < KSK; ++ks) {
-                    const int klo = 32 * ks + 8 * g;
-                    av[j] = mfma16x16x32(tr_operand_in<TileS<DV>>(sR, klo, klo + 4, colq, lane), ka[ks], av[j]);
-                }
-            }
+                        for (int ks = 0; ks < KSV; ++ks)
+                            gq[qb] = mfma16x16x32(
+                                *reinterpret_cast<const bf16x8 *>(sDY + TV::off(16 * qb + l16, 32 * ks + 8 * g)),
+                                va[ks], gq[qb]);
+                        const float4 dd4 = *reinterpret_cast<const float4 *>(sDD + 16 * qb + 4 * g);
+                        const float dda[4] = {dd4.x, dd4.y, dd4.z, dd4.w};
+                        // dY . v rounded to bf16 before dd is added: dd was formed
+                        // (dQ pass) from these same rounded in-chunk products, and
+                        // at the first token dY . v + dd cancels only with them
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                if (2 * s2 + 1 >= kblk) {
-                    uint4 gu, pu;
-                    gu.x = pack_bf16x2(gq[2 * s2][0], gq[2 * s2][1]);
-                    gu.y = pack_bf16x2(gq[2 * s2][2], gq[2 * s2][3]);
-                    gu.z = pack_bf16x2(gq[2 * s2 + 1][0], gq[2 * s2 + 1][1]);
-                    gu.w = pack_bf16x2(gq[2 * s2 + 1][2], gq[2 * s2 + 1][3]);
-                    pu.x = pack_bf16x2(pq[2 * s2][0], pq[2 * s2][1]);
-                    pu.y = pack_bf16x2(pq[2 * s2][2], pq[2 * s2][3]);
-                    pu.z = pack_bf16x2(pq[2 * s2 + 1][0], pq[2 * s2 + 1][1]);
-                    pu.w = pack_bf16x2(pq[2 * s2 + 1][2], pq[2 * s2 + 1][3]);
-                    const bf16x8 gop = as_bf16x8(gu), pop = as_bf16x8(pu);
-                    const int klo = 32 * s2 + 4 * g, khi = klo + 16;
-#pragma unroll
-                    for (int j = 0; j < NTK; ++j) {
-                        const int nt = dh * NTK + j;
-                        const int colq = 32 * (nt >> 1) + 8 * qd + 4 * (nt & 1);
-                        ak[j] = mfma16x16x32(tr_operand<DK>(sQ, klo, khi, colq, lane), gop, ak[j]);
-                    }
-#pragma unroll
-                    for (int j = 0; j < NTV; ++j) {
-                        const int nt = dh * NTV + j;
-                        const int colq = 32 * (nt >> 1) + 8 * qd + 4 * (nt & 1);
-                        av[j] = mfma16x16x32(tr_operand<DV>(sDY, klo, khi, colq, lane), pop, av[j]);
+                        for (int i = 0; i < 4; ++i) {
+                            const bool keep = qb > kblk || 4 * g + i >= l16;
+                            gq[qb][i] = keep ? bf16_round(gq[qb][i]) + dda[i] : 0.f;
+                        }
                     }
                 }
+                f32x4 ak[NTK];
+#pragma unroll
+                for (int j = 0; j < NTK; ++j) {
+                    ak[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    const int nt = dh * NTK + j;
+                    const int dkr = perm_dv(nt, l16);
+#pragma unroll
+                    for (int ks = 0; ks < KSV; ++ks)
+                        ak[j] = mfma16x16x32(tiles_row_operand<DV>(sR, dkr, 32 * ks + 8 * g), va[ks], ak[j]);
+                    const float4 rf = *reinterpret_cast<const float4 *>(sRf + 32 * (nt >> 1) + 8 * g + 4 * (nt & 1));
+                    ak[j][0] += rf.x;
+                    ak[j][1] += rf.y;
+                    ak[j][2] += rf.z;
+                    ak[j][3] += rf.w;
+                }
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    if (2 * s2 + 1 >= kblk) {
+                        const bf16x8 gop = pack_b(gq, s2);
+                        const int klo = 32 * s2 + 4 * g, khi = klo + 16;
+#pragma unroll
+                        for (int j = 0; j < NTK; ++j) {
+                            const int nt = dh * NTK + j;
+                            const int colq = 32 * (nt >> 1) + 8 * qd + 4 * (nt & 1);
+                            ak[j] = mfma16x16x32(tr_operand<DK>(sQ, klo, khi, colq, lane), gop, ak[j]);
+                        }
+                    }
+                }
+                store_grad_rows<DK, NTK, kScalePhi, PHI>(ak, dh * NTK, sK, tk, dk + orow * DK, tk < valid, g);
             }
-            const size_t orow = row0 + (size_t)c * kChunk + tk;
-            store_grad_rows<DK, NTK, kScalePhi, PHI>(ak, dh * NTK, sK, tk, dk + orow * DK, tk < valid, g);
-            store_grad_rows<DV, NTV, kScaleNone, PHI>(av, dh * NTV, nullptr, tk, dv + orow * DV, tk < valid, g);
+            // keep the dV phase's loads from being hoisted into the dK phase
+            // (they would double the live registers)
+            __builtin_amdgcn_sched_barrier(0);
+            // ---- dV: P[query][key] = phi(q) . phi(k) (query >= key), then
+            // dV^T = R^T phi(k) + dY^T P
+            {
+                bf16x8 ka[KSK];
+#pragma unroll
+                for (int ks = 0; ks < KSK; ++ks)
+                    ka[ks] = *reinterpret_cast<const bf16x8 *>(sK + TK::off(tk, 32 * ks + 8 * g));
+                f32x4 pq[4];
+#pragma unroll
+                for (int qb = 0; qb < 4; ++qb) {
+                    pq[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    if (qb >= kblk) {
+#pragma unroll
+                        for (int ks = 0; ks < KSK; ++ks)
+                            pq[qb] = mfma16x16x32(
+                                *reinterpret_cast<const bf16x8 *>(sQ + TK::off(16 * qb + l16, 32 * ks + 8 * g)),
+                                ka[ks], pq[qb]);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const bool keep = qb > kblk || 4 * g + i >= l16;
+                            pq[qb][i] = keep ? pq[qb][i] : 0.f;
+                        }
+                    }
+                }
+                f32x4 av[NTV];
+#pragma unroll
+                for (int j = 0; j < NTV; ++j) {
+                    av[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    const int nt = dh * NTV + j;
+                    const int colq = 32 * (nt >> 1) + 8 * qd + 4 * (nt & 1);
+#pragma unroll
+                    for (int ks = 0; ks < KSK; ++ks) {
+                        const int klo = 32 * ks + 8 * g;
+                        av[j] = mfma16x16x32(tr_operand_in<TileS<DV>>(sR, klo, klo + 4, colq, lane), ka[ks], av[j]);
+                    }
+                }
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    if (2 * s2 + 1 >= kblk) {
+                        const bf16x8 pop = pack_b(pq, s2);
+                        const int klo = 32 * s2 + 4 * g, khi = klo + 16;
+#pragma unroll
+                        for (int j = 0; j < NTV; ++j) {
+                            const int nt = dh * NTV + j;
+                            const int colq = 32 * (nt >> 1) + 8 * qd + 4 * (nt & 1);
+                            av[j] = mfma16x16x32(tr_operand<DV>(sDY, klo, khi, colq, lane), pop, av[j]);
+                        }
+                    }
+                }
+                store_grad_rows<DV, NTV, kScaleNone, PHI>(av, dh * NTV, nullptr, tk, dv + orow * DV, tk < valid, g);
+            }
         };
         switch (kblk_w) {
         case 0: chunk_work(std::integral_constant<int, 0>{}); break;

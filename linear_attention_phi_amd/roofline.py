@@ -35,6 +35,35 @@ def decode_bytes(B, H, Dk, Dv, in_bytes, out_bytes=None, *, gated=False) -> int:
     return B * H * (2 * state + (2 * Dk + Dv) * in_bytes + Dv * out_bytes + (4 if gated else 0))
 
 
+def backward_bytes(B, H, N, Dk, Dv, in_bytes) -> int:
+    """Q, K, V, dO and the saved fp32 denominators read once; dQ, dK, dV written once."""
+    return B * H * N * ((2 * Dk + 2 * Dv) * in_bytes + 4 + (2 * Dk + Dv) * in_bytes)
+
+
+def backward_kernel_bytes(kernel, B, H, N, Dk, Dv, in_bytes) -> int | None:
+    """What one launch of a whole-sequence backward kernel must move."""
+    rows = B * H * N
+    if kernel == "bwd_dq_bf16":  # q, k, v, dO, den in; dq, dd out
+        return rows * ((3 * Dk + 2 * Dv) * in_bytes + 8)
+    if kernel == "bwd_dkv_bf16":  # q, k, v, dO, den, dd in; dk, dv out
+        return rows * ((3 * Dk + 3 * Dv) * in_bytes + 8)
+    return None
+
+
+def backward_kernel_flops(kernel, B, H, N, Dk, Dv) -> int | None:
+    """Recurrence-level flops of a backward kernel (2 Dk Dv per token for each
+    state-sized product): dQ pass S dY and the forward state update; dK/dV
+    pass R v, R^T phi(k) and the reverse state update."""
+    per = {"bwd_dq_bf16": 4, "bwd_dkv_bf16": 6}.get(kernel)
+    return None if per is None else per * B * H * N * Dk * Dv
+
+
+def backward_flops(B, H, N, Dk, Dv) -> int:
+    """Per token, 2 Dk Dv each for: the forward state update (recomputed), S dY,
+    the reverse state update, R v and R^T phi(k)."""
+    return 10 * B * H * N * Dk * Dv
+
+
 def method_flops(B, H, N, Dk, Dv) -> int:
     """Write S += phi(k) v^T and read phi(q)^T S per token: 2 Dk Dv each."""
     return 4 * B * H * N * Dk * Dv
