@@ -147,6 +147,28 @@ def backward_case(name, dev, inputs=None):
     return w, fn, rf.backward_bytes(w.B, w.H, w.N, w.Dk, w.Dv, 2)
 
 
+SNAP_POSITIONS = "8 prefix-cache points at 16384 m - 1 (m = 1..8) and the last 8 tokens"
+
+
+def snapshot_positions(N):
+    return sorted({16384 * m - 1 for m in range(1, 9) if 16384 * m - 1 < N} | {N - 1 - i for i in range(8)})
+
+
+def snapshots_case(name, dev, inputs=None):
+    """Causal forward that also returns the state after snapshot_positions(N)."""
+    w = synth.WORKLOADS[name]
+    q, k, v = inputs if inputs is not None else (x.to(dev) for x in synth.qkv(w))
+    pos = snapshot_positions(w.N)
+    ws = torch.empty(la.workspace_size(la.KIND_FORWARD, w.B, w.H, w.N, w.Dk, w.Dv, la.BF16), dtype=torch.uint8,
+                     device=dev)
+
+    def fn():
+        la.linattn_forward_snapshots(q, k, v, pos, workspace=ws)
+    # the forward's bytes plus each snapshot's state written once
+    nbytes = rf.forward_bytes(w.B, w.H, w.N, w.Dk, w.Dv, 2) + w.B * w.H * len(pos) * (w.Dk * w.Dv + w.Dk) * 4
+    return w, fn, nbytes, pos
+
+
 def kernel_bytes(kernel, w):
     """Algorithmic bytes one launch of a library kernel moves on workload w (None if not a whole-pass kernel)."""
     if kernel.startswith("bwd_"):
@@ -266,7 +288,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-paths", action="store_true")
-    ap.add_argument("--path", choices=["forward", "gated", "decode", "noncausal", "backward"], default=None)
+    ap.add_argument("--path", choices=["forward", "gated", "decode", "noncausal", "backward", "snapshots"],
+                    default=None)
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -280,7 +303,7 @@ def main():
         copy_calibration(dev, args.steps)
         return
 
-    if args.path in ("decode", "gated", "noncausal", "backward"):
+    if args.path in ("decode", "gated", "noncausal", "backward", "snapshots"):
         # single-path run (used for counter collection); prints its own line
         run_single_path(args, dev, stream)
         return
@@ -347,6 +370,11 @@ def other_paths(args, dev, stream, headline_inputs):
     w, fn, nbytes = noncausal_case(HEADLINE, dev, headline_inputs)
     out["noncausal"] = path_entry(w, fn, nbytes, stream, args, w.B * w.N, key="noncausal_" + w.name)
     del fn
+    log("[bench] forward with state snapshots")
+    w, fn, nbytes, pos = snapshots_case(HEADLINE, dev, headline_inputs)
+    out["snapshots"] = path_entry(w, fn, nbytes, stream, args, w.B * w.N, key="snapshots_" + w.name)
+    out["snapshots"]["positions"] = SNAP_POSITIONS
+    del fn
     log("[bench] backward")
     w, fn, nbytes = backward_case(HEADLINE, dev, headline_inputs)
     out["backward"] = path_entry(w, fn, nbytes, stream, args, w.B * w.N, key="backward_" + w.name,
@@ -361,6 +389,9 @@ def run_single_path(args, dev, stream):
     elif args.path == "decode":
         w, fn, nbytes, reset = decode_case(dev)
         r = path_entry(w, fn, nbytes, stream, args, w.B, reset=reset)
+    elif args.path == "snapshots":
+        w, fn, nbytes, _ = snapshots_case(HEADLINE, dev)
+        r = path_entry(w, fn, nbytes, stream, args, w.B * w.N, key="snapshots_" + w.name)
     elif args.path == "backward":
         w, fn, nbytes = backward_case(HEADLINE, dev)
         r = path_entry(w, fn, nbytes, stream, args, w.B * w.N, key="backward_" + w.name,

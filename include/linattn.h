@@ -56,6 +56,7 @@ extern "C" {
 #endif
 
 #define LINATTN_ABI_VERSION 2
+#define LINATTN_MAX_SNAPSHOTS 256
 
 enum linattn_dtype { LINATTN_F32 = 0, LINATTN_BF16 = 1 };
 enum linattn_phi { LINATTN_PHI_ELU1 = 0, LINATTN_PHI_IDENTITY = 1 };
@@ -170,6 +171,37 @@ int linattn_backward(const void *q, const void *k, const void *v,
                      int B, int H, int N, int Dk, int Dv, int dtype, int phi,
                      float eps, void *workspace, size_t workspace_bytes,
                      void *hip_stream);
+
+/*
+ * Causal forward that also returns the summary after chosen tokens: for each
+ * listed position p, S_p and z_p, the state once token p has been added (and
+ * decayed, when gated).  The product-order page ("What a summary can't do")
+ * notes that prefix caching and rolling back speculative tokens need a copy of
+ * the summary at the exact position, since a summary cannot be cut like a KV
+ * cache; these are those copies, taken in the same pass.
+ *
+ *   alpha      NULL (ungated) or [B][H][N] fp32 gates, as linattn_forward_gated.
+ *   positions  HOST array of n_pos token indices, each in [0, N); any order,
+ *              repeats allowed; 1 <= n_pos <= LINATTN_MAX_SNAPSHOTS.  The same
+ *              positions apply to every (b, h).
+ *   s_snap     output [B][H][n_pos][Dk][Dv] fp32; z_snap output
+ *              [B][H][n_pos][Dk] fp32 (required; must not overlap the other
+ *              arguments).
+ * o, s_final, z_final, s_init, z_init, eps and the workspace (kind
+ * LINATTN_KIND_GATED with alpha, else LINATTN_KIND_FORWARD) as
+ * linattn_forward(_gated).  Restricted to the chunked bf16 path (bf16, Dk and
+ * Dv in {64, 128}).  A snapshot at N - 1 equals (s_final, z_final) up to
+ * summation order.
+ */
+int linattn_forward_snapshots(const void *q, const void *k, const void *v,
+                              const float *alpha, void *o,
+                              const float *s_init, const float *z_init,
+                              float *s_final, float *z_final,
+                              const int *positions, int n_pos,
+                              float *s_snap, float *z_snap,
+                              int B, int H, int N, int Dk, int Dv, int dtype,
+                              int phi, float eps, void *workspace,
+                              size_t workspace_bytes, void *hip_stream);
 
 /*
  * Non-causal form: S = sum_t phi(k_t) v_t^T and z = sum_t phi(k_t) over the

@@ -34,6 +34,7 @@ SIGNATURES = {
     "linattn_forward_gated": ([_P] * 9 + [_I] * 7 + [_F, _P, _SZ, _P], _I),
     "linattn_forward_train": ([_P] * 9 + [_I] * 7 + [_F, _P, _SZ, _P], _I),
     "linattn_backward": ([_P] * 10 + [_I] * 7 + [_F, _P, _SZ, _P], _I),
+    "linattn_forward_snapshots": ([_P] * 10 + [_I] + [_P] * 2 + [_I] * 7 + [_F, _P, _SZ, _P], _I),
     "linattn_forward_noncausal": ([_P] * 6 + [_I] * 7 + [_F, _P, _SZ, _P], _I),
     "linattn_decode_step": ([_P] * 7 + [_I] * 6 + [_F, _P], _I),
     "linattn_workspace_size": ([_I] * 7, _SZ),
@@ -224,6 +225,52 @@ def linattn_backward(q, k, v, den, dout, s_init=None, z_init=None, *, eps=1e-6, 
                                 ws.numel(), _stream(q))
     _check(rc, "linattn_backward")
     return dq, dk, dv
+
+
+MAX_SNAPSHOTS = 256
+
+
+def linattn_forward_snapshots(q, k, v, positions, alpha=None, s_init=None, z_init=None, *, eps=1e-6,
+                              phi=PHI_ELU1, workspace=None):
+    """Causal forward that also returns the state after each listed token.
+
+    positions: ints in [0, N) (at most MAX_SNAPSHOTS) -> (o, s_snap [B, H, n, Dk, Dv],
+    z_snap [B, H, n, Dk], s_final, z_final).  alpha [B, H, N] fp32 or None.
+    bf16 with Dk, Dv in {64, 128}.
+    """
+    _dev(q, "q")
+    code = _dtype_code(q)
+    _dev(k, "k", q.dtype)
+    _dev(v, "v", q.dtype)
+    B, H, N, Dk = q.shape
+    Dv = v.shape[-1]
+    if tuple(k.shape) != (B, H, N, Dk) or tuple(v.shape[:3]) != (B, H, N):
+        raise ValueError("q, k, v shapes do not match")
+    if (s_init is None) != (z_init is None):
+        raise ValueError("pass both s_init and z_init or neither")
+    _dev(s_init, "s_init", torch.float32)
+    _dev(z_init, "z_init", torch.float32)
+    _dev(alpha, "alpha", torch.float32)
+    if alpha is not None and tuple(alpha.shape) != (B, H, N):
+        raise ValueError("alpha must be [B, H, N]")
+    pos = [int(p) for p in positions]
+    n = len(pos)
+    if not 1 <= n <= MAX_SNAPSHOTS:
+        raise ValueError(f"1 to {MAX_SNAPSHOTS} positions")
+    parr = (ctypes.c_int * n)(*pos)
+    o = torch.empty((B, H, N, Dv), dtype=q.dtype, device=q.device)
+    s_snap = torch.empty((B, H, n, Dk, Dv), dtype=torch.float32, device=q.device)
+    z_snap = torch.empty((B, H, n, Dk), dtype=torch.float32, device=q.device)
+    s_final = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device)
+    z_final = torch.empty((B, H, Dk), dtype=torch.float32, device=q.device)
+    kind = KIND_GATED if alpha is not None else KIND_FORWARD
+    ws, _ = _workspace(kind, B, H, N, Dk, Dv, code, q.device, workspace)
+    rc = lib().linattn_forward_snapshots(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(o), _ptr(s_init),
+                                         _ptr(z_init), _ptr(s_final), _ptr(z_final),
+                                         ctypes.cast(parr, ctypes.c_void_p), n, _ptr(s_snap), _ptr(z_snap), B, H, N,
+                                         Dk, Dv, code, phi, float(eps), _ptr(ws), ws.numel(), _stream(q))
+    _check(rc, "linattn_forward_snapshots")
+    return o, s_snap, z_snap, s_final, z_final
 
 
 def linattn_forward_noncausal(q, k, v, *, eps=1e-6, phi=PHI_ELU1, want_state=True, out=None, workspace=None):

@@ -163,17 +163,26 @@ template <typename F> void with_phi(int phi, F &&f) {
         f(std::integral_constant<int, LINATTN_PHI_ELU1>{});
 }
 
+// Snapshot request of linattn_forward_snapshots (null: none).
+struct SnapRequest {
+    SnapList list;
+    float *s_snap, *z_snap;
+};
+static_assert(kMaxSnapshots == LINATTN_MAX_SNAPSHOTS, "snapshot limit");
+
 template <int DK, int DV, bool GATED>
 int run_mfma_causal(const Plan &pl, const void *q, const void *k, const void *v, const float *alpha, void *o,
                     const float *s_init, const float *z_init, float *s_final, float *z_final, float *den,
-                    int BH, int N, int phi, float eps, char *ws, hipStream_t st) {
+                    const SnapRequest *snap, int BH, int N, int phi, float eps, char *ws, hipStream_t st) {
     const float *start = s_init, *start_z = z_init;
     size_t sbh = (size_t)DK * DV, sseg = 0, zbh = DK;
     if (pl.P > 1) {
         float *states = reinterpret_cast<float *>(ws);
         float *gam = GATED ? reinterpret_cast<float *>(ws + pl.ws_states) : nullptr;
-        // the sub-segments of the last output segment are never needed
-        const int P_run = (pl.P - 1) * pl.R;
+        // the sub-segments of the last output segment are never needed by
+        // the output pass; snapshots use all but the very last, so that no
+        // snapshot runs over more than one sub-segment
+        const int P_run = snap ? pl.P * pl.R - 1 : (pl.P - 1) * pl.R;
         LA_TRY(launch("seg_state_bf16", st, [&] {
             if constexpr (kEight<DK, DV>)
                 with_phi(phi, [&](auto PH) {
@@ -188,12 +197,35 @@ int run_mfma_causal(const Plan &pl, const void *q, const void *k, const void *v,
             seg_prefix<<<dim3((unsigned)((pl.E + 255) / 256), BH), dim3(256), 0, st>>>(
                 states, gam, s_init, z_init, pl.Ps, P_run + 1, DK, DV, (int)pl.E);
         }));
+        if (snap) {
+            if constexpr (kEight<DK, DV>) {
+                LA_TRY(launch("snap_state_bf16", st, [&] {
+                    with_phi(phi, [&](auto PH) {
+                        snap_state8_bf16<DK, DV, GATED, PH()><<<dim3(snap->list.n * BH), dim3(kThreads8), 0, st>>>(
+                            (const uint16_t *)k, (const uint16_t *)v, alpha, states, (size_t)pl.Ps * pl.E,
+                            pl.sub_len, P_run, nullptr, nullptr, snap->s_snap, snap->z_snap, N, snap->list);
+                    });
+                }));
+            }
+        }
         // output segment p starts from the prefix before state cell p * R
         start = states;
         start_z = states + (size_t)DK * DV;
         sbh = (size_t)pl.Ps * pl.E;
         sseg = (size_t)pl.R * pl.E;
         zbh = (size_t)pl.Ps * pl.E;
+    }
+    if (snap && pl.P == 1) {
+        // one segment: every snapshot runs from the initial state at token 0
+        if constexpr (kEight<DK, DV>) {
+            LA_TRY(launch("snap_state_bf16", st, [&] {
+                with_phi(phi, [&](auto PH) {
+                    snap_state8_bf16<DK, DV, GATED, PH()><<<dim3(snap->list.n * BH), dim3(kThreads8), 0, st>>>(
+                        (const uint16_t *)k, (const uint16_t *)v, alpha, nullptr, 0, pl.seg_len, 0, s_init, z_init,
+                        snap->s_snap, snap->z_snap, N, snap->list);
+                });
+            }));
+        }
     }
     return launch(GATED ? "fwd_out_bf16_gated" : "fwd_out_bf16", st, [&] {
         if constexpr (kEight<DK, DV>)
@@ -421,7 +453,7 @@ template <typename T, typename... A> int recur_noncausal_dk(int Dk, A &&...a) {
 int forward_impl(bool gated, const void *q, const void *k, const void *v, const float *alpha, void *o,
                  const float *s_init, const float *z_init, float *s_final, float *z_final, int B, int H, int N,
                  int Dk, int Dv, int dtype, int phi, float eps, void *workspace, size_t workspace_bytes,
-                 void *hip_stream, float *den = nullptr) {
+                 void *hip_stream, float *den = nullptr, const SnapRequest *snap = nullptr) {
     LA_TRY(check_common(B, H, N, Dk, Dv, dtype, phi, eps));
     if (!q || !k || !v || !o || (gated && !alpha)) return LINATTN_EINVAL;
     if ((s_init == nullptr) != (z_init == nullptr)) return LINATTN_EINVAL;
@@ -437,9 +469,9 @@ int forward_impl(bool gated, const void *q, const void *k, const void *v, const 
     if (pl.mfma) {
         if (gated)
             return by_dims_mfma<MfmaCausal<true>::F>(Dk, Dv, pl, q, k, v, alpha, o, s_init, z_init, s_final, z_final,
-                                                    den, BH, N, phi, eps, ws, st);
+                                                    den, snap, BH, N, phi, eps, ws, st);
         return by_dims_mfma<MfmaCausal<false>::F>(Dk, Dv, pl, q, k, v, alpha, o, s_init, z_init, s_final, z_final,
-                                                 den, BH, N, phi, eps, ws, st);
+                                                 den, snap, BH, N, phi, eps, ws, st);
     }
     if (dtype == LINATTN_BF16) {
         if (gated)
@@ -517,6 +549,34 @@ int linattn_forward_train(const void *q, const void *k, const void *v, void *o, 
         return LINATTN_EINVAL;
     return forward_impl(false, q, k, v, nullptr, o, s_init, z_init, s_final, z_final, B, H, N, Dk, Dv, dtype, phi,
                         eps, workspace, workspace_bytes, hip_stream, den);
+}
+
+int linattn_forward_snapshots(const void *q, const void *k, const void *v, const float *alpha, void *o,
+                              const float *s_init, const float *z_init, float *s_final, float *z_final,
+                              const int *positions, int n_pos, float *s_snap, float *z_snap, int B, int H, int N,
+                              int Dk, int Dv, int dtype, int phi, float eps, void *workspace, size_t workspace_bytes,
+                              void *hip_stream) {
+    LA_TRY(check_common(B, H, N, Dk, Dv, dtype, phi, eps));
+    LA_TRY(check_train(Dk, Dv, dtype));
+    if (!positions || !s_snap || !z_snap || n_pos < 1 || n_pos > LINATTN_MAX_SNAPSHOTS) return LINATTN_EINVAL;
+    SnapRequest req;
+    req.list.n = n_pos;
+    for (int i = 0; i < n_pos; ++i) {
+        if (positions[i] < 0 || positions[i] >= N) return LINATTN_EINVAL;
+        req.list.pos[i] = positions[i];
+    }
+    for (int i = n_pos; i < kMaxSnapshots; ++i) req.list.pos[i] = 0;
+    req.s_snap = s_snap;
+    req.z_snap = z_snap;
+    const size_t BH = (size_t)B * H;
+    const size_t nq = BH * N * Dk * 2, nv = BH * N * Dv * 2, ns = BH * n_pos * Dk * Dv * 4, nz = BH * n_pos * Dk * 4;
+    const void *others[7] = {q, k, v, o, alpha, s_final, z_final};
+    const size_t osz[7] = {nq, nq, nv, nv, BH * N * 4, BH * Dk * Dv * 4, BH * Dk * 4};
+    for (int b = 0; b < 7; ++b)
+        if (overlaps(s_snap, ns, others[b], osz[b]) || overlaps(z_snap, nz, others[b], osz[b])) return LINATTN_EINVAL;
+    if (overlaps(s_snap, ns, z_snap, nz)) return LINATTN_EINVAL;
+    return forward_impl(alpha != nullptr, q, k, v, alpha, o, s_init, z_init, s_final, z_final, B, H, N, Dk, Dv,
+                        dtype, phi, eps, workspace, workspace_bytes, hip_stream, nullptr, &req);
 }
 
 int linattn_backward(const void *q, const void *k, const void *v, const float *den, const void *dout, void *dq,

@@ -305,39 +305,26 @@ __device__ __forceinline__ float colsum_from_lds(const float *red, int col) {
 }
 
 // ====================================================================== kernels
-// Segment-state pass (see seg_state_bf16): dS = phi(K)^T V and dz over one
-// state sub-segment, plus the segment's gate product.
-// PHI: the feature map (0: elu + 1, 1: identity, kFeatElu: elu), fixed at
-// compile time so that phi costs no per-element select.  VBAR: the cell also
-// holds the column sums of V (Dv more floats after z), the constant part of
-// the state when the features are written 1 + elu.
-template <int DK, int DV, bool GATED, int PHI, bool VBAR = false>
-__global__ __launch_bounds__(kThreads8, 4) void seg_state8_bf16(const uint16_t *__restrict__ k,
-                                                                const uint16_t *__restrict__ v,
-                                                                const float *__restrict__ alpha,
-                                                                float *__restrict__ ws, float *__restrict__ gam, int N,
-                                                                int P, int P_run, int seg_len) {
+// Carry a state over tokens [t_begin, t_end) of head bh: st holds the state
+// before t_begin on entry and the state after t_end - 1 on return (gated: the
+// decay of each chunk applies to what st held).  The range's gate log2-sum
+// and zero count are added to seg_lsum, seg_zeros; with VBAR, the column sums
+// of this thread's V units are added to vsum (the unit layout repeats every
+// 512 units, so a thread's columns are the same in every chunk).  Two
+// workgroups share a compute unit, so one chunk of loads in flight per
+// workgroup (refilled as soon as it is staged) keeps both fed.
+template <int DK, int DV, bool GATED, int PHI, bool VBAR>
+__device__ __forceinline__ void range_state8(const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+                                             const float *__restrict__ alpha, size_t bh, int N, int t_begin,
+                                             int t_end, State8<DK, DV> &st, uint16_t *sK, uint16_t *sV,
+                                             float (&vsum)[8], float &seg_lsum, int &seg_zeros) {
     constexpr int phi_mode = PHI;
-    __shared__ __attribute__((aligned(16))) uint16_t sK[kChunk * Tile<DK>::RS];
-    __shared__ __attribute__((aligned(16))) uint16_t sV[kChunk * Tile<DV>::RS];
-
-    const int seg = blockIdx.x % P_run, bh = blockIdx.x / P_run;
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
-    const int t_begin = seg * seg_len;
-    const int t_end = min(N, t_begin + seg_len);
     const int nch = (t_end - t_begin + kChunk - 1) / kChunk;
-    const uint16_t *kb = k + ((size_t)bh * N + t_begin) * DK;
-    const uint16_t *vb = v + ((size_t)bh * N + t_begin) * DV;
-    const float *ab = GATED ? alpha + (size_t)bh * N + t_begin : nullptr;
-
-    State8<DK, DV> st;
-    state8_load<DK, DV>(st, nullptr, nullptr, w, lane);
+    const uint16_t *kb = k + (bh * N + t_begin) * DK;
+    const uint16_t *vb = v + (bh * N + t_begin) * DV;
+    const float *ab = GATED ? alpha + bh * N + t_begin : nullptr;
     const bf16x8 ones = bf16_ones8();
-    float seg_lsum = 0.f;
-    int seg_zeros = 0;
-    // VBAR: this thread's V columns are the same in every chunk (the unit
-    // layout repeats every 512 units), so it sums them over the whole range
-    float vsum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 
     struct Buf {
         Units<DK> k;
@@ -385,11 +372,40 @@ __global__ __launch_bounds__(kThreads8, 4) void seg_state8_bf16(const uint16_t *
         state8_update<DK, DV>(st, sK, sV, w, lane, ones, phi_mode ? 0.f : (float)(kChunk - valid));
         __syncthreads();
     };
-    // Two workgroups share a compute unit, so one chunk of loads in flight
-    // per workgroup (refilled as soon as it is staged) keeps both fed.
-    Buf b0;
-    issue(b0, 0);
-    for (int c = 0; c < nch; ++c) step(b0, c);
+    if (nch > 0) {
+        Buf b0;
+        issue(b0, 0);
+        for (int c = 0; c < nch; ++c) step(b0, c);
+    }
+}
+
+// Segment-state pass (see seg_state_bf16): dS = phi(K)^T V and dz over one
+// state sub-segment, plus the segment's gate product.
+// PHI: the feature map (0: elu + 1, 1: identity, kFeatElu: elu), fixed at
+// compile time so that phi costs no per-element select.  VBAR: the cell also
+// holds the column sums of V (Dv more floats after z), the constant part of
+// the state when the features are written 1 + elu.
+template <int DK, int DV, bool GATED, int PHI, bool VBAR = false>
+__global__ __launch_bounds__(kThreads8, 4) void seg_state8_bf16(const uint16_t *__restrict__ k,
+                                                                const uint16_t *__restrict__ v,
+                                                                const float *__restrict__ alpha,
+                                                                float *__restrict__ ws, float *__restrict__ gam, int N,
+                                                                int P, int P_run, int seg_len) {
+    __shared__ __attribute__((aligned(16))) uint16_t sK[kChunk * Tile<DK>::RS];
+    __shared__ __attribute__((aligned(16))) uint16_t sV[kChunk * Tile<DV>::RS];
+
+    const int seg = blockIdx.x % P_run, bh = blockIdx.x / P_run;
+    const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
+    const int t_begin = seg * seg_len;
+    const int t_end = min(N, t_begin + seg_len);
+
+    State8<DK, DV> st;
+    state8_load<DK, DV>(st, nullptr, nullptr, w, lane);
+    float seg_lsum = 0.f;
+    int seg_zeros = 0;
+    float vsum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    range_state8<DK, DV, GATED, PHI, VBAR>(k, v, alpha, bh, N, t_begin, t_end, st, sK, sV, vsum, seg_lsum,
+                                           seg_zeros);
     constexpr size_t E = (size_t)DK * DV + DK + (VBAR ? DV : 0);
     float *dst = ws + ((size_t)bh * P + seg) * E;
     state8_store<DK, DV>(st, dst, w, lane);
@@ -402,6 +418,54 @@ __global__ __launch_bounds__(kThreads8, 4) void seg_state8_bf16(const uint16_t *
         if (tid < DV) dst[DK * DV + DK + tid] = colsum_from_lds<DV>(red, tid);
     }
     if (GATED && tid == 0) gam[(size_t)bh * P + seg] = seg_zeros > 0 ? 0.f : __builtin_amdgcn_exp2f(seg_lsum);
+}
+
+// Snapshot positions of one call (the same for every (b, h)), passed by value
+// in the kernel arguments.
+constexpr int kMaxSnapshots = 256;
+struct SnapList {
+    int n;
+    int pos[kMaxSnapshots];
+};
+
+// State snapshots: (S, z) after token p for each listed p, written to
+// s_snap [BH][n][Dk][Dv] and z_snap [BH][n][Dk].  Each workgroup starts from
+// the last prefix cell at or before token p + 1 (cells of cell_len tokens,
+// the last one usable is max_cell; null cells: the initial state or zero at
+// token 0) and carries the state over the tokens from there through p, the
+// forward's own algebra (gated: the decays of those tokens apply to the
+// cell's state).  A snapshot just before a cell edge is a copy of the cell.
+template <int DK, int DV, bool GATED, int PHI>
+__global__ __launch_bounds__(kThreads8, 4) void snap_state8_bf16(
+    const uint16_t *__restrict__ k, const uint16_t *__restrict__ v, const float *__restrict__ alpha,
+    const float *__restrict__ cells, size_t cell_stride_bh, int cell_len, int max_cell,
+    const float *__restrict__ s_init, const float *__restrict__ z_init, float *__restrict__ s_snap,
+    float *__restrict__ z_snap, int N, SnapList snaps) {
+    __shared__ __attribute__((aligned(16))) uint16_t sK[kChunk * Tile<DK>::RS];
+    __shared__ __attribute__((aligned(16))) uint16_t sV[kChunk * Tile<DV>::RS];
+
+    const int i = blockIdx.x % snaps.n, bh = blockIdx.x / snaps.n;
+    const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
+    const int p = snaps.pos[i];
+    const int cell = cells ? min((p + 1) / cell_len, max_cell) : 0;
+    const int t_begin = cell * cell_len;
+
+    State8<DK, DV> st;
+    if (cells) {
+        const float *c0 = cells + bh * cell_stride_bh + (size_t)cell * (DK * DV + DK);
+        state8_load<DK, DV>(st, c0, c0 + DK * DV, w, lane);
+    } else {
+        state8_load<DK, DV>(st, s_init ? s_init + (size_t)bh * DK * DV : nullptr,
+                            z_init ? z_init + (size_t)bh * DK : nullptr, w, lane);
+    }
+    float seg_lsum = 0.f;
+    int seg_zeros = 0;
+    float vsum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    range_state8<DK, DV, GATED, PHI, false>(k, v, alpha, bh, N, t_begin, p + 1, st, sK, sV, vsum, seg_lsum,
+                                            seg_zeros);
+    const size_t o = (size_t)bh * snaps.n + i;
+    state8_store<DK, DV>(st, s_snap + o * DK * DV, w, lane);
+    state8_store_z<DK, DV>(st, z_snap + o * DK, w, lane);
 }
 
 // Causal output pass (see fwd_out_bf16): wave w serves query block w / 2 and

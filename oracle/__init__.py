@@ -128,6 +128,27 @@ def forward(q, k, v, s_init=None, z_init=None, *, alpha=None, eps=1e-6,
     return o, s, z
 
 
+def snapshots(q, k, v, positions, s_init=None, z_init=None, *, alpha=None, phi_mode=PHI_ELU1, nthreads=None):
+    """The summary after each listed token, in fp64: (S_p, z_p) is the final state of the
+    forward over tokens 0..p ("Linear Attention: what happens when you change the product
+    order", section "What a summary can't do": restoring a summary needs a copy taken at that
+    exact position).  Returns s [B, H, n, Dk, Dv], z [B, H, n, Dk].
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    a = _f64(alpha)
+    B, H, N, Dk = q.shape
+    Dv = v.shape[-1]
+    pos = [int(p) for p in positions]
+    s = np.empty((B, H, len(pos), Dk, Dv))
+    z = np.empty((B, H, len(pos), Dk))
+    for i, p in enumerate(pos):
+        assert 0 <= p < N
+        _, s[:, :, i], z[:, :, i] = forward(q[:, :, :p + 1], k[:, :, :p + 1], v[:, :, :p + 1], s_init, z_init,
+                                            alpha=None if a is None else a[:, :, :p + 1], phi_mode=phi_mode,
+                                            want_o=False, nthreads=nthreads)
+    return s, z
+
+
 def forward_gated(q, k, v, alpha, s_init=None, z_init=None, **kw):
     return forward(q, k, v, s_init, z_init, alpha=alpha, **kw)
 
