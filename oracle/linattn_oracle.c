@@ -378,6 +378,83 @@ int oracle_backward(const double *q, const double *k, const double *v,
     return err ? -1 : 0;
 }
 
+/* Delta rule ("Linear Attention: what happens when you change the product
+ * order", section "The summary runs out of room"): before writing, the
+ * summary is read with the key, and only the difference between the value
+ * and that read is written, so that re-reading with the same key returns the
+ * new value.  Per token, for one (batch, head) pair:
+ *   kh_t = phi(k_t) / |phi(k_t)|_2             (unit key; a zero key writes nothing)
+ *   u_t  = S_{t-1}^T kh_t                      (read before the write)
+ *   S_t  = S_{t-1} + beta_t kh_t (v_t - u_t)^T (write the difference; beta_t = 1 unless given)
+ *   o_t  = S_t^T phi(q_t)                      (read with the query; no normalizer)
+ * s holds the running state on entry and on exit. */
+static void delta_one(const double *q, const double *k, const double *v,
+                      const double *beta, double *o, double *s, int64_t N,
+                      int Dk, int Dv, int mode, double *kh, double *u)
+{
+    for (int64_t t = 0; t < N; ++t) {
+        const double *qt = q + t * Dk, *kt = k + t * Dk, *vt = v + t * Dv;
+        double nrm = 0.0;
+        for (int i = 0; i < Dk; ++i) {
+            kh[i] = phi(kt[i], mode);
+            nrm += kh[i] * kh[i];
+        }
+        nrm = sqrt(nrm);
+        for (int i = 0; i < Dk; ++i)
+            kh[i] = nrm > 0.0 ? kh[i] / nrm : 0.0;
+        for (int j = 0; j < Dv; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < Dk; ++i)
+                acc += s[(int64_t)i * Dv + j] * kh[i];
+            u[j] = acc;
+        }
+        const double b = beta ? beta[t] : 1.0;
+        for (int i = 0; i < Dk; ++i)
+            for (int j = 0; j < Dv; ++j)
+                s[(int64_t)i * Dv + j] += b * kh[i] * (vt[j] - u[j]);
+        if (o) {
+            for (int j = 0; j < Dv; ++j) {
+                double acc = 0.0;
+                for (int i = 0; i < Dk; ++i)
+                    acc += s[(int64_t)i * Dv + j] * phi(qt[i], mode);
+                o[t * Dv + j] = acc;
+            }
+        }
+    }
+}
+
+/* Delta-rule forward over BH pairs; beta [BH][N] or NULL (all ones); s_init
+ * NULL for zero; o, s_final may be NULL. */
+int oracle_delta(const double *q, const double *k, const double *v,
+                 const double *beta, const double *s_init, double *o,
+                 double *s_final, int64_t BH, int64_t N, int Dk, int Dv,
+                 int mode, int nthreads)
+{
+    if (!q || !k || !v || BH < 0 || N < 0 || Dk < 1 || Dv < 1)
+        return -1;
+    int err = 0;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads > 0 ? nthreads : 1)
+    for (int64_t bh = 0; bh < BH; ++bh) {
+        double *s = calloc((size_t)Dk * Dv, sizeof(double));
+        double *kh = malloc(sizeof(double) * Dk);
+        double *u = malloc(sizeof(double) * Dv);
+        if (!s || !kh || !u) {
+#pragma omp atomic write
+            err = 1;
+        } else {
+            if (s_init)
+                memcpy(s, s_init + bh * Dk * Dv, sizeof(double) * Dk * Dv);
+            delta_one(q + bh * N * Dk, k + bh * N * Dk, v + bh * N * Dv,
+                      beta ? beta + bh * N : NULL, o ? o + bh * N * Dv : NULL,
+                      s, N, Dk, Dv, mode, kh, u);
+            if (s_final)
+                memcpy(s_final + bh * Dk * Dv, s, sizeof(double) * Dk * Dv);
+        }
+        free(s); free(kh); free(u);
+    }
+    return err ? -1 : 0;
+}
+
 void oracle_phi(const double *x, double *y, int64_t n, int mode)
 {
     for (int64_t i = 0; i < n; ++i)

@@ -38,10 +38,20 @@ BACKWARD_MUTANTS = {
 }
 
 
-@pytest.mark.parametrize("name", sorted(MUTANTS) + sorted(BACKWARD_MUTANTS))
+DELTA_MUTANTS = {
+    "delta_key_not_unit": ("kh[i] = nrm > 0.0 ? kh[i] / nrm : 0.0;", "kh[i] = kh[i];"),
+    "delta_writes_value": ("b * kh[i] * (vt[j] - u[j]);", "b * kh[i] * vt[j];"),
+    "delta_beta_ignored": ("const double b = beta ? beta[t] : 1.0;", "const double b = 1.0;"),
+    "delta_read_with_query": ("acc += s[(int64_t)i * Dv + j] * kh[i];", "acc += s[(int64_t)i * Dv + j] * phi(q[t * Dk + i], mode);"),
+}
+PINS = {**{n: "test_oracle.py" for n in MUTANTS}, **{n: "test_oracle_backward.py" for n in BACKWARD_MUTANTS},
+        **{n: "test_oracle_delta.py" for n in DELTA_MUTANTS}}
+
+
+@pytest.mark.parametrize("name", sorted(PINS))
 def test_mutant_is_caught(name, tmp_path):
-    old, new = MUTANTS.get(name) or BACKWARD_MUTANTS[name]
-    pins = "test_oracle_backward.py" if name in BACKWARD_MUTANTS else "test_oracle.py"
+    old, new = {**MUTANTS, **BACKWARD_MUTANTS, **DELTA_MUTANTS}[name]
+    pins = PINS[name]
     src = open(SRC).read()
     assert src.count(old) >= 1, f"mutation site for {name} not found"
     mutated = src.replace(old, new, 1)
