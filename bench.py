@@ -169,8 +169,21 @@ def snapshots_case(name, dev, inputs=None):
     return w, fn, nbytes, pos
 
 
+def delta_case(name, dev):
+    """Delta rule over its own workload (beta absent: the full overwrite)."""
+    w = synth.WORKLOADS[name]
+    q, k, v = (x.to(dev) for x in synth.qkv(w))
+    o = torch.empty((w.B, w.H, w.N, w.Dv), dtype=w.dtype, device=dev)
+
+    def fn():
+        la.linattn_forward_delta(q, k, v, out=o)
+    return w, fn, rf.delta_bytes(w.B, w.H, w.N, w.Dk, w.Dv, 2)
+
+
 def kernel_bytes(kernel, w):
     """Algorithmic bytes one launch of a library kernel moves on workload w (None if not a whole-pass kernel)."""
+    if kernel == "delta_bf16":
+        return rf.delta_bytes(w.B, w.H, w.N, w.Dk, w.Dv, 2)
     if kernel.startswith("bwd_"):
         return rf.backward_kernel_bytes(kernel, w.B, w.H, w.N, w.Dk, w.Dv, 2)
     if kernel.startswith("fwd_out_bf16"):
@@ -190,6 +203,8 @@ def kernel_flops(kernel, w, path_flops):
         return path_flops
     if kernel.startswith("bwd_"):
         return rf.backward_kernel_flops(kernel, w.B, w.H, w.N, w.Dk, w.Dv)
+    if kernel == "delta_bf16":
+        return rf.delta_flops(w.B, w.H, w.N, w.Dk, w.Dv)
     return None
 
 
@@ -288,7 +303,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-paths", action="store_true")
-    ap.add_argument("--path", choices=["forward", "gated", "decode", "noncausal", "backward", "snapshots"],
+    ap.add_argument("--path", choices=["forward", "gated", "decode", "noncausal", "backward", "snapshots", "delta"],
                     default=None)
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
@@ -303,7 +318,7 @@ def main():
         copy_calibration(dev, args.steps)
         return
 
-    if args.path in ("decode", "gated", "noncausal", "backward", "snapshots"):
+    if args.path in ("decode", "gated", "noncausal", "backward", "snapshots", "delta"):
         # single-path run (used for counter collection); prints its own line
         run_single_path(args, dev, stream)
         return
@@ -379,6 +394,11 @@ def other_paths(args, dev, stream, headline_inputs):
     w, fn, nbytes = backward_case(HEADLINE, dev, headline_inputs)
     out["backward"] = path_entry(w, fn, nbytes, stream, args, w.B * w.N, key="backward_" + w.name,
                                  flops=rf.backward_flops(w.B, w.H, w.N, w.Dk, w.Dv))
+    del fn
+    log("[bench] delta rule")
+    w, fn, nbytes = delta_case("delta_b16h16_n4096_d128", dev)
+    out["delta"] = path_entry(w, fn, nbytes, stream, args, w.B * w.N,
+                              flops=rf.delta_flops(w.B, w.H, w.N, w.Dk, w.Dv))
     return out
 
 
@@ -389,6 +409,9 @@ def run_single_path(args, dev, stream):
     elif args.path == "decode":
         w, fn, nbytes, reset = decode_case(dev)
         r = path_entry(w, fn, nbytes, stream, args, w.B, reset=reset)
+    elif args.path == "delta":
+        w, fn, nbytes = delta_case("delta_b16h16_n4096_d128", dev)
+        r = path_entry(w, fn, nbytes, stream, args, w.B * w.N, flops=rf.delta_flops(w.B, w.H, w.N, w.Dk, w.Dv))
     elif args.path == "snapshots":
         w, fn, nbytes, _ = snapshots_case(HEADLINE, dev)
         r = path_entry(w, fn, nbytes, stream, args, w.B * w.N, key="snapshots_" + w.name)

@@ -173,6 +173,30 @@ int linattn_backward(const void *q, const void *k, const void *v,
                      void *hip_stream);
 
 /*
+ * Delta rule ("Linear Attention: what happens when you change the product
+ * order", section "The summary runs out of room": before writing, read the
+ * summary with the key and write only the difference to the value, so that
+ * re-reading with the same key returns the new value).  Per token:
+ *   kh_t = phi(k_t) / |phi(k_t)|_2   (unit key; a zero key writes nothing)
+ *   S_t  = S_{t-1} + beta_t kh_t (v_t - S_{t-1}^T kh_t)^T
+ *   o_t  = S_t^T phi(q_t)            (no normalizer)
+ *
+ *   beta      NULL (every beta_t = 1, the page's full overwrite) or
+ *             [B][H][N] fp32 write strengths.
+ *   s_init    NULL (zero) or [B][H][Dk][Dv] fp32; s_final NULL or output
+ *             [B][H][Dk][Dv] fp32 (may alias s_init).
+ *   o         output [B][H][N][Dv] bf16; must not overlap the inputs.
+ * Chunked bf16 path only (bf16, Dk and Dv in {64, 128}); no workspace.  One
+ * workgroup per (b, h): the heads run in parallel, the chunks of a sequence
+ * in order.
+ */
+int linattn_forward_delta(const void *q, const void *k, const void *v,
+                          const float *beta, void *o,
+                          const float *s_init, float *s_final,
+                          int B, int H, int N, int Dk, int Dv, int dtype,
+                          int phi, void *hip_stream);
+
+/*
  * Causal forward that also returns the summary after chosen tokens: for each
  * listed position p, S_p and z_p, the state once token p has been added (and
  * decayed, when gated).  The product-order page ("What a summary can't do")

@@ -14,6 +14,7 @@
 #include "fwd_bf16.hpp"
 #include "fwd8_bf16.hpp"
 #include "bwd8_bf16.hpp"
+#include "delta8_bf16.hpp"
 #include "recur.hpp"
 #include "scan_decode.hpp"
 
@@ -549,6 +550,42 @@ int linattn_forward_train(const void *q, const void *k, const void *v, void *o, 
         return LINATTN_EINVAL;
     return forward_impl(false, q, k, v, nullptr, o, s_init, z_init, s_final, z_final, B, H, N, Dk, Dv, dtype, phi,
                         eps, workspace, workspace_bytes, hip_stream, den);
+}
+
+int linattn_forward_delta(const void *q, const void *k, const void *v, const float *beta, void *o,
+                          const float *s_init, float *s_final, int B, int H, int N, int Dk, int Dv, int dtype,
+                          int phi, void *hip_stream) {
+    LA_TRY(check_common(B, H, N, Dk, Dv, dtype, phi, 0.f));
+    LA_TRY(check_train(Dk, Dv, dtype));
+    if (!q || !k || !v || !o) return LINATTN_EINVAL;
+    const size_t BH = (size_t)B * H;
+    const size_t nq = BH * N * Dk * 2, nv = BH * N * Dv * 2, ns = BH * Dk * Dv * 4;
+    const void *ins[5] = {q, k, v, beta, s_init};
+    const size_t insz[5] = {nq, nq, nv, BH * N * 4, ns};
+    for (int b = 0; b < 5; ++b)
+        if (overlaps(o, nv, ins[b], insz[b]) || (b < 4 && overlaps(s_final, ns, ins[b], insz[b])))
+            return LINATTN_EINVAL;
+    if (overlaps(o, nv, s_final, ns)) return LINATTN_EINVAL;
+    hipStream_t st = (hipStream_t)hip_stream;
+    auto run = [&](auto DKc, auto DVc) {
+        constexpr int DK = decltype(DKc)::value, DV = decltype(DVc)::value;
+        return launch("delta_bf16", st, [&] {
+            with_phi(phi, [&](auto PH) {
+                if (beta)
+                    delta8_bf16<DK, DV, PH(), true><<<dim3((unsigned)BH), dim3(kThreads8), 0, st>>>(
+                        (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, beta, (uint16_t *)o, s_init,
+                        s_final, N);
+                else
+                    delta8_bf16<DK, DV, PH(), false><<<dim3((unsigned)BH), dim3(kThreads8), 0, st>>>(
+                        (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, nullptr, (uint16_t *)o, s_init,
+                        s_final, N);
+            });
+        });
+    };
+    using I64 = std::integral_constant<int, 64>;
+    using I128 = std::integral_constant<int, 128>;
+    if (Dk == 64) return Dv == 64 ? run(I64{}, I64{}) : run(I64{}, I128{});
+    return Dv == 64 ? run(I128{}, I64{}) : run(I128{}, I128{});
 }
 
 int linattn_forward_snapshots(const void *q, const void *k, const void *v, const float *alpha, void *o,

@@ -1,0 +1,293 @@
+// delta8_bf16.hpp -- the delta rule, chunked, eight waves per workgroup, head
+// dims Dk, Dv in {64, 128}, bf16 in and out, fp32 state.
+//
+// Per token ("Linear Attention: what happens when you change the product
+// order", section "The summary runs out of room": read with the key before
+// writing, write only the difference):
+//   kh_t = phi(k_t) / |phi(k_t)|,  S_t = S_{t-1} + beta_t kh_t (v_t - S_{t-1}^T kh_t)^T,
+//   o_t  = S_t^T phi(q_t).
+// With S_0 the state at a chunk's start and D the chunk's rows
+// delta_t = beta_t (v_t - S_{t-1}^T kh_t), expanding S_{t-1} over the chunk
+// gives, for the chunk's rows (Kh, Q, V, beta):
+//   (I + diag(beta) tril(Kh Kh^T, -1)) D = diag(beta) (V - Kh S_0)
+//   O = Q S_0 + tril(Q Kh^T) D      (diagonal included)
+//   S_C = S_0 + Kh^T D.
+// The unit lower-triangular system is solved by forward substitution in fp32
+// (one thread per value column); everything else is bf16 MFMA with fp32
+// accumulation, in the tile layouts and wave pairing of fwd8_bf16.hpp.  One
+// workgroup carries one (b, h) through its chunks in order.
+#pragma once
+
+#include "bwd8_bf16.hpp"
+
+namespace linattn {
+
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi), eight at a time, as
+// MFMA operands (hi carries 8 significant bits, hi + lo about 16).
+__device__ __forceinline__ void split_bf16x8(const float (&x)[8], bf16x8 &hi, bf16x8 &lo) {
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        h[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
+        l[e] = pack_bf16x2(x[2 * e] - bf_lo(h[e]), x[2 * e + 1] - bf_hi(h[e]));
+    }
+    hi = as_bf16x8(make_uint4(h[0], h[1], h[2], h[3]));
+    lo = as_bf16x8(make_uint4(l[0], l[1], l[2], l[3]));
+}
+
+template <int DK, int DV, int PHI, bool BETA>
+__global__ __launch_bounds__(kThreads8, 1) void delta8_bf16(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    const float *__restrict__ beta, uint16_t *__restrict__ o, const float *__restrict__ s_init,
+    float *__restrict__ s_final, int N) {
+    using TK = Tile<DK>;
+    using TV = Tile<DV>;
+    constexpr int KSK = DK / 32;
+    constexpr int NTV = DV / 16 / 2; // value tiles per wave
+    constexpr int XS = DV + 4;       // fp32 row stride of the right-hand side / solution
+    constexpr int AS = kChunk + 4;   // fp32 row stride of the coupling matrix
+    __shared__ __attribute__((aligned(16))) uint16_t sQ[kChunk * TK::RS]; // phi(Q)
+    __shared__ __attribute__((aligned(16))) uint16_t sK[kChunk * TK::RS]; // unit keys
+    __shared__ __attribute__((aligned(16))) uint16_t sV[kChunk * TV::RS]; // V, then D (bf16)
+    __shared__ __attribute__((aligned(16))) uint16_t sS[DK * DV];         // S_0 in bf16
+    __shared__ __attribute__((aligned(16))) float sX[kChunk * XS];        // diag(beta)(V - Kh S_0), then D
+    __shared__ __attribute__((aligned(16))) float sA[kChunk * AS];        // diag(beta) tril(Kh Kh^T, -1)
+    __shared__ __attribute__((aligned(16))) float sB[kChunk];             // beta (0 past the end)
+
+    const size_t bh = blockIdx.x;
+    const int tid = threadIdx.x, w = wave_id();
+    const int blk_w = w < 4 ? (w >> 1) : 5 - (w >> 1), dh = w & 1;
+    const bf16x8 ones = bf16_ones8();
+    const int nch = (N + kChunk - 1) / kChunk;
+    const size_t row0 = bh * N;
+
+    State8<DK, DV> st;
+    state8_load<DK, DV>(st, s_init ? s_init + bh * DK * DV : nullptr, nullptr, w, tid & 63);
+    state8_to_lds<DK, DV>(st, sS, w, tid & 63);
+
+    struct Buf {
+        Units<DK> q, k;
+        Units<DV> v;
+    };
+    auto rows_in = [&](int c) { return min(kChunk, N - c * kChunk); };
+    auto issue = [&](Buf &b, int c) {
+        const size_t r = row0 + (size_t)c * kChunk;
+        const int nv = rows_in(c);
+        b.q.load(q + r * DK, nv, tid);
+        b.k.load(k + r * DK, nv, tid);
+        b.v.load(v + r * DV, nv, tid);
+    };
+    Buf buf;
+    if (nch > 0) issue(buf, 0);
+    for (int c = 0; c < nch; ++c) {
+        const int valid = rows_in(c);
+        // ---- stage phi(Q), unit keys (zero past the end), V, beta
+        {
+            constexpr int CG = Units<DK>::CG;
+#pragma unroll
+            for (int i = 0; i < Units<DK>::N; ++i) {
+                const int row = Units<DK>::row_of(tid, i), col = Units<DK>::col_of(tid, i);
+                *reinterpret_cast<uint4 *>(sQ + TK::off(row, col)) = phi_pack8(buf.q.r[i], PHI);
+                const uint32_t kw[4] = {buf.k.r[i].x, buf.k.r[i].y, buf.k.r[i].z, buf.k.r[i].w};
+                float f[8], nrm = 0.f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    f[2 * e] = phi_fast(bf_lo(kw[e]), PHI);
+                    f[2 * e + 1] = phi_fast(bf_hi(kw[e]), PHI);
+                    nrm = fmaf(f[2 * e], f[2 * e], fmaf(f[2 * e + 1], f[2 * e + 1], nrm));
+                }
+#pragma unroll
+                for (int m = 1; m < CG; m <<= 1) nrm += __shfl_xor(nrm, m, 64);
+                // a zero key (or a row past the end) writes nothing
+                const float inv = (row < valid && nrm > 0.f) ? 1.f / sqrtf(nrm) : 0.f;
+                *reinterpret_cast<uint4 *>(sK + TK::off(row, col)) =
+                    make_uint4(pack_bf16x2(f[0] * inv, f[1] * inv), pack_bf16x2(f[2] * inv, f[3] * inv),
+                               pack_bf16x2(f[4] * inv, f[5] * inv), pack_bf16x2(f[6] * inv, f[7] * inv));
+            }
+#pragma unroll
+            for (int i = 0; i < Units<DV>::N; ++i)
+                *reinterpret_cast<uint4 *>(sV + TV::off(Units<DV>::row_of(tid, i), Units<DV>::col_of(tid, i))) =
+                    buf.v.r[i];
+            if (tid < kChunk) {
+                const size_t r = row0 + (size_t)c * kChunk + tid;
+                sB[tid] = tid < valid ? (BETA ? beta[r] : 1.f) : 0.f;
+            }
+        }
+        if (c + 1 < nch) issue(buf, c + 1);
+        __syncthreads();
+
+        // ---- right-hand side diag(beta)(V - Kh S_0) and the coupling diag(beta) tril(Kh Kh^T, -1)
+        {
+            const int lane = lane_in_loop(tid & 63);
+            const int l16 = lane & 15, g = lane >> 4, qd = lane & 3;
+            const int tk = 16 * blk_w + l16; // this wave's keys
+            bf16x8 ka[KSK];
+#pragma unroll
+            for (int ks = 0; ks < KSK; ++ks) ka[ks] = *reinterpret_cast<const bf16x8 *>(sK + TK::off(tk, 32 * ks + 8 * g));
+            // (Kh S_0)^T tiles: value rows (permuted), key columns
+#pragma unroll
+            for (int j = 0; j < NTV; ++j) {
+                f32x4 r = f32x4{0.f, 0.f, 0.f, 0.f};
+                const int nt = dh * NTV + j;
+                const int colq = 32 * (nt >> 1) + 8 * qd + 4 * (nt & 1);
+#pragma unroll
+                for (int ks = 0; ks < KSK; ++ks) {
+                    const int klo = 32 * ks + 8 * g;
+                    r = mfma16x16x32(tr_operand_in<TileS<DV>>(sS, klo, klo + 4, colq, lane), ka[ks], r);
+                }
+                // lane holds key tk, values 32 (nt >> 1) + 8 g + 4 (nt & 1) + i
+                const int vc = 32 * (nt >> 1) + 8 * g + 4 * (nt & 1);
+                const uint2 vv = *reinterpret_cast<const uint2 *>(sV + TV::off(tk, vc));
+                const float b = sB[tk];
+                *reinterpret_cast<float4 *>(sX + tk * XS + vc) =
+                    make_float4(b * (bf_lo(vv.x) - r[0]), b * (bf_hi(vv.x) - r[1]), b * (bf_lo(vv.y) - r[2]),
+                                b * (bf_hi(vv.y) - r[3]));
+            }
+            // Gram blocks (row block blk_w, column blocks dh, dh + 2 at or below it)
+#pragma unroll
+            for (int cb2 = 0; cb2 < 2; ++cb2) {
+                const int cb = dh + 2 * cb2;
+                if (cb <= blk_w) {
+                    f32x4 gr = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < KSK; ++ks)
+                        gr = mfma16x16x32(
+                            *reinterpret_cast<const bf16x8 *>(sK + TK::off(16 * cb + l16, 32 * ks + 8 * g)), ka[ks],
+                            gr);
+                    // gr[i] = Kh[16 cb + 4 g + i] . Kh[tk]: the coupling A[tk][j] for
+                    // j = 16 cb + 4 g + i, strictly below the diagonal
+                    const float b = sB[tk];
+                    float4 a4;
+                    a4.x = 16 * cb + 4 * g + 0 < tk ? b * gr[0] : 0.f;
+                    a4.y = 16 * cb + 4 * g + 1 < tk ? b * gr[1] : 0.f;
+                    a4.z = 16 * cb + 4 * g + 2 < tk ? b * gr[2] : 0.f;
+                    a4.w = 16 * cb + 4 * g + 3 < tk ? b * gr[3] : 0.f;
+                    *reinterpret_cast<float4 *>(sA + tk * AS + 16 * cb + 4 * g) = a4;
+                } else {
+                    *reinterpret_cast<float4 *>(sA + tk * AS + 16 * cb + 4 * g) = make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---- forward substitution: D_i = X_i - sum_{j < i} A_ij D_j, one thread per
+        // value column; four partial sums per row keep the dependent chains short
+        if (tid < DV) {
+            float d[kChunk];
+#pragma unroll
+            for (int i = 0; i < kChunk; ++i) {
+                const float *ai = sA + i * AS;
+                float x0 = sX[i * XS + tid], x1 = 0.f, x2 = 0.f, x3 = 0.f;
+#pragma unroll
+                for (int j = 0; j + 3 < i; j += 4) {
+                    const float4 a4 = *reinterpret_cast<const float4 *>(ai + j);
+                    x0 = fmaf(-a4.x, d[j], x0);
+                    x1 = fmaf(-a4.y, d[j + 1], x1);
+                    x2 = fmaf(-a4.z, d[j + 2], x2);
+                    x3 = fmaf(-a4.w, d[j + 3], x3);
+                }
+#pragma unroll
+                for (int j = i & ~3; j < i; ++j) x0 = fmaf(-ai[j], d[j], x0);
+                d[i] = (x0 + x1) + (x2 + x3);
+            }
+#pragma unroll
+            for (int i = 0; i < kChunk; ++i) {
+                sX[i * XS + tid] = d[i];
+                sV[TV::off(i, tid)] = (uint16_t)f32_to_bf16_bits(d[i]);
+            }
+        }
+        __syncthreads();
+
+        // ---- outputs O^T = S_0^T phi(Q)^T + D^T tril(Q Kh^T)^T, and the state update
+        {
+            const int lane = lane_in_loop(tid & 63);
+            const int l16 = lane & 15, g = lane >> 4, qd = lane & 3;
+            auto chunk_out = [&](auto blk_c) {
+                constexpr int qblk = decltype(blk_c)::value;
+                const int tq = 16 * qblk + l16;
+                bf16x8 qa[KSK];
+#pragma unroll
+                for (int ks = 0; ks < KSK; ++ks)
+                    qa[ks] = *reinterpret_cast<const bf16x8 *>(sQ + TK::off(tq, 32 * ks + 8 * g));
+                f32x4 acc[NTV];
+#pragma unroll
+                for (int j = 0; j < NTV; ++j) {
+                    acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    const int nt = dh * NTV + j;
+                    const int colq = 32 * (nt >> 1) + 8 * qd + 4 * (nt & 1);
+#pragma unroll
+                    for (int ks = 0; ks < KSK; ++ks) {
+                        const int klo = 32 * ks + 8 * g;
+                        acc[j] = mfma16x16x32(tr_operand_in<TileS<DV>>(sS, klo, klo + 4, colq, lane), qa[ks], acc[j]);
+                    }
+                }
+                // scores^T [key][query] = Kh_key . phi(q)_query, keys at or before the query
+                f32x4 sc[4];
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) {
+                    sc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    if (kb <= qblk) {
+#pragma unroll
+                        for (int ks = 0; ks < KSK; ++ks)
+                            sc[kb] = mfma16x16x32(
+                                *reinterpret_cast<const bf16x8 *>(sK + TK::off(16 * kb + l16, 32 * ks + 8 * g)),
+                                qa[ks], sc[kb]);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (kb == qblk && 4 * g + i > l16) sc[kb][i] = 0.f;
+                    }
+                }
+                // D^T tril(.)^T with both factors split into bf16 high and low
+                // parts (three products): the new writes largely cancel the
+                // old summary along the keys, and one bf16 rounding of either
+                // factor shows in O at the percent level
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    if (2 * s2 <= qblk) {
+                        float x[8];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            x[i] = sc[2 * s2][i];
+                            x[4 + i] = sc[2 * s2 + 1][i];
+                        }
+                        bf16x8 bhi, blo;
+                        split_bf16x8(x, bhi, blo);
+                        const int klo = 32 * s2 + 4 * g, khi = klo + 16;
+#pragma unroll
+                        for (int j = 0; j < NTV; ++j) {
+                            const int nt = dh * NTV + j;
+                            // this lane's column of D (value perm_dv(nt, l16)), rows klo.. and khi..
+                            const int col = perm_dv(nt, l16);
+                            float dcol[8];
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                dcol[r] = sX[(klo + r) * XS + col];
+                                dcol[4 + r] = sX[(khi + r) * XS + col];
+                            }
+                            bf16x8 dhi, dlo;
+                            split_bf16x8(dcol, dhi, dlo);
+                            acc[j] = mfma16x16x32(dhi, bhi, acc[j]);
+                            acc[j] = mfma16x16x32(dlo, bhi, acc[j]);
+                            acc[j] = mfma16x16x32(dhi, blo, acc[j]);
+                        }
+                    }
+                }
+                store_grad_rows<DV, NTV, kScaleNone, PHI>(acc, dh * NTV, nullptr, tq,
+                                                          o + (row0 + (size_t)c * kChunk + tq) * DV, tq < valid, g);
+            };
+            switch (blk_w) {
+            case 0: chunk_out(std::integral_constant<int, 0>{}); break;
+            case 1: chunk_out(std::integral_constant<int, 1>{}); break;
+            case 2: chunk_out(std::integral_constant<int, 2>{}); break;
+            default: chunk_out(std::integral_constant<int, 3>{}); break;
+            }
+            // S += Kh^T D (rows past the end have zero keys; z is not used)
+            state8_update<DK, DV>(st, sK, sV, w, lane, ones, 0.f);
+        }
+        __syncthreads();
+        if (c + 1 < nch) state8_to_lds<DK, DV>(st, sS, w, tid & 63);
+    }
+    if (s_final) state8_store<DK, DV>(st, s_final + bh * DK * DV, w, tid & 63);
+}
+
+} // namespace linattn

@@ -64,6 +64,16 @@ def backward_flops(B, H, N, Dk, Dv) -> int:
     return 10 * B * H * N * Dk * Dv
 
 
+def delta_bytes(B, H, N, Dk, Dv, in_bytes) -> int:
+    """Delta rule: Q, K, V read once, O written once, the final state written once (fp32)."""
+    return B * H * (N * (2 * Dk + 2 * Dv) * in_bytes + Dk * Dv * 4)
+
+
+def delta_flops(B, H, N, Dk, Dv) -> int:
+    """Per token 2 Dk Dv each for the read with the key, the write and the read with the query."""
+    return 6 * B * H * N * Dk * Dv
+
+
 def method_flops(B, H, N, Dk, Dv) -> int:
     """Write S += phi(k) v^T and read phi(q)^T S per token: 2 Dk Dv each."""
     return 4 * B * H * N * Dk * Dv

@@ -119,6 +119,10 @@ WORKLOADS = {
     "gated_b2h16_n16384_d128": Workload("gated_b2h16_n16384_d128", 2, 16, 16384, 128, 128,
                                         torch.bfloat16, 1005, q_scale=_R128, k_scale=_R128,
                                         v_scale=_R128, gated=True),
+    # delta rule: unscaled q, k (elu + 1 of N(0, 1), so that the unit keys are
+    # far from all parallel), 256 heads (one workgroup each)
+    "delta_b16h16_n4096_d128": Workload("delta_b16h16_n4096_d128", 16, 16, 4096, 128, 128,
+                                        torch.bfloat16, 1006),
 }
 
 

@@ -176,3 +176,40 @@ def test_training_forward_and_backward_reject_bad_arguments(L):
     assert bwd(L, N=131072) == EWORKSPACE
     need = L.linattn_workspace_size(3, 1, 1, 131072, 64, 64, 1)
     assert bwd(L, N=131072, ws=FAKE[10], wsb=need - 1) == EWORKSPACE
+
+
+def delta(L, q=FAKE[0], k=FAKE[1], v=FAKE[2], beta=None, o=FAKE[3], si=None, sf=None, B=1, H=1, N=64, Dk=64,
+          Dv=64, dtype=1, phi=0):
+    return L.linattn_forward_delta(q, k, v, beta, o, si, sf, B, H, N, Dk, Dv, dtype, phi, None)
+
+
+def test_delta_rejects_bad_arguments(L):
+    assert delta(L, dtype=0) == EDTYPE
+    assert delta(L, Dk=32) == ESHAPE
+    assert delta(L, phi=7) == EDTYPE
+    for name in ("q", "k", "v", "o"):
+        assert delta(L, **{name: None}) == EINVAL, name
+    assert delta(L, o=FAKE[0]) == EINVAL    # o overlaps q
+    assert delta(L, sf=FAKE[3]) == EINVAL   # s_final overlaps o
+    assert delta(L, N=0) == EINVAL
+
+
+def snaps(L, positions=(0, 5), n=None, ss=FAKE[6], zs=FAKE[7], N=64, Dk=64, Dv=64, dtype=1, alpha=None):
+    arr = (ctypes.c_int * max(1, len(positions)))(*positions) if positions is not None else None
+    n = len(positions) if n is None and positions is not None else (n or 0)
+    return L.linattn_forward_snapshots(FAKE[0], FAKE[1], FAKE[2], alpha, FAKE[3], None, None, None, None,
+                                       ctypes.cast(arr, ctypes.c_void_p) if arr is not None else None, n, ss, zs,
+                                       1, 1, N, Dk, Dv, dtype, 0, 1e-6, None, 0, None)
+
+
+def test_snapshots_reject_bad_arguments(L):
+    assert snaps(L, dtype=0) == EDTYPE
+    assert snaps(L, Dk=16, Dv=16) == ESHAPE
+    assert snaps(L, positions=None) == EINVAL
+    assert snaps(L, positions=[0], n=0) == EINVAL
+    assert snaps(L, positions=list(range(257)), N=1000) == EINVAL  # more than LINATTN_MAX_SNAPSHOTS
+    assert snaps(L, positions=[64]) == EINVAL                       # past the end (N = 64)
+    assert snaps(L, positions=[-1]) == EINVAL
+    assert snaps(L, ss=None) == EINVAL
+    assert snaps(L, ss=FAKE[0]) == EINVAL                           # s_snap overlaps q
+    assert snaps(L, zs=FAKE[6]) == EINVAL                           # z_snap overlaps s_snap

@@ -1,0 +1,88 @@
+"""GPU parity of the delta rule against the fp64 oracle.
+
+linattn_forward_delta runs through the C ABI; O is compared row-normwise and
+the final state per head with oracle.delta on the same seeded bf16 inputs
+(q, k, v drawn N(0, 1): with elu + 1 the unit keys are then far from all
+parallel).  Shapes span several chunks, ragged tails, one token, both head
+dims and their mix; beta absent (full overwrite) or drawn in (0, 1); an
+initial state; and the product-order page's worked example (keys in two of 64
+dims, the identity map) on the GPU path.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linear_attention_phi_amd import binding as la
+from linear_attention_phi_amd import synth
+from parity import TOL, assert_close
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+BF = torch.bfloat16
+
+
+def make(B, H, N, Dk, Dv, seed, with_beta=False):
+    w = synth.Workload("t", B, H, N, Dk, Dv, BF, seed)
+    q, k, v = synth.qkv(w)
+    beta = None
+    if with_beta:
+        beta = torch.sigmoid(synth.normal_heads(seed, synth.G_ID, B, H, N, 1, 1.0, torch.float32)[..., 0])
+    return q, k, v, beta
+
+
+def check(q, k, v, beta=None, s0=None, phi=la.PHI_ELU1):
+    d = [x.to(DEV) for x in (q, k, v)]
+    o, s = la.linattn_forward_delta(*d, None if beta is None else beta.to(DEV),
+                                    None if s0 is None else s0.to(DEV), phi=phi)
+    torch.cuda.synchronize()
+    ro, rs = oracle.delta(q, k, v, beta, s0, phi_mode=phi)
+    tol = TOL[BF]
+    assert_close("O", o.cpu(), ro, tol)
+    assert_close("S", s.cpu(), rs, tol, per="head")
+    return o, s
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 700, 64, 64), (2, 2, 1000, 128, 128), (1, 3, 333, 64, 128),
+                                   (1, 1, 1, 128, 128), (1, 1, 65, 128, 64), (4, 4, 200, 128, 128)])
+def test_delta(shape):
+    check(*make(*shape, seed=1200 + sum(shape)))
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 700, 128, 128), (2, 1, 130, 64, 64)])
+def test_delta_with_beta(shape):
+    check(*make(*shape, seed=1220 + sum(shape), with_beta=True))
+
+
+def test_delta_with_initial_state_and_resume():
+    q, k, v, beta = make(1, 2, 600, 128, 128, seed=1230, with_beta=True)
+    s0 = torch.randn(1, 2, 128, 128, generator=torch.Generator().manual_seed(7)) * 0.1
+    o, s = check(q, k, v, beta, s0)
+    # two calls (the second from the first's final state) give the same tail
+    o1, s1 = la.linattn_forward_delta(q[:, :, :256].to(DEV), k[:, :, :256].to(DEV), v[:, :, :256].to(DEV),
+                                      beta[:, :, :256].to(DEV), s0.to(DEV))
+    o2, s2 = la.linattn_forward_delta(q[:, :, 256:].to(DEV), k[:, :, 256:].to(DEV), v[:, :, 256:].to(DEV),
+                                      beta[:, :, 256:].to(DEV), s1)
+    torch.cuda.synchronize()
+    assert torch.equal(o2.cpu(), o[:, :, 256:].cpu()) and torch.equal(s2.cpu(), s.cpu())
+
+
+def test_worked_example_on_the_gpu():
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "summary_scalar_values.json")))
+    D = 64
+    keys = np.zeros((3, D))
+    keys[:, :2] = g["keys"]
+    vals = np.zeros((3, D))
+    vals[:, 0] = g["values"]
+    qs = keys.copy()
+    qs[2] = 0.0
+    qs[2, 0] = 1.0  # the last read uses the query (1, 0)
+    q, k, v = (torch.tensor(x[None, None], dtype=BF) for x in (qs, keys, vals))
+    o, s = check(q, k, v, phi=la.PHI_IDENTITY)
+    p = g["printed"]["delta_rule"]
+    # bf16 inputs (0.6 and 0.8 are not exact in bf16) and bf16 operands: within 1%
+    np.testing.assert_allclose(s[0, 0, :2, 0].cpu().numpy(), p["state"], rtol=1e-2)
+    np.testing.assert_allclose(float(o[0, 0, 2, 0]), p["read_with_1_0"], rtol=1e-2)
