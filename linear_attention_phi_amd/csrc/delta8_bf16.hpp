@@ -12,8 +12,9 @@
 //   (I + diag(beta) tril(Kh Kh^T, -1)) D = diag(beta) (V - Kh S_0)
 //   O = Q S_0 + tril(Q Kh^T) D      (diagonal included)
 //   S_C = S_0 + Kh^T D.
-// The unit lower-triangular system is solved by forward substitution in fp32
-// (one thread per value column); everything else is bf16 MFMA with fp32
+// The unit lower-triangular system is solved in 16-row blocks: the inverses of
+// the diagonal blocks by forward substitution in fp32, the rest as MFMA
+// products on bf16 high/low parts; everything else is bf16 MFMA with fp32
 // accumulation, in the tile layouts and wave pairing of fwd8_bf16.hpp.  One
 // workgroup carries one (b, h) through its chunks in order.
 #pragma once
@@ -35,6 +36,33 @@ __device__ __forceinline__ void split_bf16x8(const float (&x)[8], bf16x8 &hi, bf
     lo = as_bf16x8(make_uint4(l[0], l[1], l[2], l[3]));
 }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// The same split for four values, as operands of the 16 x 16 x 16 bf16 MFMA.
+__device__ __forceinline__ void split_bf16x4(float a, float b, float c, float d, s16x4 &hi, s16x4 &lo) {
+    const uint32_t h0 = pack_bf16x2(a, b), h1 = pack_bf16x2(c, d);
+    const uint32_t l0 = pack_bf16x2(a - bf_lo(h0), b - bf_hi(h0)), l1 = pack_bf16x2(c - bf_lo(h1), d - bf_hi(h1));
+    hi = __builtin_bit_cast(s16x4, make_uint2(h0, h1));
+    lo = __builtin_bit_cast(s16x4, make_uint2(l0, l1));
+}
+
+// 16 x 16 x 16 bf16 MFMA, fp32 accumulate.  Lane l supplies A[l%16][4(l/16)+i],
+// B[4(l/16)+i][l%16] and receives C[4(l/16)+i][l%16] (i = 0..3), so a result
+// is directly the B operand of a following product over its rows.
+__device__ __forceinline__ f32x4 mfma16x16x16(s16x4 a, s16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// a b + c with both factors split into bf16 high and low parts (three products).
+__device__ __forceinline__ f32x4 mfma16_split(float4 a, f32x4 b, f32x4 c) {
+    s16x4 ahi, alo, bhi, blo;
+    split_bf16x4(a.x, a.y, a.z, a.w, ahi, alo);
+    split_bf16x4(b[0], b[1], b[2], b[3], bhi, blo);
+    c = mfma16x16x16(ahi, bhi, c);
+    c = mfma16x16x16(alo, bhi, c);
+    return mfma16x16x16(ahi, blo, c);
+}
+
 template <int DK, int DV, int PHI, bool BETA>
 __global__ __launch_bounds__(kThreads8, 1) void delta8_bf16(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
@@ -53,6 +81,7 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8_bf16(
     __shared__ __attribute__((aligned(16))) float sX[kChunk * XS];        // diag(beta)(V - Kh S_0), then D
     __shared__ __attribute__((aligned(16))) float sA[kChunk * AS];        // diag(beta) tril(Kh Kh^T, -1)
     __shared__ __attribute__((aligned(16))) float sB[kChunk];             // beta (0 past the end)
+    __shared__ __attribute__((aligned(16))) float sT[4 * 16 * 16];        // inverses of A's diagonal blocks
 
     const size_t bh = blockIdx.x;
     const int tid = threadIdx.x, w = wave_id();
@@ -170,30 +199,54 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8_bf16(
         }
         __syncthreads();
 
-        // ---- forward substitution: D_i = X_i - sum_{j < i} A_ij D_j, one thread per
-        // value column; four partial sums per row keep the dependent chains short
-        if (tid < DV) {
-            float d[kChunk];
+        // ---- solve (I + A) D = X.  Wave 0 inverts the four 16 x 16 diagonal
+        // blocks (lane = block * 16 + column: forward substitution on a unit
+        // vector); then each wave takes 16 value columns through the blocks in
+        // order, Y_b = X_b - sum_{k < b} A_bk D_k and D_b = (I + A_bb)^-1 Y_b, as
+        // 16 x 16 x 16 MFMAs on bf16 high and low parts (about 16 significant
+        // bits), with no workgroup barrier in between.
+        if (w == 0) {
+            const int lane = tid & 63;
+            const int b = lane >> 4, cc = lane & 15;
+            const float *ab = sA + 16 * b * AS + 16 * b;
+            float t[16];
 #pragma unroll
-            for (int i = 0; i < kChunk; ++i) {
-                const float *ai = sA + i * AS;
-                float x0 = sX[i * XS + tid], x1 = 0.f, x2 = 0.f, x3 = 0.f;
+            for (int r = 0; r < 16; ++r) {
+                float x = r == cc ? 1.f : 0.f;
 #pragma unroll
-                for (int j = 0; j + 3 < i; j += 4) {
-                    const float4 a4 = *reinterpret_cast<const float4 *>(ai + j);
-                    x0 = fmaf(-a4.x, d[j], x0);
-                    x1 = fmaf(-a4.y, d[j + 1], x1);
-                    x2 = fmaf(-a4.z, d[j + 2], x2);
-                    x3 = fmaf(-a4.w, d[j + 3], x3);
-                }
-#pragma unroll
-                for (int j = i & ~3; j < i; ++j) x0 = fmaf(-ai[j], d[j], x0);
-                d[i] = (x0 + x1) + (x2 + x3);
+                for (int j = 0; j < r; ++j) x = fmaf(-ab[r * AS + j], t[j], x);
+                t[r] = x;
             }
 #pragma unroll
-            for (int i = 0; i < kChunk; ++i) {
-                sX[i * XS + tid] = d[i];
-                sV[TV::off(i, tid)] = (uint16_t)f32_to_bf16_bits(d[i]);
+            for (int r = 0; r < 16; ++r) sT[(16 * b + r) * 16 + cc] = t[r];
+        }
+        __syncthreads();
+        if (w < DV / 16) {
+            const int lane = lane_in_loop(tid & 63);
+            const int l16 = lane & 15, g = lane >> 4;
+            const int col = 16 * w + l16;
+            f32x4 dblk[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                f32x4 y;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) y[i] = sX[(16 * b + 4 * g + i) * XS + col];
+#pragma unroll
+                for (int kb = 0; kb < b; ++kb) {
+                    const float4 a4 = *reinterpret_cast<const float4 *>(sA + (16 * b + l16) * AS + 16 * kb + 4 * g);
+                    y = mfma16_split(make_float4(-a4.x, -a4.y, -a4.z, -a4.w), dblk[kb], y);
+                }
+                const float4 t4 = *reinterpret_cast<const float4 *>(sT + (16 * b + l16) * 16 + 4 * g);
+                dblk[b] = mfma16_split(t4, y, f32x4{0.f, 0.f, 0.f, 0.f});
+            }
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 16 * b + 4 * g + i;
+                    sX[row * XS + col] = dblk[b][i];
+                    sV[TV::off(row, col)] = (uint16_t)f32_to_bf16_bits(dblk[b][i]);
+                }
             }
         }
         __syncthreads();
