@@ -58,7 +58,7 @@ extern "C" {
 #define LINATTN_ABI_VERSION 2
 #define LINATTN_MAX_SNAPSHOTS 256
 
-enum linattn_dtype { LINATTN_F32 = 0, LINATTN_BF16 = 1 };
+enum linattn_dtype { LINATTN_F32 = 0, LINATTN_BF16 = 1, LINATTN_FP8_E4M3 = 2 /* state storage only */ };
 enum linattn_phi { LINATTN_PHI_ELU1 = 0, LINATTN_PHI_IDENTITY = 1 };
 enum linattn_kind {
     LINATTN_KIND_FORWARD = 0,
@@ -259,6 +259,27 @@ int linattn_decode_step(const void *q, const void *k, const void *v,
                         float *s, float *z, const float *alpha, void *o,
                         int B, int H, int Dk, int Dv, int dtype, int phi,
                         float eps, void *hip_stream);
+
+/*
+ * The decode step with the carried state stored in a narrower type: S and z
+ * are read from state_dtype, the update is computed in fp32, rounded once
+ * (round to nearest even) back to state_dtype, and the read uses the value as
+ * stored.  The product-order page ("What a summary can't do") warns that a
+ * summary rewritten every token in low precision accumulates rounding error;
+ * this is that summary, at half (bf16) or a quarter (fp8) of the fp32 bytes.
+ *
+ *   s, z        [B][H][Dk][Dv] and [B][H][Dk] of state_dtype, IN/OUT.
+ *   state_dtype LINATTN_F32 (same as linattn_decode_step), LINATTN_BF16, or
+ *               LINATTN_FP8_E4M3 (OCP e4m3: 3 mantissa bits, largest finite
+ *               448; a larger magnitude is stored as NaN, so an ungated sum
+ *               overflows after a few hundred tokens).
+ * Other arguments as linattn_decode_step.
+ */
+int linattn_decode_step_lowp(const void *q, const void *k, const void *v,
+                             void *s, void *z, int state_dtype,
+                             const float *alpha, void *o,
+                             int B, int H, int Dk, int Dv, int dtype, int phi,
+                             float eps, void *hip_stream);
 
 /*
  * Workspace bytes a call of the given kind needs for these sizes (0 when the

@@ -16,7 +16,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblinattn.so")
 
-F32, BF16 = 0, 1
+F32, BF16, FP8_E4M3 = 0, 1, 2
 PHI_ELU1, PHI_IDENTITY = 0, 1
 KIND_FORWARD, KIND_GATED, KIND_NONCAUSAL, KIND_BACKWARD = 0, 1, 2, 3
 
@@ -34,6 +34,7 @@ SIGNATURES = {
     "linattn_forward_gated": ([_P] * 9 + [_I] * 7 + [_F, _P, _SZ, _P], _I),
     "linattn_forward_train": ([_P] * 9 + [_I] * 7 + [_F, _P, _SZ, _P], _I),
     "linattn_backward": ([_P] * 10 + [_I] * 7 + [_F, _P, _SZ, _P], _I),
+    "linattn_decode_step_lowp": ([_P] * 5 + [_I] + [_P] * 2 + [_I] * 6 + [_F, _P], _I),
     "linattn_forward_delta": ([_P] * 7 + [_I] * 7 + [_P], _I),
     "linattn_forward_snapshots": ([_P] * 10 + [_I] + [_P] * 2 + [_I] * 7 + [_F, _P, _SZ, _P], _I),
     "linattn_forward_noncausal": ([_P] * 6 + [_I] * 7 + [_F, _P, _SZ, _P], _I),
@@ -341,6 +342,35 @@ def linattn_decode_step(q, k, v, s, z, alpha=None, *, eps=1e-6, phi=PHI_ELU1, ou
     rc = lib().linattn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(s), _ptr(z), _ptr(alpha), _ptr(o), B, H, Dk,
                                    Dv, code, phi, float(eps), _stream(q))
     _check(rc, "linattn_decode_step")
+    return o
+
+
+_STATE_CODES = {torch.float32: F32, torch.bfloat16: BF16, torch.float8_e4m3fn: FP8_E4M3}
+
+
+def linattn_decode_step_lowp(q, k, v, s, z, alpha=None, *, eps=1e-6, phi=PHI_ELU1, out=None):
+    """linattn_decode_step with S, z stored as float32, bfloat16 or float8_e4m3fn (their dtype decides)."""
+    _dev(q, "q")
+    code = _dtype_code(q)
+    _dev(k, "k", q.dtype)
+    _dev(v, "v", q.dtype)
+    B, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if s.dtype not in _STATE_CODES or z.dtype != s.dtype:
+        raise TypeError("s and z must share one of float32, bfloat16, float8_e4m3fn")
+    _dev(s, "s", s.dtype)
+    _dev(z, "z", s.dtype)
+    if tuple(s.shape) != (B, H, Dk, Dv) or tuple(z.shape) != (B, H, Dk) or tuple(k.shape) != (B, H, Dk):
+        raise ValueError("decode shapes do not match")
+    if alpha is not None:
+        _dev(alpha, "alpha", torch.float32)
+        if tuple(alpha.shape) != (B, H):
+            raise ValueError("alpha must be [B, H]")
+    o = out if out is not None else torch.empty((B, H, Dv), dtype=q.dtype, device=q.device)
+    _dev(o, "out", q.dtype)
+    rc = lib().linattn_decode_step_lowp(_ptr(q), _ptr(k), _ptr(v), _ptr(s), _ptr(z), _STATE_CODES[s.dtype],
+                                        _ptr(alpha), _ptr(o), B, H, Dk, Dv, code, phi, float(eps), _stream(q))
+    _check(rc, "linattn_decode_step_lowp")
     return o
 
 

@@ -488,19 +488,19 @@ int forward_impl(bool gated, const void *q, const void *k, const void *v, const 
                                          eps, ws, st);
 }
 
-template <typename T, int DK, int DV>
-void launch_decode(const void *q, const void *k, const void *v, float *s, float *z, const float *alpha, void *o,
-                   int BH, int phi, float eps, hipStream_t st) {
-    decode_step_kernel<T, DK, DV><<<dim3(BH), dim3(256), 0, st>>>((const T *)q, (const T *)k, (const T *)v, s, z,
-                                                                    alpha, (T *)o, phi, eps);
+template <typename T, int DK, int DV, typename SS>
+void launch_decode(const void *q, const void *k, const void *v, SS *s, SS *z, const float *alpha, void *o, int BH,
+                   int phi, float eps, hipStream_t st) {
+    decode_step_kernel<T, DK, DV, SS><<<dim3(BH), dim3(256), 0, st>>>((const T *)q, (const T *)k, (const T *)v, s,
+                                                                        z, alpha, (T *)o, phi, eps);
 }
 
-template <typename T>
-bool decode_dims(int Dk, int Dv, const void *q, const void *k, const void *v, float *s, float *z, const float *alpha,
+template <typename T, typename SS = float>
+bool decode_dims(int Dk, int Dv, const void *q, const void *k, const void *v, SS *s, SS *z, const float *alpha,
                  void *o, int BH, int phi, float eps, hipStream_t st) {
 #define LA_D(X, Y)                                                                                                     \
     if (Dk == X && Dv == Y) {                                                                                          \
-        launch_decode<T, X, Y>(q, k, v, s, z, alpha, o, BH, phi, eps, st);                                             \
+        launch_decode<T, X, Y, SS>(q, k, v, s, z, alpha, o, BH, phi, eps, st);                                         \
         return true;                                                                                                   \
     }
     LA_D(16, 16) LA_D(16, 32) LA_D(16, 64) LA_D(16, 128)
@@ -676,6 +676,38 @@ int linattn_decode_step(const void *q, const void *k, const void *v, float *s, f
             decode_dims<uint16_t>(Dk, Dv, q, k, v, s, z, alpha, o, (int)BH, phi, eps, st);
         else
             decode_dims<float>(Dk, Dv, q, k, v, s, z, alpha, o, (int)BH, phi, eps, st);
+    });
+}
+
+int linattn_decode_step_lowp(const void *q, const void *k, const void *v, void *s, void *z, int state_dtype,
+                             const float *alpha, void *o, int B, int H, int Dk, int Dv, int dtype, int phi, float eps,
+                             void *hip_stream) {
+    LA_TRY(check_common(B, H, 1, Dk, Dv, dtype, phi, eps));
+    if (state_dtype != LINATTN_F32 && state_dtype != LINATTN_BF16 && state_dtype != LINATTN_FP8_E4M3)
+        return LINATTN_EDTYPE;
+    if (!q || !k || !v || !s || !z || !o) return LINATTN_EINVAL;
+    const size_t BH = (size_t)B * H;
+    const size_t es = dtype == LINATTN_BF16 ? 2 : 4;
+    const size_t ss = state_dtype == LINATTN_F32 ? 4 : state_dtype == LINATTN_BF16 ? 2 : 1;
+    if (overlaps(o, BH * Dv * es, s, BH * Dk * Dv * ss) || overlaps(o, BH * Dv * es, z, BH * Dk * ss) ||
+        overlaps(s, BH * Dk * Dv * ss, z, BH * Dk * ss))
+        return LINATTN_EINVAL;
+    hipStream_t st = (hipStream_t)hip_stream;
+    auto go = [&](auto tq, auto ts) {
+        using T = decltype(tq);
+        using SS = decltype(ts);
+        decode_dims<T, SS>(Dk, Dv, q, k, v, (SS *)s, (SS *)z, alpha, o, (int)BH, phi, eps, st);
+    };
+    return launch("decode_step", st, [&] {
+        if (dtype == LINATTN_BF16) {
+            if (state_dtype == LINATTN_F32) go(uint16_t{}, float{});
+            else if (state_dtype == LINATTN_BF16) go(uint16_t{}, uint16_t{});
+            else go(uint16_t{}, uint8_t{});
+        } else {
+            if (state_dtype == LINATTN_F32) go(float{}, float{});
+            else if (state_dtype == LINATTN_BF16) go(float{}, uint16_t{});
+            else go(float{}, uint8_t{});
+        }
     });
 }
 

@@ -111,20 +111,79 @@ template <> __device__ __forceinline__ void store_elem<uint16_t>(uint16_t *p, si
     p[i] = (uint16_t)f32_to_bf16_bits(v);
 }
 
-// One decode step per (b, h), in place, streaming the fp32 state once:
+// Storage of the carried state: fp32, bf16 or fp8 (OCP e4m3, as converted by
+// gfx950: round to nearest even, magnitudes past 448 become NaN).  Four
+// consecutive elements at a time; rnd() is the value as stored.
+template <typename SS> struct StateIO;
+template <> struct StateIO<float> {
+    __device__ static __forceinline__ f32x4 load4(const float *p, size_t u) {
+        return __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p) + u);
+    }
+    __device__ static __forceinline__ void store4(float *p, size_t u, f32x4 x) {
+        __builtin_nontemporal_store(x, reinterpret_cast<f32x4 *>(p) + u);
+    }
+    __device__ static __forceinline__ float rnd(float x) { return x; }
+    __device__ static __forceinline__ float load1(const float *p, size_t i) { return p[i]; }
+    __device__ static __forceinline__ void store1(float *p, size_t i, float x) { p[i] = x; }
+};
+template <> struct StateIO<uint16_t> {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    __device__ static __forceinline__ f32x4 load4(const uint16_t *p, size_t u) {
+        const u32x2 w = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p) + u);
+        return f32x4{bf_lo(w[0]), bf_hi(w[0]), bf_lo(w[1]), bf_hi(w[1])};
+    }
+    __device__ static __forceinline__ void store4(uint16_t *p, size_t u, f32x4 x) {
+        const u32x2 w = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x2 *>(p) + u);
+    }
+    __device__ static __forceinline__ float rnd(float x) { return bf16_round(x); }
+    __device__ static __forceinline__ float load1(const uint16_t *p, size_t i) { return bf16_bits_to_f32(p[i]); }
+    __device__ static __forceinline__ void store1(uint16_t *p, size_t i, float x) {
+        p[i] = (uint16_t)f32_to_bf16_bits(x);
+    }
+};
+template <> struct StateIO<uint8_t> {
+    __device__ static __forceinline__ f32x4 load4(const uint8_t *p, size_t u) {
+        const int w = (int)__builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p) + u);
+        return f32x4{__builtin_amdgcn_cvt_f32_fp8(w, 0), __builtin_amdgcn_cvt_f32_fp8(w, 1),
+                     __builtin_amdgcn_cvt_f32_fp8(w, 2), __builtin_amdgcn_cvt_f32_fp8(w, 3)};
+    }
+    __device__ static __forceinline__ void store4(uint8_t *p, size_t u, f32x4 x) {
+        int w = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], w, true);
+        __builtin_nontemporal_store((uint32_t)w, reinterpret_cast<uint32_t *>(p) + u);
+    }
+    __device__ static __forceinline__ float rnd(float x) {
+        return __builtin_amdgcn_cvt_f32_fp8(__builtin_amdgcn_cvt_pk_fp8_f32(x, 0.f, 0, false), 0);
+    }
+    __device__ static __forceinline__ float load1(const uint8_t *p, size_t i) {
+        return __builtin_amdgcn_cvt_f32_fp8((int)p[i], 0);
+    }
+    __device__ static __forceinline__ void store1(uint8_t *p, size_t i, float x) {
+        p[i] = (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(x, 0.f, 0, false) & 0xff);
+    }
+};
+
+// One decode step per (b, h), in place, streaming the state once:
 //   S <- a S + phi(k) v^T,  z <- a z + phi(k),  o = phi(q)^T S / (phi(q)^T z + eps)
 // (the read uses the updated state: "Linear Attention: accumulating KV into a
 // fixed-size state", section "State update and read as equations"; the
 // one-token-at-a-time RNN mode of the "Transformers are RNNs" review).
-// One workgroup of 256 threads per (b, h).  Thread -> (row group, float4
-// column): the DV/4 float4 columns of a row are covered by consecutive
-// threads, so every pass of the workgroup reads and writes whole rows
-// (coalesced), and all passes are issued before any is consumed.
-template <typename T, int DK, int DV>
+// SS is the storage type of S and z (fp32 normally; bf16 or fp8 to study the
+// drift of a low-precision summary rewritten every token, which the
+// product-order page warns about in "What a summary can't do"): the update is
+// computed in fp32 from the stored values, rounded once to SS, and the read
+// uses the value as stored.
+// One workgroup of 256 threads per (b, h).  Thread -> (row group, 4-element
+// column unit): the DV/4 units of a row are covered by consecutive threads,
+// so every pass of the workgroup reads and writes whole rows (coalesced), and
+// all passes are issued before any is consumed.
+template <typename T, int DK, int DV, typename SS = float>
 __global__ __launch_bounds__(256) void decode_step_kernel(const T *__restrict__ q, const T *__restrict__ k,
-                                                          const T *__restrict__ v, float *__restrict__ s,
-                                                          float *__restrict__ z, const float *__restrict__ alpha,
+                                                          const T *__restrict__ v, SS *__restrict__ s,
+                                                          SS *__restrict__ z, const float *__restrict__ alpha,
                                                           T *__restrict__ o, int phi_mode, float eps) {
+    using IO = StateIO<SS>;
     constexpr int C4 = DV / 4;                 // float4 columns per row
     constexpr int RPP = 256 / C4;              // rows one pass of the workgroup covers
     constexpr int ROWS = DK < RPP ? DK : RPP;  // rows per pass actually used
@@ -137,13 +196,13 @@ __global__ __launch_bounds__(256) void decode_step_kernel(const T *__restrict__ 
     const int bh = blockIdx.x;
     const int tid = threadIdx.x;
     const float a = alpha ? alpha[bh] : 1.f;
-    f32x4 *sb = reinterpret_cast<f32x4 *>(s + (size_t)bh * DK * DV);
+    SS *sb = s + (size_t)bh * DK * DV;
     const int c4 = tid % C4, r0 = tid / C4;
     const bool act = tid < ACTIVE;
     f32x4 st[PASSES];
     if (act) {
 #pragma unroll
-        for (int p = 0; p < PASSES; ++p) st[p] = __builtin_nontemporal_load(sb + (size_t)(r0 + p * ROWS) * C4 + c4);
+        for (int p = 0; p < PASSES; ++p) st[p] = IO::load4(sb, (size_t)(r0 + p * ROWS) * C4 + c4);
     }
     if (tid < DK) {
         sq[tid] = phi_exact(load_elem<T>(q, (size_t)bh * DK + tid), phi_mode);
@@ -155,8 +214,8 @@ __global__ __launch_bounds__(256) void decode_step_kernel(const T *__restrict__ 
     // z <- a z + phi(k) and the denominator phi(q).z (threads 0..DK-1)
     float dpart = 0.f;
     if (tid < DK) {
-        const float zn = fmaf(a, z[(size_t)bh * DK + tid], sk[tid]);
-        z[(size_t)bh * DK + tid] = zn;
+        const float zn = IO::rnd(fmaf(a, IO::load1(z, (size_t)bh * DK + tid), sk[tid]));
+        IO::store1(z, (size_t)bh * DK + tid, zn);
         dpart = sq[tid] * zn;
     }
 #pragma unroll
@@ -173,10 +232,10 @@ __global__ __launch_bounds__(256) void decode_step_kernel(const T *__restrict__ 
             f32x4 x = st[p];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                x[e] = fmaf(a, x[e], fk * vv[e]);
+                x[e] = IO::rnd(fmaf(a, x[e], fk * vv[e]));
                 num[e] = fmaf(fq, x[e], num[e]);
             }
-            __builtin_nontemporal_store(x, sb + (size_t)row * C4 + c4);
+            IO::store4(sb, (size_t)row * C4 + c4, x);
         }
         *reinterpret_cast<f32x4 *>(&red[r0][4 * c4]) = num;
     }

@@ -73,6 +73,10 @@ def _load():
             lib.oracle_backward.restype = i32
             lib.oracle_delta.argtypes = [P] * 7 + [i64, i64, i32, i32, i32, i32]
             lib.oracle_delta.restype = i32
+            lib.oracle_decode_lowp.argtypes = [P] * 7 + [i64, i32, i32, i32, f64, i32]
+            lib.oracle_decode_lowp.restype = i32
+            lib.oracle_state_round.argtypes = [f64, i32]
+            lib.oracle_state_round.restype = f64
             lib.oracle_phi.argtypes = [P, P, i64, i32]
             lib.oracle_phi.restype = None
             _lib = lib
@@ -213,6 +217,35 @@ def decode_step(q, k, v, s, z, *, alpha=None, eps=1e-6, phi_mode=PHI_ELU1, nthre
                                     nthreads or _threads(B * H))
     if rc != 0:
         raise RuntimeError("oracle_decode_step failed")
+    return o, s, z
+
+
+STATE_F32, STATE_BF16, STATE_FP8_E4M3 = 0, 1, 2
+
+
+def state_round(x, state_dtype):
+    """Elementwise rounding to a state storage type (bf16, OCP fp8 e4m3 with NaN past 448, or fp32)."""
+    x = np.asarray(x, dtype=np.float64)
+    f = _load().oracle_state_round
+    return np.vectorize(lambda t: f(float(t), state_dtype), otypes=[np.float64])(x)
+
+
+def decode_lowp(q, k, v, s, z, state_dtype, *, alpha=None, eps=1e-6, phi_mode=PHI_ELU1):
+    """One decode step with the state stored in a narrower type ("Linear Attention: what happens when
+    you change the product order", section "What a summary can't do": a summary rewritten every token
+    in low precision).  s, z hold stored values (float64 arrays); returns (o, s_new, z_new).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    s = _f64(s).copy()
+    z = _f64(z).copy()
+    B, H, Dk = q.shape
+    Dv = v.shape[-1]
+    a = _f64(alpha)
+    o = np.empty((B, H, Dv))
+    rc = _load().oracle_decode_lowp(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(s), _ptr(z), _ptr(o), B * H, Dk, Dv,
+                                    phi_mode, float(eps), state_dtype)
+    if rc != 0:
+        raise RuntimeError("oracle_decode_lowp failed")
     return o, s, z
 
 

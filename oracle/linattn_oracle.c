@@ -227,6 +227,78 @@ int oracle_decode_step(const double *q, const double *k, const double *v,
     return err ? -1 : 0;
 }
 
+/* Round x to the nearest number with p significant bits, ties to even; below
+ * 2^emin the grid is fixed at 2^(emin - p + 1) (subnormals).  bf16 is p = 8,
+ * emin = -126; OCP fp8 e4m3 is p = 4, emin = -6, with 448 the largest finite
+ * magnitude (a larger one is stored as NaN, as the gfx950 conversion does). */
+static double round_sig(double x, int p, int emin)
+{
+    if (x == 0.0 || !isfinite(x))
+        return x;
+    int e;
+    frexp(x, &e); /* |x| in [2^(e-1), 2^e) */
+    int ex = e - 1;
+    if (ex < emin)
+        ex = emin;
+    const double q = ldexp(1.0, ex - (p - 1));
+    return nearbyint(x / q) * q; /* default rounding mode: nearest, ties to even */
+}
+
+#define STATE_F32 0
+#define STATE_BF16 1
+#define STATE_FP8_E4M3 2
+
+double oracle_state_round(double x, int sdt)
+{
+    if (sdt == STATE_BF16)
+        return round_sig(x, 8, -126);
+    if (sdt == STATE_FP8_E4M3) {
+        const double r = round_sig(x, 4, -6);
+        return fabs(r) > 448.0 ? NAN : r;
+    }
+    return (double)(float)x;
+}
+
+/* A decode step with the state stored in a narrower type (state dtype sdt):
+ * S <- round(a S + phi(k) v^T), z <- round(a z + phi(k)) elementwise, then
+ * o = phi(q)^T S / (phi(q)^T z + eps) from the stored values.  The rounding
+ * decides a stored code, so it is taken on the same fp32 value the library
+ * rounds: phi(k) in fp32, the product phi(k) v in fp32, then one fused
+ * multiply-add a * S + phi(k) v in fp32; the read is in fp64. */
+int oracle_decode_lowp(const double *q, const double *k, const double *v,
+                       const double *alpha, double *s, double *z, double *o,
+                       int64_t BH, int Dk, int Dv, int mode, double eps,
+                       int sdt)
+{
+    if (!q || !k || !v || !s || !z || BH < 0 || Dk < 1 || Dv < 1)
+        return -1;
+    for (int64_t bh = 0; bh < BH; ++bh) {
+        const double *qt = q + bh * Dk, *kt = k + bh * Dk, *vt = v + bh * Dv;
+        double *sb = s + bh * Dk * Dv, *zb = z + bh * Dk;
+        const float a = alpha ? (float)alpha[bh] : 1.0f;
+        double den = 0.0;
+        for (int i = 0; i < Dk; ++i) {
+            const float fk = (float)phi(kt[i], mode);
+            zb[i] = oracle_state_round((double)fmaf(a, (float)zb[i], fk), sdt);
+            for (int j = 0; j < Dv; ++j) {
+                const float pr = fk * (float)vt[j];
+                sb[(int64_t)i * Dv + j] =
+                    oracle_state_round((double)fmaf(a, (float)sb[(int64_t)i * Dv + j], pr), sdt);
+            }
+            den += phi(qt[i], mode) * zb[i];
+        }
+        if (o) {
+            for (int j = 0; j < Dv; ++j) {
+                double num = 0.0;
+                for (int i = 0; i < Dk; ++i)
+                    num += phi(qt[i], mode) * sb[(int64_t)i * Dv + j];
+                o[bh * Dv + j] = num / (den + eps);
+            }
+        }
+    }
+    return 0;
+}
+
 /* The feature map alone, elementwise, for the closed-form pins. */
 /* Derivative of phi: 1 on x >= 0 and exp(x) on x < 0 for elu + 1 (elu's
  * derivative, the +1 offset drops out); 1 everywhere for the identity map. */

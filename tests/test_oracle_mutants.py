@@ -44,13 +44,18 @@ DELTA_MUTANTS = {
     "delta_beta_ignored": ("const double b = beta ? beta[t] : 1.0;", "const double b = 1.0;"),
     "delta_read_with_query": ("acc += s[(int64_t)i * Dv + j] * kh[i];", "acc += s[(int64_t)i * Dv + j] * phi(q[t * Dk + i], mode);"),
 }
+LOWP_MUTANTS = {
+    "lowp_truncates": ("return nearbyint(x / q) * q;", "return trunc(x / q) * q;"),
+    "lowp_fp8_saturates": ("return fabs(r) > 448.0 ? NAN : r;", "return fabs(r) > 448.0 ? copysign(448.0, r) : r;"),
+    "lowp_denominator_shifted": ("den += phi(qt[i], mode) * zb[i];", "den += phi(qt[i], mode) * (zb[i] + 0.5);"),
+}
 PINS = {**{n: "test_oracle.py" for n in MUTANTS}, **{n: "test_oracle_backward.py" for n in BACKWARD_MUTANTS},
-        **{n: "test_oracle_delta.py" for n in DELTA_MUTANTS}}
+        **{n: "test_oracle_delta.py" for n in DELTA_MUTANTS}, **{n: "test_oracle_lowp.py" for n in LOWP_MUTANTS}}
 
 
 @pytest.mark.parametrize("name", sorted(PINS))
 def test_mutant_is_caught(name, tmp_path):
-    old, new = {**MUTANTS, **BACKWARD_MUTANTS, **DELTA_MUTANTS}[name]
+    old, new = {**MUTANTS, **BACKWARD_MUTANTS, **DELTA_MUTANTS, **LOWP_MUTANTS}[name]
     pins = PINS[name]
     src = open(SRC).read()
     assert src.count(old) >= 1, f"mutation site for {name} not found"
