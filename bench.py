@@ -222,7 +222,7 @@ def noncausal_case(name, dev, inputs=None):
     return w, fn, nbytes
 
 
-def decode_case(dev):
+def decode_state(dev):
     """Decode workload: the state after a 2048-token seeded prefix, built by the library's own forward."""
     w = synth.WORKLOADS["decode_b256h32_d128"]
     s = torch.empty((w.B, w.H, w.Dk, w.Dv), dtype=torch.float32, device=dev)
@@ -232,6 +232,11 @@ def decode_case(dev):
         # the prefix's queries do not enter the state; keys stand in for them
         la.linattn_forward(kp, kp, vp, s_final=s[b:b + 1], z_final=z[b:b + 1])
     q, k, v = (x.to(dev) for x in synth.decode_token(w))
+    return w, s, z, q, k, v
+
+
+def decode_case(dev):
+    w, s, z, q, k, v = decode_state(dev)
     o = torch.empty((w.B, w.H, w.Dv), dtype=w.dtype, device=dev)
     s0, z0 = s.clone(), z.clone()
 
@@ -242,6 +247,23 @@ def decode_case(dev):
         s.copy_(s0)
         z.copy_(z0)
     nbytes = rf.decode_bytes(w.B, w.H, w.Dk, w.Dv, 2)
+    return w, fn, nbytes, reset
+
+
+def decode_lowp_case(dev, state_dtype):
+    """The decode workload with the state stored in a narrower type (the prefix state rounded once)."""
+    w, s32, z32, q, k, v = decode_state(dev)
+    s0, z0 = s32.to(state_dtype), z32.to(state_dtype)
+    s, z = s0.clone(), z0.clone()
+    o = torch.empty((w.B, w.H, w.Dv), dtype=w.dtype, device=dev)
+
+    def fn():
+        la.linattn_decode_step_lowp(q, k, v, s, z, out=o)
+
+    def reset():
+        s.copy_(s0)
+        z.copy_(z0)
+    nbytes = rf.decode_bytes(w.B, w.H, w.Dk, w.Dv, 2, state_bytes=s0.element_size())
     return w, fn, nbytes, reset
 
 
@@ -303,7 +325,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-paths", action="store_true")
-    ap.add_argument("--path", choices=["forward", "gated", "decode", "noncausal", "backward", "snapshots", "delta"],
+    ap.add_argument("--path", choices=["forward", "gated", "decode", "decode_bf16_state", "noncausal", "backward",
+                                       "snapshots", "delta"],
                     default=None)
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
@@ -318,7 +341,7 @@ def main():
         copy_calibration(dev, args.steps)
         return
 
-    if args.path in ("decode", "gated", "noncausal", "backward", "snapshots", "delta"):
+    if args.path in ("decode", "decode_bf16_state", "gated", "noncausal", "backward", "snapshots", "delta"):
         # single-path run (used for counter collection); prints its own line
         run_single_path(args, dev, stream)
         return
@@ -353,7 +376,7 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def path_entry(w, fn, nbytes, stream, args, tokens, reset=None, flops=None, key=None):
+def path_entry(w, fn, nbytes, stream, args, tokens, reset=None, flops=None, key=None, kernel_nbytes=None):
     ms = timed(fn, args.steps, args.warmup, stream)
     if reset:
         reset()
@@ -364,7 +387,7 @@ def path_entry(w, fn, nbytes, stream, args, tokens, reset=None, flops=None, key=
     key = key or w.name
     return {"workload": key, "ms_per_step": round(ms, 4), "Mtokens_per_s": round(tokens / (ms * 1e-3) / 1e6, 3),
             "path_roofline_frac": round(rf.hbm_time_s(nbytes) / (ms * 1e-3), 4),
-            "roofline": roofline_entry(dom, kt[dom]["avg_ms"], kernel_bytes(dom, w), key,
+            "roofline": roofline_entry(dom, kt[dom]["avg_ms"], kernel_nbytes or kernel_bytes(dom, w), key,
                                        kernel_flops(dom, w, flops)),
             "kernels_ms": {n: round(e["avg_ms"], 4) for n, e in kt.items()}}
 
@@ -380,6 +403,12 @@ def other_paths(args, dev, stream, headline_inputs):
     w, fn, nbytes, reset = decode_case(dev)
     out["decode"] = path_entry(w, fn, nbytes, stream, args, w.B, reset=reset)
     out["decode"]["steps_per_s"] = round(1e3 / out["decode"]["ms_per_step"], 1)
+    del fn
+    log("[bench] decode step, bf16 state")
+    w, fn, nbytes, reset = decode_lowp_case(dev, torch.bfloat16)
+    out["decode_bf16_state"] = path_entry(w, fn, nbytes, stream, args, w.B, reset=reset, key="decode_bf16_state",
+                                          kernel_nbytes=nbytes)
+    out["decode_bf16_state"]["steps_per_s"] = round(1e3 / out["decode_bf16_state"]["ms_per_step"], 1)
     del fn
     log("[bench] non-causal form")
     w, fn, nbytes = noncausal_case(HEADLINE, dev, headline_inputs)
@@ -409,6 +438,9 @@ def run_single_path(args, dev, stream):
     elif args.path == "decode":
         w, fn, nbytes, reset = decode_case(dev)
         r = path_entry(w, fn, nbytes, stream, args, w.B, reset=reset)
+    elif args.path == "decode_bf16_state":
+        w, fn, nbytes, reset = decode_lowp_case(dev, torch.bfloat16)
+        r = path_entry(w, fn, nbytes, stream, args, w.B, reset=reset, key="decode_bf16_state", kernel_nbytes=nbytes)
     elif args.path == "delta":
         w, fn, nbytes = delta_case("delta_b16h16_n4096_d128", dev)
         r = path_entry(w, fn, nbytes, stream, args, w.B * w.N, flops=rf.delta_flops(w.B, w.H, w.N, w.Dk, w.Dv))

@@ -28,10 +28,10 @@ def forward_bytes(B, H, N, Dk, Dv, in_bytes, out_bytes=None, *, gated=False,
     return B * H * (N * per_token + state * (int(state_in) + int(state_out)))
 
 
-def decode_bytes(B, H, Dk, Dv, in_bytes, out_bytes=None, *, gated=False) -> int:
-    """The fp32 (S, z) read and written once, q/k/v read once, o written once."""
+def decode_bytes(B, H, Dk, Dv, in_bytes, out_bytes=None, *, gated=False, state_bytes=4) -> int:
+    """(S, z) read and written once (fp32 unless state_bytes says otherwise), q/k/v read once, o written once."""
     out_bytes = in_bytes if out_bytes is None else out_bytes
-    state = (Dk * Dv + Dk) * 4
+    state = (Dk * Dv + Dk) * state_bytes
     return B * H * (2 * state + (2 * Dk + Dv) * in_bytes + Dv * out_bytes + (4 if gated else 0))
 
 
