@@ -178,9 +178,13 @@ int linattn_backward(const void *q, const void *k, const void *v,
  * summary with the key and write only the difference to the value, so that
  * re-reading with the same key returns the new value).  Per token:
  *   kh_t = phi(k_t) / |phi(k_t)|_2   (unit key; a zero key writes nothing)
- *   S_t  = S_{t-1} + beta_t kh_t (v_t - S_{t-1}^T kh_t)^T
+ *   S'   = a_t S_{t-1}               (the gated form the same section names,
+ *                                     Gated DeltaNet; a_t = 1 when ungated)
+ *   S_t  = S' + beta_t kh_t (v_t - S'^T kh_t)^T
  *   o_t  = S_t^T phi(q_t)            (no normalizer)
  *
+ *   alpha     NULL (ungated) or [B][H][N] fp32 gates in [0, 1] (a gate of 0
+ *             clears the summary exactly).
  *   beta      NULL (every beta_t = 1, the page's full overwrite) or
  *             [B][H][N] fp32 write strengths.
  *   s_init    NULL (zero) or [B][H][Dk][Dv] fp32; s_final NULL or output
@@ -191,7 +195,7 @@ int linattn_backward(const void *q, const void *k, const void *v,
  * in order.
  */
 int linattn_forward_delta(const void *q, const void *k, const void *v,
-                          const float *beta, void *o,
+                          const float *alpha, const float *beta, void *o,
                           const float *s_init, float *s_final,
                           int B, int H, int N, int Dk, int Dv, int dtype,
                           int phi, void *hip_stream);

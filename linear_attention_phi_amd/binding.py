@@ -35,7 +35,7 @@ SIGNATURES = {
     "linattn_forward_train": ([_P] * 9 + [_I] * 7 + [_F, _P, _SZ, _P], _I),
     "linattn_backward": ([_P] * 10 + [_I] * 7 + [_F, _P, _SZ, _P], _I),
     "linattn_decode_step_lowp": ([_P] * 5 + [_I] + [_P] * 2 + [_I] * 6 + [_F, _P], _I),
-    "linattn_forward_delta": ([_P] * 7 + [_I] * 7 + [_P], _I),
+    "linattn_forward_delta": ([_P] * 8 + [_I] * 7 + [_P], _I),
     "linattn_forward_snapshots": ([_P] * 10 + [_I] + [_P] * 2 + [_I] * 7 + [_F, _P, _SZ, _P], _I),
     "linattn_forward_noncausal": ([_P] * 6 + [_I] * 7 + [_F, _P, _SZ, _P], _I),
     "linattn_decode_step": ([_P] * 7 + [_I] * 6 + [_F, _P], _I),
@@ -229,10 +229,11 @@ def linattn_backward(q, k, v, den, dout, s_init=None, z_init=None, *, eps=1e-6, 
     return dq, dk, dv
 
 
-def linattn_forward_delta(q, k, v, beta=None, s_init=None, *, phi=PHI_ELU1, want_state=True, out=None):
-    """Delta rule: read with the unit key phi(k)/|phi(k)|, write beta times the difference,
-    o = S^T phi(q).  beta [B, H, N] fp32 or None (ones) -> (o, s_final or None).
-    bf16 with Dk, Dv in {64, 128}.
+def linattn_forward_delta(q, k, v, beta=None, s_init=None, *, alpha=None, phi=PHI_ELU1, want_state=True,
+                          out=None):
+    """Delta rule: decay the summary by alpha (gated form), read it with the unit key
+    phi(k)/|phi(k)|, write beta times the difference, o = S^T phi(q).  alpha, beta [B, H, N]
+    fp32 or None (ones) -> (o, s_final or None).  bf16 with Dk, Dv in {64, 128}.
     """
     _dev(q, "q")
     code = _dtype_code(q)
@@ -242,14 +243,15 @@ def linattn_forward_delta(q, k, v, beta=None, s_init=None, *, phi=PHI_ELU1, want
     Dv = v.shape[-1]
     if tuple(k.shape) != (B, H, N, Dk) or tuple(v.shape[:3]) != (B, H, N):
         raise ValueError("q, k, v shapes do not match")
-    _dev(beta, "beta", torch.float32)
-    if beta is not None and tuple(beta.shape) != (B, H, N):
-        raise ValueError("beta must be [B, H, N]")
+    for name, t in (("beta", beta), ("alpha", alpha)):
+        _dev(t, name, torch.float32)
+        if t is not None and tuple(t.shape) != (B, H, N):
+            raise ValueError(f"{name} must be [B, H, N]")
     _dev(s_init, "s_init", torch.float32)
     o = out if out is not None else torch.empty((B, H, N, Dv), dtype=q.dtype, device=q.device)
     s_final = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device) if want_state else None
-    rc = lib().linattn_forward_delta(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(o), _ptr(s_init), _ptr(s_final),
-                                     B, H, N, Dk, Dv, code, phi, _stream(q))
+    rc = lib().linattn_forward_delta(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(o), _ptr(s_init),
+                                     _ptr(s_final), B, H, N, Dk, Dv, code, phi, _stream(q))
     _check(rc, "linattn_forward_delta")
     return o, s_final
 

@@ -552,18 +552,18 @@ int linattn_forward_train(const void *q, const void *k, const void *v, void *o, 
                         eps, workspace, workspace_bytes, hip_stream, den);
 }
 
-int linattn_forward_delta(const void *q, const void *k, const void *v, const float *beta, void *o,
-                          const float *s_init, float *s_final, int B, int H, int N, int Dk, int Dv, int dtype,
-                          int phi, void *hip_stream) {
+int linattn_forward_delta(const void *q, const void *k, const void *v, const float *alpha, const float *beta,
+                          void *o, const float *s_init, float *s_final, int B, int H, int N, int Dk, int Dv,
+                          int dtype, int phi, void *hip_stream) {
     LA_TRY(check_common(B, H, N, Dk, Dv, dtype, phi, 0.f));
     LA_TRY(check_train(Dk, Dv, dtype));
     if (!q || !k || !v || !o) return LINATTN_EINVAL;
     const size_t BH = (size_t)B * H;
     const size_t nq = BH * N * Dk * 2, nv = BH * N * Dv * 2, ns = BH * Dk * Dv * 4;
-    const void *ins[5] = {q, k, v, beta, s_init};
-    const size_t insz[5] = {nq, nq, nv, BH * N * 4, ns};
-    for (int b = 0; b < 5; ++b)
-        if (overlaps(o, nv, ins[b], insz[b]) || (b < 4 && overlaps(s_final, ns, ins[b], insz[b])))
+    const void *ins[6] = {q, k, v, beta, alpha, s_init};
+    const size_t insz[6] = {nq, nq, nv, BH * N * 4, BH * N * 4, ns};
+    for (int b = 0; b < 6; ++b)
+        if (overlaps(o, nv, ins[b], insz[b]) || (b < 5 && overlaps(s_final, ns, ins[b], insz[b])))
             return LINATTN_EINVAL;
     if (overlaps(o, nv, s_final, ns)) return LINATTN_EINVAL;
     hipStream_t st = (hipStream_t)hip_stream;
@@ -571,14 +571,20 @@ int linattn_forward_delta(const void *q, const void *k, const void *v, const flo
         constexpr int DK = decltype(DKc)::value, DV = decltype(DVc)::value;
         return launch("delta_bf16", st, [&] {
             with_phi(phi, [&](auto PH) {
-                if (beta)
-                    delta8_bf16<DK, DV, PH(), true><<<dim3((unsigned)BH), dim3(kThreads8), 0, st>>>(
-                        (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, beta, (uint16_t *)o, s_init,
-                        s_final, N);
-                else
-                    delta8_bf16<DK, DV, PH(), false><<<dim3((unsigned)BH), dim3(kThreads8), 0, st>>>(
-                        (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, nullptr, (uint16_t *)o, s_init,
-                        s_final, N);
+                auto go = [&](auto BT, auto GT) {
+                    delta8_bf16<DK, DV, PH(), BT(), GT()><<<dim3((unsigned)BH), dim3(kThreads8), 0, st>>>(
+                        (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, alpha, beta, (uint16_t *)o,
+                        s_init, s_final, N);
+                };
+                using T = std::true_type;
+                using F = std::false_type;
+                if (alpha) {
+                    if (beta) go(T{}, T{});
+                    else go(F{}, T{});
+                } else {
+                    if (beta) go(T{}, F{});
+                    else go(F{}, F{});
+                }
             });
         });
     };

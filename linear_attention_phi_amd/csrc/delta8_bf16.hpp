@@ -63,11 +63,18 @@ __device__ __forceinline__ f32x4 mfma16_split(float4 a, f32x4 b, f32x4 c) {
     return mfma16x16x16(ahi, blo, c);
 }
 
-template <int DK, int DV, int PHI, bool BETA>
+// GATED: the summary is first decayed by a_t (the gated form, Gated DeltaNet).
+// With g_t the product of the chunk's gates through t and D(j -> t) the
+// product of those after j through t, the chunk's system, outputs and state
+// become
+//   (I + diag(beta) (tril(Kh Kh^T, -1) o Dec)) D = diag(beta) (V - diag(g) Kh S_0)
+//   O = diag(g) Q S_0 + (tril(Q Kh^T) o Dec) D,   S_C = g_C S_0 + Kh^T diag(D(j -> C)) D,
+// Dec[t][j] = D(j -> t); exact zeros across a zero gate, as in the gated forward.
+template <int DK, int DV, int PHI, bool BETA, bool GATED>
 __global__ __launch_bounds__(kThreads8, 1) void delta8_bf16(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
-    const float *__restrict__ beta, uint16_t *__restrict__ o, const float *__restrict__ s_init,
-    float *__restrict__ s_final, int N) {
+    const float *__restrict__ alpha, const float *__restrict__ beta, uint16_t *__restrict__ o,
+    const float *__restrict__ s_init, float *__restrict__ s_final, int N) {
     using TK = Tile<DK>;
     using TV = Tile<DV>;
     constexpr int KSK = DK / 32;
@@ -82,6 +89,9 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8_bf16(
     __shared__ __attribute__((aligned(16))) float sA[kChunk * AS];        // diag(beta) tril(Kh Kh^T, -1)
     __shared__ __attribute__((aligned(16))) float sB[kChunk];             // beta (0 past the end)
     __shared__ __attribute__((aligned(16))) float sT[4 * 16 * 16];        // inverses of A's diagonal blocks
+    // gated: the chunk's inclusive gate prefix per token (log2 sum, zero count)
+    __shared__ __attribute__((aligned(16))) float sGl[GATED ? kChunk : 4];
+    __shared__ __attribute__((aligned(16))) int sGz[GATED ? kChunk : 4];
 
     const size_t bh = blockIdx.x;
     const int tid = threadIdx.x, w = wave_id();
@@ -140,10 +150,20 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8_bf16(
             if (tid < kChunk) {
                 const size_t r = row0 + (size_t)c * kChunk + tid;
                 sB[tid] = tid < valid ? (BETA ? beta[r] : 1.f) : 0.f;
+                if (GATED) {
+                    ChunkGates cg;
+                    cg.build(tid < valid ? alpha[r] : 1.f, tid < valid);
+                    sGl[tid] = cg.lsum;
+                    sGz[tid] = cg.zeros;
+                }
             }
         }
         if (c + 1 < nch) issue(buf, c + 1);
         __syncthreads();
+
+        // decay from after token j through token t (j < t), and through t from the chunk's start
+        auto dec = [&](int t, int j) { return decay_between(sGl[t], sGz[t], sGl[j], sGz[j]); };
+        auto gam = [&](int t) { return decay_between(sGl[t], sGz[t], 0.f, 0); };
 
         // ---- right-hand side diag(beta)(V - Kh S_0) and the coupling diag(beta) tril(Kh Kh^T, -1)
         {
@@ -168,6 +188,7 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8_bf16(
                 const int vc = 32 * (nt >> 1) + 8 * g + 4 * (nt & 1);
                 const uint2 vv = *reinterpret_cast<const uint2 *>(sV + TV::off(tk, vc));
                 const float b = sB[tk];
+                if (GATED) r *= gam(tk);
                 *reinterpret_cast<float4 *>(sX + tk * XS + vc) =
                     make_float4(b * (bf_lo(vv.x) - r[0]), b * (bf_hi(vv.x) - r[1]), b * (bf_lo(vv.y) - r[2]),
                                 b * (bf_hi(vv.y) - r[3]));
@@ -186,6 +207,13 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8_bf16(
                     // gr[i] = Kh[16 cb + 4 g + i] . Kh[tk]: the coupling A[tk][j] for
                     // j = 16 cb + 4 g + i, strictly below the diagonal
                     const float b = sB[tk];
+                    if (GATED) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int j = 16 * cb + 4 * g + i;
+                            gr[i] *= j < tk ? dec(tk, j) : 0.f;
+                        }
+                    }
                     float4 a4;
                     a4.x = 16 * cb + 4 * g + 0 < tk ? b * gr[0] : 0.f;
                     a4.y = 16 * cb + 4 * g + 1 < tk ? b * gr[1] : 0.f;
@@ -239,13 +267,16 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8_bf16(
                 const float4 t4 = *reinterpret_cast<const float4 *>(sT + (16 * b + l16) * 16 + 4 * g);
                 dblk[b] = mfma16_split(t4, y, f32x4{0.f, 0.f, 0.f, 0.f});
             }
+            // D as solved for the outputs; for the state update each row is
+            // decayed to the chunk's end
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int row = 16 * b + 4 * g + i;
                     sX[row * XS + col] = dblk[b][i];
-                    sV[TV::off(row, col)] = (uint16_t)f32_to_bf16_bits(dblk[b][i]);
+                    const float dk = GATED ? dec(valid - 1, row) : 1.f;
+                    sV[TV::off(row, col)] = (uint16_t)f32_to_bf16_bits(dblk[b][i] * dk);
                 }
             }
         }
@@ -273,6 +304,7 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8_bf16(
                         const int klo = 32 * ks + 8 * g;
                         acc[j] = mfma16x16x32(tr_operand_in<TileS<DV>>(sS, klo, klo + 4, colq, lane), qa[ks], acc[j]);
                     }
+                    if (GATED) acc[j] *= gam(tq);
                 }
                 // scores^T [key][query] = Kh_key . phi(q)_query, keys at or before the query
                 f32x4 sc[4];
@@ -286,8 +318,10 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8_bf16(
                                 *reinterpret_cast<const bf16x8 *>(sK + TK::off(16 * kb + l16, 32 * ks + 8 * g)),
                                 qa[ks], sc[kb]);
 #pragma unroll
-                        for (int i = 0; i < 4; ++i)
+                        for (int i = 0; i < 4; ++i) {
                             if (kb == qblk && 4 * g + i > l16) sc[kb][i] = 0.f;
+                            else if (GATED) sc[kb][i] *= dec(tq, 16 * kb + 4 * g + i);
+                        }
                     }
                 }
                 // D^T tril(.)^T with both factors split into bf16 high and low
@@ -334,7 +368,9 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8_bf16(
             case 2: chunk_out(std::integral_constant<int, 2>{}); break;
             default: chunk_out(std::integral_constant<int, 3>{}); break;
             }
-            // S += Kh^T D (rows past the end have zero keys; z is not used)
+            // S <- g_C S + Kh^T D (rows decayed to the chunk's end; rows past the
+            // end have zero keys; z is not used)
+            if (GATED) state8_scale<DK, DV>(st, gam(valid - 1));
             state8_update<DK, DV>(st, sK, sV, w, lane, ones, 0.f);
         }
         __syncthreads();

@@ -71,7 +71,7 @@ def _load():
             lib.oracle_decode_step.restype = i32
             lib.oracle_backward.argtypes = [P] * 12 + [i64, i64, i32, i32, i32, f64, i32]
             lib.oracle_backward.restype = i32
-            lib.oracle_delta.argtypes = [P] * 7 + [i64, i64, i32, i32, i32, i32]
+            lib.oracle_delta.argtypes = [P] * 8 + [i64, i64, i32, i32, i32, i32]
             lib.oracle_delta.restype = i32
             lib.oracle_decode_lowp.argtypes = [P] * 7 + [i64, i32, i32, i32, f64, i32]
             lib.oracle_decode_lowp.restype = i32
@@ -155,11 +155,12 @@ def snapshots(q, k, v, positions, s_init=None, z_init=None, *, alpha=None, phi_m
     return s, z
 
 
-def delta(q, k, v, beta=None, s_init=None, *, phi_mode=PHI_ELU1, want_o=True, nthreads=None):
+def delta(q, k, v, beta=None, s_init=None, *, alpha=None, phi_mode=PHI_ELU1, want_o=True, nthreads=None):
     """Delta-rule forward ("Linear Attention: what happens when you change the product order",
-    section "The summary runs out of room"): per token, read the summary with the unit key
-    phi(k)/|phi(k)|, write beta times the difference to the value, read with phi(q).
-    beta [B, H, N] or None (ones).  Returns (O, S_final) in fp64.
+    section "The summary runs out of room"): per token, decay the summary by alpha (the gated
+    form, Gated DeltaNet), read it with the unit key phi(k)/|phi(k)|, write beta times the
+    difference to the value, read with phi(q).  alpha, beta [B, H, N] or None (ones).
+    Returns (O, S_final) in fp64.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, H, N, Dk = q.shape
@@ -168,13 +169,16 @@ def delta(q, k, v, beta=None, s_init=None, *, phi_mode=PHI_ELU1, want_o=True, nt
     b = _f64(beta)
     if b is not None:
         assert b.shape == (B, H, N)
+    a = _f64(alpha)
+    if a is not None:
+        assert a.shape == (B, H, N)
     si = _f64(s_init)
     if si is not None:
         assert si.shape == (B, H, Dk, Dv)
     o = np.empty((B, H, N, Dv)) if want_o else None
     s = np.empty((B, H, Dk, Dv))
-    rc = _load().oracle_delta(_ptr(q), _ptr(k), _ptr(v), _ptr(b), _ptr(si), _ptr(o), _ptr(s), B * H, N, Dk, Dv,
-                              phi_mode, nthreads or _threads(B * H))
+    rc = _load().oracle_delta(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(si), _ptr(o), _ptr(s), B * H, N,
+                              Dk, Dv, phi_mode, nthreads or _threads(B * H))
     if rc != 0:
         raise RuntimeError("oracle_delta failed")
     return o, s

@@ -454,17 +454,24 @@ int oracle_backward(const double *q, const double *k, const double *v,
  * order", section "The summary runs out of room"): before writing, the
  * summary is read with the key, and only the difference between the value
  * and that read is written, so that re-reading with the same key returns the
- * new value.  Per token, for one (batch, head) pair:
+ * new value.  The same section's gated form (Gated DeltaNet: a global decay
+ * combined with the selective overwrite) first decays the whole summary by
+ * a_t.  Per token, for one (batch, head) pair:
  *   kh_t = phi(k_t) / |phi(k_t)|_2             (unit key; a zero key writes nothing)
- *   u_t  = S_{t-1}^T kh_t                      (read before the write)
- *   S_t  = S_{t-1} + beta_t kh_t (v_t - u_t)^T (write the difference; beta_t = 1 unless given)
+ *   S'   = a_t S_{t-1}                         (a_t = 1 unless gated)
+ *   u_t  = S'^T kh_t                           (read before the write)
+ *   S_t  = S' + beta_t kh_t (v_t - u_t)^T      (write the difference; beta_t = 1 unless given)
  *   o_t  = S_t^T phi(q_t)                      (read with the query; no normalizer)
  * s holds the running state on entry and on exit. */
 static void delta_one(const double *q, const double *k, const double *v,
-                      const double *beta, double *o, double *s, int64_t N,
-                      int Dk, int Dv, int mode, double *kh, double *u)
+                      const double *alpha, const double *beta, double *o,
+                      double *s, int64_t N, int Dk, int Dv, int mode,
+                      double *kh, double *u)
 {
     for (int64_t t = 0; t < N; ++t) {
+        if (alpha)
+            for (int64_t e = 0; e < (int64_t)Dk * Dv; ++e)
+                s[e] *= alpha[t];
         const double *qt = q + t * Dk, *kt = k + t * Dk, *vt = v + t * Dv;
         double nrm = 0.0;
         for (int i = 0; i < Dk; ++i) {
@@ -495,12 +502,13 @@ static void delta_one(const double *q, const double *k, const double *v,
     }
 }
 
-/* Delta-rule forward over BH pairs; beta [BH][N] or NULL (all ones); s_init
- * NULL for zero; o, s_final may be NULL. */
+/* Delta-rule forward over BH pairs; alpha, beta [BH][N] or NULL (all ones);
+ * s_init NULL for zero; o, s_final may be NULL. */
 int oracle_delta(const double *q, const double *k, const double *v,
-                 const double *beta, const double *s_init, double *o,
-                 double *s_final, int64_t BH, int64_t N, int Dk, int Dv,
-                 int mode, int nthreads)
+                 const double *alpha, const double *beta,
+                 const double *s_init, double *o, double *s_final,
+                 int64_t BH, int64_t N, int Dk, int Dv, int mode,
+                 int nthreads)
 {
     if (!q || !k || !v || BH < 0 || N < 0 || Dk < 1 || Dv < 1)
         return -1;
@@ -517,8 +525,8 @@ int oracle_delta(const double *q, const double *k, const double *v,
             if (s_init)
                 memcpy(s, s_init + bh * Dk * Dv, sizeof(double) * Dk * Dv);
             delta_one(q + bh * N * Dk, k + bh * N * Dk, v + bh * N * Dv,
-                      beta ? beta + bh * N : NULL, o ? o + bh * N * Dv : NULL,
-                      s, N, Dk, Dv, mode, kh, u);
+                      alpha ? alpha + bh * N : NULL, beta ? beta + bh * N : NULL,
+                      o ? o + bh * N * Dv : NULL, s, N, Dk, Dv, mode, kh, u);
             if (s_final)
                 memcpy(s_final + bh * Dk * Dv, s, sizeof(double) * Dk * Dv);
         }

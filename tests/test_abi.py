@@ -178,9 +178,9 @@ def test_training_forward_and_backward_reject_bad_arguments(L):
     assert bwd(L, N=131072, ws=FAKE[10], wsb=need - 1) == EWORKSPACE
 
 
-def delta(L, q=FAKE[0], k=FAKE[1], v=FAKE[2], beta=None, o=FAKE[3], si=None, sf=None, B=1, H=1, N=64, Dk=64,
-          Dv=64, dtype=1, phi=0):
-    return L.linattn_forward_delta(q, k, v, beta, o, si, sf, B, H, N, Dk, Dv, dtype, phi, None)
+def delta(L, q=FAKE[0], k=FAKE[1], v=FAKE[2], alpha=None, beta=None, o=FAKE[3], si=None, sf=None, B=1, H=1, N=64,
+          Dk=64, Dv=64, dtype=1, phi=0):
+    return L.linattn_forward_delta(q, k, v, alpha, beta, o, si, sf, B, H, N, Dk, Dv, dtype, phi, None)
 
 
 def test_delta_rejects_bad_arguments(L):
@@ -192,6 +192,7 @@ def test_delta_rejects_bad_arguments(L):
     assert delta(L, o=FAKE[0]) == EINVAL    # o overlaps q
     assert delta(L, sf=FAKE[3]) == EINVAL   # s_final overlaps o
     assert delta(L, N=0) == EINVAL
+    assert delta(L, alpha=FAKE[3]) == EINVAL  # gates overlap o
 
 
 def snaps(L, positions=(0, 5), n=None, ss=FAKE[6], zs=FAKE[7], N=64, Dk=64, Dv=64, dtype=1, alpha=None):

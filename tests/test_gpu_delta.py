@@ -5,8 +5,9 @@ the final state per head with oracle.delta on the same seeded bf16 inputs
 (q, k, v drawn N(0, 1): with elu + 1 the unit keys are then far from all
 parallel).  Shapes span several chunks, ragged tails, one token, both head
 dims and their mix; beta absent (full overwrite) or drawn in (0, 1); an
-initial state; and the product-order page's worked example (keys in two of 64
-dims, the identity map) on the GPU path.
+initial state; the gated form (gates sigmoid(N(4, 1)) with an exact zero, and
+gates of one against the ungated kernel); and the product-order page's worked
+example (keys in two of 64 dims, the identity map) on the GPU path.
 """
 import json
 import os
@@ -34,12 +35,13 @@ def make(B, H, N, Dk, Dv, seed, with_beta=False):
     return q, k, v, beta
 
 
-def check(q, k, v, beta=None, s0=None, phi=la.PHI_ELU1):
+def check(q, k, v, beta=None, s0=None, phi=la.PHI_ELU1, alpha=None):
     d = [x.to(DEV) for x in (q, k, v)]
     o, s = la.linattn_forward_delta(*d, None if beta is None else beta.to(DEV),
-                                    None if s0 is None else s0.to(DEV), phi=phi)
+                                    None if s0 is None else s0.to(DEV), phi=phi,
+                                    alpha=None if alpha is None else alpha.to(DEV))
     torch.cuda.synchronize()
-    ro, rs = oracle.delta(q, k, v, beta, s0, phi_mode=phi)
+    ro, rs = oracle.delta(q, k, v, beta, s0, alpha=alpha, phi_mode=phi)
     tol = TOL[BF]
     assert_close("O", o.cpu(), ro, tol)
     assert_close("S", s.cpu(), rs, tol, per="head")
@@ -68,6 +70,26 @@ def test_delta_with_initial_state_and_resume():
                                       beta[:, :, 256:].to(DEV), s1)
     torch.cuda.synchronize()
     assert torch.equal(o2.cpu(), o[:, :, 256:].cpu()) and torch.equal(s2.cpu(), s.cpu())
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 700, 128, 128), (2, 2, 333, 64, 128), (1, 1, 65, 128, 64)])
+def test_gated_delta(shape):
+    # gates a = sigmoid(N(4, 1)) (a memory of ~50 tokens), one exact zero gate
+    q, k, v, beta = make(*shape, seed=1240 + sum(shape), with_beta=True)
+    a = synth.gate_heads(1240 + sum(shape), *shape[:3])
+    a[0, 0, shape[2] // 2] = 0.0
+    s0 = torch.randn(*shape[:2], shape[3], shape[4], generator=torch.Generator().manual_seed(9)) * 0.1
+    check(q, k, v, beta, s0, alpha=a)
+    check(q, k, v, alpha=a)
+
+
+def test_gate_of_one_equals_ungated_on_the_gpu():
+    q, k, v, _ = make(1, 2, 200, 128, 128, seed=1250)
+    d = [x.to(DEV) for x in (q, k, v)]
+    o1, s1 = la.linattn_forward_delta(*d)
+    o2, s2 = la.linattn_forward_delta(*d, alpha=torch.ones(1, 2, 200, device=DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
 
 
 def test_worked_example_on_the_gpu():

@@ -102,3 +102,41 @@ def test_only_the_key_direction_matters():
         o2, s2 = oracle.delta(q, k * scale, v, phi_mode=mode)
         np.testing.assert_allclose(o2, o1, rtol=1e-10, atol=1e-12)
         np.testing.assert_allclose(s2, s1, rtol=1e-10, atol=1e-12)
+
+
+# ---- the gated form (the same section: Gated DeltaNet, a global decay combined with the overwrite)
+
+def test_gate_of_one_is_the_plain_rule():
+    q, k, v = rand(1, 2, 30, 6, 4, seed=37)
+    o1, s1 = oracle.delta(q, k, v)
+    o2, s2 = oracle.delta(q, k, v, alpha=np.ones((1, 2, 30)))
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(s1, s2)
+
+
+def test_zero_gate_forgets_everything_before():
+    # a_t = 0 clears the summary: from token t on, the run equals a fresh run
+    # started at t (u_t = 0, S_t = beta_t kh_t v_t^T)
+    q, k, v = rand(1, 1, 40, 5, 3, seed=38)
+    a = np.random.default_rng(39).uniform(0.5, 1.0, (1, 1, 40))
+    a[0, 0, 17] = 0.0
+    s0 = np.random.default_rng(40).standard_normal((1, 1, 5, 3))
+    o, s = oracle.delta(q, k, v, alpha=a, s_init=s0)
+    o_tail, s_tail = oracle.delta(q[:, :, 17:], k[:, :, 17:], v[:, :, 17:], alpha=np.concatenate(
+        [np.ones((1, 1, 1)), a[:, :, 18:]], axis=2))
+    np.testing.assert_allclose(o[:, :, 17:], o_tail, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(s, s_tail, rtol=1e-12, atol=1e-12)
+
+
+def test_gated_orthogonal_unit_keys_are_the_decayed_sum():
+    # distinct orthonormal keys never read each other, so the state is the
+    # additive sum of outer products, each decayed by the gates after it
+    D, Dv = 6, 3
+    r = np.random.default_rng(41)
+    basis = np.linalg.qr(r.standard_normal((D, D)))[0]
+    k = basis[r.permutation(D)][None, None]
+    v = r.standard_normal((1, 1, D, Dv))
+    a = r.uniform(0.3, 1.0, (1, 1, D))
+    _, s = oracle.delta(k, k, v, alpha=a, phi_mode=ID)
+    ref = sum(np.prod(a[0, 0, j + 1:]) * np.outer(k[0, 0, j], v[0, 0, j]) for j in range(D))
+    np.testing.assert_allclose(s[0, 0], ref, rtol=1e-12, atol=1e-12)

@@ -42,6 +42,7 @@ DELTA_MUTANTS = {
     "delta_key_not_unit": ("kh[i] = nrm > 0.0 ? kh[i] / nrm : 0.0;", "kh[i] = kh[i];"),
     "delta_writes_value": ("b * kh[i] * (vt[j] - u[j]);", "b * kh[i] * vt[j];"),
     "delta_beta_ignored": ("const double b = beta ? beta[t] : 1.0;", "const double b = 1.0;"),
+    "delta_gate_ignored": ("s[e] *= alpha[t];", "s[e] *= 1.0;"),
     "delta_read_with_query": ("acc += s[(int64_t)i * Dv + j] * kh[i];", "acc += s[(int64_t)i * Dv + j] * phi(q[t * Dk + i], mode);"),
 }
 LOWP_MUTANTS = {
