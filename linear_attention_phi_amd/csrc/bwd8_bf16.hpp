@@ -106,30 +106,39 @@ __device__ __forceinline__ void stage_dy(const Units<DV> &g, const float (&den)[
     }
 }
 
-// Row sums of phi(Q) in fp32 from the raw rows (sum over the DK / 8
-// consecutive lanes of a row), into sSq[row].
-template <int DK, int PHI>
-__device__ __forceinline__ void stage_phi_rowsum(const Units<DK> &q, float *sSq, int tid) {
+// The dQ pass's staging: phi(Q) in bf16 (the values every later use of phi(q)
+// reads, so that the pass's dd stays consistent with its own arithmetic), the
+// row sums of those bf16 values in fp32 (sum over the DK / 8 consecutive lanes
+// of a row, into sSq[row]), the features KF of K, and V as is.
+template <int DK, int DV, int PHI, int KF, bool DD>
+__device__ __forceinline__ void stage_dq(const BwdBuf<DK, DV, DD> &b, uint16_t *sQ, uint16_t *sK, uint16_t *sV,
+                                         float *sSq, int tid) {
     constexpr int CG = Units<DK>::CG;
 #pragma unroll
     for (int i = 0; i < Units<DK>::N; ++i) {
-        const uint32_t wv[4] = {q.r[i].x, q.r[i].y, q.r[i].z, q.r[i].w};
+        const int row = Units<DK>::row_of(tid, i), col = Units<DK>::col_of(tid, i);
+        const uint4 f = phi_pack8(b.q.r[i], PHI);
+        *reinterpret_cast<uint4 *>(sQ + Tile<DK>::off(row, col)) = f;
+        const uint32_t fw[4] = {f.x, f.y, f.z, f.w};
         float x = 0.f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x += phi_fast(bf_lo(wv[e]), PHI) + phi_fast(bf_hi(wv[e]), PHI);
+        for (int e = 0; e < 4; ++e) x += bf_lo(fw[e]) + bf_hi(fw[e]);
 #pragma unroll
         for (int m = 1; m < CG; m <<= 1) x += __shfl_xor(x, m, 64);
-        if (Units<DK>::col_of(tid, i) == 0) sSq[Units<DK>::row_of(tid, i)] = x;
+        if (col == 0) sSq[row] = x;
+        *reinterpret_cast<uint4 *>(sK + Tile<DK>::off(row, col)) = phi_pack8(b.k.r[i], KF);
     }
+#pragma unroll
+    for (int i = 0; i < Units<DV>::N; ++i)
+        *reinterpret_cast<uint4 *>(sV + Tile<DV>::off(Units<DV>::row_of(tid, i), Units<DV>::col_of(tid, i))) =
+            b.v.r[i];
 }
 
-// The staged Q and K rows into their tiles through feature map QF / KF
-// (phi_fast modes, or kRaw for the inputs as they are), and V as is.
-constexpr int kRaw = -1;
+// The staged Q and K rows into their tiles through feature maps QF / KF
+// (phi_fast modes), and V as is.
 template <int F>
 __device__ __forceinline__ uint4 feat8(uint4 raw) {
-    if constexpr (F == kRaw) return raw;
-    else return phi_pack8(raw, F);
+    return phi_pack8(raw, F);
 }
 template <int DK, int DV, int QF, int KF, bool DD>
 __device__ __forceinline__ void stage_qkv(const BwdBuf<DK, DV, DD> &b, uint16_t *sQ, uint16_t *sK, uint16_t *sV,
@@ -156,13 +165,12 @@ __device__ __forceinline__ bf16x8 tiles_row_operand(const uint16_t *t, int row, 
 }
 
 // phi'(x) for elu + 1 (1 for the identity map): 1 on x >= 0, exp(x) below,
-// from phi(x) = exp(x) < 1 there (kScalePhi) or from x itself (kScaleRaw).
-constexpr int kScaleNone = 0, kScalePhi = 1, kScaleRaw = 2;
+// read from phi(x) = exp(x) < 1 there (kScalePhi).
+constexpr int kScaleNone = 0, kScalePhi = 1;
 template <int PHI, int MODE>
 __device__ __forceinline__ float dphi_of(float f) {
     if (PHI || MODE == kScaleNone) return 1.f;
-    if (MODE == kScalePhi) return fminf(1.f, f);
-    return f >= 0.f ? 1.f : __builtin_amdgcn_exp2f(f * 1.4426950408889634f);
+    return fminf(1.f, f);
 }
 
 // Store 16 rows x (2 * NTW) permuted tiles of a gradient, scaled by phi'
@@ -232,7 +240,7 @@ __global__ __launch_bounds__(kThreads8, 1) void bwd_dq8_bf16(
     constexpr int FEAT = KAPPA ? kFeatElu : PHI;
     constexpr int KSV = DV / 32;     // k-steps over value dims
     constexpr int NTK = DK / 16 / 2; // key-dim tiles per wave
-    __shared__ __attribute__((aligned(16))) uint16_t sQ[kChunk * TK::RS]; // raw q
+    __shared__ __attribute__((aligned(16))) uint16_t sQ[kChunk * TK::RS]; // phi(q), bf16
     __shared__ __attribute__((aligned(16))) uint16_t sK[kChunk * TK::RS]; // features of k (elu for elu + 1)
     __shared__ __attribute__((aligned(16))) uint16_t sV[kChunk * TV::RS];
     __shared__ __attribute__((aligned(16))) uint16_t sDY[kChunk * TV::RS];
@@ -284,8 +292,7 @@ __global__ __launch_bounds__(kThreads8, 1) void bwd_dq8_bf16(
 #pragma unroll
             for (int i = 0; i < Units<DV>::N; ++i) add_bf16x8(vsum, buf.v.r[i]);
         }
-        stage_qkv<DK, DV, kRaw, FEAT>(buf, sQ, sK, sV, tid);
-        stage_phi_rowsum<DK, PHI>(buf.q, sSq, tid);
+        stage_dq<DK, DV, PHI, FEAT>(buf, sQ, sK, sV, sSq, tid);
         stage_dy<DV>(buf.g, buf.den, buf.dd, sDY, nullptr, tid);
         if (c + 1 < nch) issue(buf, c + 1);
         __syncthreads();
@@ -390,10 +397,10 @@ __global__ __launch_bounds__(kThreads8, 1) void bwd_dq8_bf16(
                 const uint32_t rw[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
-                    fq[2 * pp][2 * e] = phi_fast(bf_lo(rw[e]), PHI);
-                    fq[2 * pp][2 * e + 1] = phi_fast(bf_hi(rw[e]), PHI);
-                    fq[2 * pp + 1][2 * e] = phi_fast(bf_lo(rw[2 + e]), PHI);
-                    fq[2 * pp + 1][2 * e + 1] = phi_fast(bf_hi(rw[2 + e]), PHI);
+                    fq[2 * pp][2 * e] = bf_lo(rw[e]);
+                    fq[2 * pp][2 * e + 1] = bf_hi(rw[e]);
+                    fq[2 * pp + 1][2 * e] = bf_lo(rw[2 + e]);
+                    fq[2 * pp + 1][2 * e + 1] = bf_hi(rw[2 + e]);
                 }
             }
             // phi(q) . A and phi(q) . zeta over this half of the key dims
@@ -431,7 +438,7 @@ __global__ __launch_bounds__(kThreads8, 1) void bwd_dq8_bf16(
             }
             const bool ok = tq < valid;
             if (ok && dh == 0 && g == 0) dd_out[row0 + (size_t)c * kChunk + tq] = ddq;
-            store_grad_rows<DK, NTK, kScaleRaw, PHI>(acc, dh * NTK, sQ, tq,
+            store_grad_rows<DK, NTK, kScalePhi, PHI>(acc, dh * NTK, sQ, tq,
                                                      dq + (row0 + (size_t)c * kChunk + tq) * DK, ok, g);
         };
         switch (qblk_w) {
