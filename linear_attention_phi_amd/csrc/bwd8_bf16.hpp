@@ -283,9 +283,13 @@ __global__ __launch_bounds__(kThreads8, 1) void bwd_dq8_bf16(
         const size_t r = row0 + (size_t)c * kChunk;
         b.load(q + r * DK, k + r * DK, v + r * DV, dout + r * DV, den + r, nullptr, rows_in(c), tid);
     };
-    BwdBuf<DK, DV, false> buf;
-    if (nch > 0) issue(buf, 0);
-    for (int c = 0; c < nch; ++c) {
+    // two chunks in flight: the loads for chunk c + 2 are issued while chunk c
+    // is worked on (the loop runs two chunks per pass so that each buffer
+    // stays in its own registers)
+    BwdBuf<DK, DV, false> buf0, buf1;
+    if (nch > 0) issue(buf0, 0);
+    if (nch > 1) issue(buf1, 1);
+    auto step = [&](BwdBuf<DK, DV, false> &buf, const int c) {
         const int valid = rows_in(c);
         float vsum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         if (KAPPA) {
@@ -294,7 +298,7 @@ __global__ __launch_bounds__(kThreads8, 1) void bwd_dq8_bf16(
         }
         stage_dq<DK, DV, PHI, FEAT>(buf, sQ, sK, sV, sSq, tid);
         stage_dy<DV>(buf.g, buf.den, buf.dd, sDY, nullptr, tid);
-        if (c + 1 < nch) issue(buf, c + 1);
+        if (c + 2 < nch) issue(buf, c + 2);
         __syncthreads();
         // tokens before this chunk (the constant part's count)
         const float n_prev = (float)(t_begin + c * kChunk);
@@ -456,6 +460,10 @@ __global__ __launch_bounds__(kThreads8, 1) void bwd_dq8_bf16(
             state_to_lds();
             if (KAPPA && tid < DV) sVb[tid] += colsum_from_lds<DV>(sVp, tid);
         }
+    };
+    for (int c = 0; c < nch; c += 2) {
+        step(buf0, c);
+        if (c + 1 < nch) step(buf1, c + 1);
     }
 }
 
@@ -464,7 +472,7 @@ __global__ __launch_bounds__(kThreads8, 1) void bwd_dq8_bf16(
 // skipped, cell j holds sub-segment R + j): dR = phi(Q)^T dY and
 // dr = phi(Q)^T dd, in the layout of the forward's segment states.
 template <int DK, int DV, int PHI>
-__global__ __launch_bounds__(kThreads8, 2) void bwd_rstate8_bf16(
+__global__ __launch_bounds__(kThreads8, 4) void bwd_rstate8_bf16(
     const uint16_t *__restrict__ q, const float *__restrict__ den, const float *__restrict__ dd,
     const uint16_t *__restrict__ dout, float *__restrict__ ws, int N, int cells_per_bh, int cell_stride,
     int first_sub, int sub_len) {
@@ -500,20 +508,26 @@ __global__ __launch_bounds__(kThreads8, 2) void bwd_rstate8_bf16(
             b.dd[i] = buffer_load_f32(rd, Units<DV>::row_of(tid, i) * 4);
         }
     };
-    Buf b;
-    if (nch > 0) issue(b, 0);
-    for (int c = 0; c < nch; ++c) {
+    // two chunks in flight (one register buffer per chunk of a pair)
+    Buf b0, b1;
+    if (nch > 0) issue(b0, 0);
+    if (nch > 1) issue(b1, 1);
+    auto step = [&](Buf &b, const int c) {
 #pragma unroll
         for (int i = 0; i < Units<DK>::N; ++i)
             *reinterpret_cast<uint4 *>(sQ + Tile<DK>::off(Units<DK>::row_of(tid, i), Units<DK>::col_of(tid, i))) =
                 phi_pack8(b.q.r[i], PHI);
         stage_dy<DV>(b.g, b.den, b.dd, sDY, sDD, tid);
-        if (c + 1 < nch) issue(b, c + 1);
+        if (c + 2 < nch) issue(b, c + 2);
         __syncthreads();
         const bf16x8 wop[kChunk / 32] = {dd_operand(sDD, 0, lane >> 4), dd_operand(sDD, 1, lane >> 4)};
         // rows past the end have dY = 0 and dd = 0: nothing to take back out
         state8_update_w<DK, DV>(st, sQ, sDY, w, lane, wop, 0.f);
         __syncthreads();
+    };
+    for (int c = 0; c < nch; c += 2) {
+        step(b0, c);
+        if (c + 1 < nch) step(b1, c + 1);
     }
     float *dst = ws + ((size_t)bh * cell_stride + cell) * (size_t)(DK * DV + DK);
     state8_store<DK, DV>(st, dst, w, lane);
@@ -570,13 +584,15 @@ __global__ __launch_bounds__(kThreads8, 1) void bwd_dkv8_bf16(
         const size_t r = row0 + (size_t)c * kChunk;
         b.load(q + r * DK, k + r * DK, v + r * DV, dout + r * DV, den + r, dd + r, rows_in(c), tid);
     };
-    BwdBuf<DK, DV> buf;
-    if (nch > 0) issue(buf, nch - 1);
-    for (int c = nch - 1; c >= 0; --c) {
+    // two chunks in flight, as in the dQ pass
+    BwdBuf<DK, DV> buf0, buf1;
+    if (nch > 0) issue(buf0, nch - 1);
+    if (nch > 1) issue(buf1, nch - 2);
+    auto step = [&](BwdBuf<DK, DV> &buf, const int c) {
         const int valid = rows_in(c);
         stage_qkv<DK, DV, PHI, PHI>(buf, sQ, sK, sV, tid);
         stage_dy<DV>(buf.g, buf.den, buf.dd, sDY, sDD, tid);
-        if (c > 0) issue(buf, c - 1);
+        if (c > 1) issue(buf, c - 2);
         __syncthreads();
 
         auto chunk_work = [&](auto kblk_c) {
@@ -719,6 +735,10 @@ __global__ __launch_bounds__(kThreads8, 1) void bwd_dkv8_bf16(
         state8_update_w<DK, DV>(st, sQ, sDY, w, lane, wop, 0.f);
         __syncthreads();
         if (c > 0) state_to_lds();
+    };
+    for (int c = nch - 1; c >= 0; c -= 2) {
+        step(buf0, c);
+        if (c > 0) step(buf1, c - 1);
     }
 }
 
