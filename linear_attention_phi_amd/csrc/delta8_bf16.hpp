@@ -53,15 +53,29 @@ __device__ __forceinline__ f32x4 mfma16x16x16(s16x4 a, s16x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
-// a b + c with both factors split into bf16 high and low parts (three products).
-__device__ __forceinline__ f32x4 mfma16_split(float4 a, f32x4 b, f32x4 c) {
-    s16x4 ahi, alo, bhi, blo;
-    split_bf16x4(a.x, a.y, a.z, a.w, ahi, alo);
-    split_bf16x4(b[0], b[1], b[2], b[3], bhi, blo);
+// a b + c from the bf16 high and low parts of both factors (three products;
+// the low parts' product is below the fp32 accumulation's resolution).
+__device__ __forceinline__ f32x4 mfma16_hl(s16x4 ahi, s16x4 alo, s16x4 bhi, s16x4 blo, f32x4 c) {
     c = mfma16x16x16(ahi, bhi, c);
     c = mfma16x16x16(alo, bhi, c);
     return mfma16x16x16(ahi, blo, c);
 }
+
+// One value's high and low bf16 parts, as split_bf16x4 forms them.
+__device__ __forceinline__ void split_bf16x1(float x, uint16_t &hi, uint16_t &lo) {
+    const uint32_t h = f32_to_bf16_bits(x);
+    hi = (uint16_t)h;
+    lo = (uint16_t)f32_to_bf16_bits(x - __uint_as_float(h << 16));
+}
+
+// The solved rows D as bf16 high and low parts, kept in the fp32 right-hand
+// side's own rows: the 16 columns 16 m .. 16 m + 15 of a row (64 bytes as
+// fp32, owned by one wave in the solve) hold their 16 high parts, then their
+// 16 low parts.  Element offsets of the high part; the low part is 16 later.
+template <int XS>
+struct DSplitTile {
+    __device__ static __forceinline__ int off(int r, int c) { return r * (2 * XS) + ((c >> 4) << 5) + (c & 15); }
+};
 
 // GATED: the summary is first decayed by a_t (the gated form, Gated DeltaNet).
 // With g_t the product of the chunk's gates through t and D(j -> t) the
@@ -86,9 +100,13 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8_bf16(
     __shared__ __attribute__((aligned(16))) uint16_t sV[kChunk * TV::RS]; // V, then D (bf16)
     __shared__ __attribute__((aligned(16))) uint16_t sS[DK * DV];         // S_0 in bf16
     __shared__ __attribute__((aligned(16))) float sX[kChunk * XS];        // diag(beta)(V - Kh S_0), then D
-    __shared__ __attribute__((aligned(16))) float sA[kChunk * AS];        // diag(beta) tril(Kh Kh^T, -1)
-    __shared__ __attribute__((aligned(16))) float sB[kChunk];             // beta (0 past the end)
-    __shared__ __attribute__((aligned(16))) float sT[4 * 16 * 16];        // inverses of A's diagonal blocks
+    // diag(beta) tril(Kh Kh^T, -1): the diagonal blocks in fp32; below them the
+    // negated blocks as bf16 high and low parts, 4 + 4 per 16-byte group
+    __shared__ __attribute__((aligned(16))) float sA[kChunk * AS];
+    __shared__ __attribute__((aligned(16))) float sB[kChunk]; // beta (0 past the end)
+    // inverses of A's diagonal blocks, bf16 high and low parts
+    __shared__ __attribute__((aligned(16))) uint16_t sTh[4 * 16 * 16];
+    __shared__ __attribute__((aligned(16))) uint16_t sTl[4 * 16 * 16];
     // gated: the chunk's inclusive gate prefix per token (log2 sum, zero count)
     __shared__ __attribute__((aligned(16))) float sGl[GATED ? kChunk : 4];
     __shared__ __attribute__((aligned(16))) int sGz[GATED ? kChunk : 4];
@@ -107,6 +125,7 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8_bf16(
     struct Buf {
         Units<DK> q, k;
         Units<DV> v;
+        float beta, alpha; // token tid of the chunk (threads below kChunk)
     };
     auto rows_in = [&](int c) { return min(kChunk, N - c * kChunk); };
     auto issue = [&](Buf &b, int c) {
@@ -115,6 +134,11 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8_bf16(
         b.q.load(q + r * DK, nv, tid);
         b.k.load(k + r * DK, nv, tid);
         b.v.load(v + r * DV, nv, tid);
+        if (tid < kChunk) {
+            const bool in = tid < nv;
+            b.beta = BETA ? (in ? beta[r + tid] : 0.f) : (in ? 1.f : 0.f);
+            b.alpha = GATED && in ? alpha[r + tid] : 1.f;
+        }
     };
     Buf buf;
     if (nch > 0) issue(buf, 0);
@@ -148,11 +172,10 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8_bf16(
                 *reinterpret_cast<uint4 *>(sV + TV::off(Units<DV>::row_of(tid, i), Units<DV>::col_of(tid, i))) =
                     buf.v.r[i];
             if (tid < kChunk) {
-                const size_t r = row0 + (size_t)c * kChunk + tid;
-                sB[tid] = tid < valid ? (BETA ? beta[r] : 1.f) : 0.f;
+                sB[tid] = buf.beta;
                 if (GATED) {
                     ChunkGates cg;
-                    cg.build(tid < valid ? alpha[r] : 1.f, tid < valid);
+                    cg.build(buf.alpha, tid < valid);
                     sGl[tid] = cg.lsum;
                     sGz[tid] = cg.zeros;
                 }
@@ -219,7 +242,14 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8_bf16(
                     a4.y = 16 * cb + 4 * g + 1 < tk ? b * gr[1] : 0.f;
                     a4.z = 16 * cb + 4 * g + 2 < tk ? b * gr[2] : 0.f;
                     a4.w = 16 * cb + 4 * g + 3 < tk ? b * gr[3] : 0.f;
-                    *reinterpret_cast<float4 *>(sA + tk * AS + 16 * cb + 4 * g) = a4;
+                    if (cb == blk_w) {
+                        *reinterpret_cast<float4 *>(sA + tk * AS + 16 * cb + 4 * g) = a4;
+                    } else {
+                        s16x4 hi, lo;
+                        split_bf16x4(-a4.x, -a4.y, -a4.z, -a4.w, hi, lo);
+                        const uint2 h2 = __builtin_bit_cast(uint2, hi), l2 = __builtin_bit_cast(uint2, lo);
+                        *reinterpret_cast<uint4 *>(sA + tk * AS + 16 * cb + 4 * g) = make_uint4(h2.x, h2.y, l2.x, l2.y);
+                    }
                 } else {
                     *reinterpret_cast<float4 *>(sA + tk * AS + 16 * cb + 4 * g) = make_float4(0.f, 0.f, 0.f, 0.f);
                 }
@@ -227,12 +257,10 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8_bf16(
         }
         __syncthreads();
 
-        // ---- solve (I + A) D = X.  Wave 0 inverts the four 16 x 16 diagonal
-        // blocks (lane = block * 16 + column: forward substitution on a unit
-        // vector); then each wave takes 16 value columns through the blocks in
-        // order, Y_b = X_b - sum_{k < b} A_bk D_k and D_b = (I + A_bb)^-1 Y_b, as
-        // 16 x 16 x 16 MFMAs on bf16 high and low parts (about 16 significant
-        // bits), with no workgroup barrier in between.
+        // ---- wave 0 inverts the four 16 x 16 diagonal blocks of I + A (lane =
+        // block * 16 + column: forward substitution on a unit vector).  Meanwhile
+        // (wave 0: afterwards) each wave forms the parts of its outputs that do
+        // not depend on D: Q S_0 and the masked scores Kh . phi(q).
         if (w == 0) {
             const int lane = tid & 63;
             const int b = lane >> 4, cc = lane & 15;
@@ -246,54 +274,22 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8_bf16(
                 t[r] = x;
             }
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sT[(16 * b + r) * 16 + cc] = t[r];
+            for (int r = 0; r < 16; ++r) split_bf16x1(t[r], sTh[(16 * b + r) * 16 + cc], sTl[(16 * b + r) * 16 + cc]);
         }
-        __syncthreads();
-        if (w < DV / 16) {
-            const int lane = lane_in_loop(tid & 63);
-            const int l16 = lane & 15, g = lane >> 4;
-            const int col = 16 * w + l16;
-            f32x4 dblk[4];
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                f32x4 y;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) y[i] = sX[(16 * b + 4 * g + i) * XS + col];
-#pragma unroll
-                for (int kb = 0; kb < b; ++kb) {
-                    const float4 a4 = *reinterpret_cast<const float4 *>(sA + (16 * b + l16) * AS + 16 * kb + 4 * g);
-                    y = mfma16_split(make_float4(-a4.x, -a4.y, -a4.z, -a4.w), dblk[kb], y);
-                }
-                const float4 t4 = *reinterpret_cast<const float4 *>(sT + (16 * b + l16) * 16 + 4 * g);
-                dblk[b] = mfma16_split(t4, y, f32x4{0.f, 0.f, 0.f, 0.f});
-            }
-            // D as solved for the outputs; for the state update each row is
-            // decayed to the chunk's end
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = 16 * b + 4 * g + i;
-                    sX[row * XS + col] = dblk[b][i];
-                    const float dk = GATED ? dec(valid - 1, row) : 1.f;
-                    sV[TV::off(row, col)] = (uint16_t)f32_to_bf16_bits(dblk[b][i] * dk);
-                }
-            }
-        }
-        __syncthreads();
-
-        // ---- outputs O^T = S_0^T phi(Q)^T + D^T tril(Q Kh^T)^T, and the state update
-        {
+        auto chunk_rest = [&](auto blk_c) {
+            constexpr int qblk = decltype(blk_c)::value;
             const int lane = lane_in_loop(tid & 63);
             const int l16 = lane & 15, g = lane >> 4, qd = lane & 3;
-            auto chunk_out = [&](auto blk_c) {
-                constexpr int qblk = decltype(blk_c)::value;
-                const int tq = 16 * qblk + l16;
+            const int tq = 16 * qblk + l16;
+            // O^T = S_0^T phi(Q)^T (+ the D part below)
+            f32x4 acc[NTV];
+            // scores^T [key][query] = Kh_key . phi(q)_query, keys at or before the query
+            f32x4 sc[4];
+            {
                 bf16x8 qa[KSK];
 #pragma unroll
                 for (int ks = 0; ks < KSK; ++ks)
                     qa[ks] = *reinterpret_cast<const bf16x8 *>(sQ + TK::off(tq, 32 * ks + 8 * g));
-                f32x4 acc[NTV];
 #pragma unroll
                 for (int j = 0; j < NTV; ++j) {
                     acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -306,8 +302,6 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8_bf16(
                     }
                     if (GATED) acc[j] *= gam(tq);
                 }
-                // scores^T [key][query] = Kh_key . phi(q)_query, keys at or before the query
-                f32x4 sc[4];
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb) {
                     sc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -324,50 +318,101 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8_bf16(
                         }
                     }
                 }
-                // D^T tril(.)^T with both factors split into bf16 high and low
-                // parts (three products): the new writes largely cancel the
-                // old summary along the keys, and one bf16 rounding of either
-                // factor shows in O at the percent level
+            }
+            __syncthreads();
+
+            // ---- solve (I + A) D = X: each wave takes 16 value columns through
+            // the blocks in order, Y_b = X_b - sum_{k < b} A_bk D_k and
+            // D_b = (I + A_bb)^-1 Y_b, as 16 x 16 x 16 MFMAs on bf16 high and low
+            // parts (about 16 significant bits), with no workgroup barrier in
+            // between.
+            if (w < DV / 16) {
+                const int col = 16 * w + l16;
+                f32x4 dblk[4];
+                s16x4 dh4[4], dl4[4];
 #pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-                    if (2 * s2 <= qblk) {
-                        float x[8];
+                for (int b = 0; b < 4; ++b) {
+                    f32x4 y;
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            x[i] = sc[2 * s2][i];
-                            x[4 + i] = sc[2 * s2 + 1][i];
-                        }
-                        bf16x8 bhi, blo;
-                        split_bf16x8(x, bhi, blo);
-                        const int klo = 32 * s2 + 4 * g, khi = klo + 16;
+                    for (int i = 0; i < 4; ++i) y[i] = sX[(16 * b + 4 * g + i) * XS + col];
 #pragma unroll
-                        for (int j = 0; j < NTV; ++j) {
-                            const int nt = dh * NTV + j;
-                            // this lane's column of D (value perm_dv(nt, l16)), rows klo.. and khi..
-                            const int col = perm_dv(nt, l16);
-                            float dcol[8];
+                    for (int kb = 0; kb < b; ++kb) {
+                        const uint4 a = *reinterpret_cast<const uint4 *>(sA + (16 * b + l16) * AS + 16 * kb + 4 * g);
+                        y = mfma16_hl(__builtin_bit_cast(s16x4, make_uint2(a.x, a.y)),
+                                      __builtin_bit_cast(s16x4, make_uint2(a.z, a.w)), dh4[kb], dl4[kb], y);
+                    }
+                    const uint2 th = *reinterpret_cast<const uint2 *>(sTh + (16 * b + l16) * 16 + 4 * g);
+                    const uint2 tl = *reinterpret_cast<const uint2 *>(sTl + (16 * b + l16) * 16 + 4 * g);
+                    s16x4 yh, yl;
+                    split_bf16x4(y[0], y[1], y[2], y[3], yh, yl);
+                    dblk[b] = mfma16_hl(__builtin_bit_cast(s16x4, th), __builtin_bit_cast(s16x4, tl), yh, yl,
+                                        f32x4{0.f, 0.f, 0.f, 0.f});
+                    split_bf16x4(dblk[b][0], dblk[b][1], dblk[b][2], dblk[b][3], dh4[b], dl4[b]);
+                }
+                // every read of this wave's right-hand side columns comes before
+                // D is written over them
+                asm volatile("" ::: "memory");
+                // D's high and low parts for the outputs; for the state update
+                // each row is decayed to the chunk's end
+                uint16_t *sXh = reinterpret_cast<uint16_t *>(sX);
 #pragma unroll
-                            for (int r = 0; r < 4; ++r) {
-                                dcol[r] = sX[(klo + r) * XS + col];
-                                dcol[4 + r] = sX[(khi + r) * XS + col];
-                            }
-                            bf16x8 dhi, dlo;
-                            split_bf16x8(dcol, dhi, dlo);
-                            acc[j] = mfma16x16x32(dhi, bhi, acc[j]);
-                            acc[j] = mfma16x16x32(dlo, bhi, acc[j]);
-                            acc[j] = mfma16x16x32(dhi, blo, acc[j]);
-                        }
+                for (int b = 0; b < 4; ++b) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int row = 16 * b + 4 * g + i;
+                        const int o = DSplitTile<XS>::off(row, col);
+                        sXh[o] = (uint16_t)dh4[b][i];
+                        sXh[o + 16] = (uint16_t)dl4[b][i];
+                        if (GATED)
+                            sV[TV::off(row, col)] = (uint16_t)f32_to_bf16_bits(dblk[b][i] * dec(valid - 1, row));
+                        else
+                            sV[TV::off(row, col)] = (uint16_t)dh4[b][i];
                     }
                 }
-                store_grad_rows<DV, NTV, kScaleNone, PHI>(acc, dh * NTV, nullptr, tq,
-                                                          o + (row0 + (size_t)c * kChunk + tq) * DV, tq < valid, g);
-            };
-            switch (blk_w) {
-            case 0: chunk_out(std::integral_constant<int, 0>{}); break;
-            case 1: chunk_out(std::integral_constant<int, 1>{}); break;
-            case 2: chunk_out(std::integral_constant<int, 2>{}); break;
-            default: chunk_out(std::integral_constant<int, 3>{}); break;
             }
+            __syncthreads();
+
+            // ---- outputs: O^T += D^T tril(Q Kh^T)^T with both factors split into
+            // bf16 high and low parts (three products): the new writes largely
+            // cancel the old summary along the keys, and one bf16 rounding of
+            // either factor shows in O at the percent level
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                if (2 * s2 <= qblk) {
+                    float x[8];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        x[i] = sc[2 * s2][i];
+                        x[4 + i] = sc[2 * s2 + 1][i];
+                    }
+                    bf16x8 bhi, blo;
+                    split_bf16x8(x, bhi, blo);
+                    const int klo = 32 * s2 + 4 * g, khi = klo + 16;
+                    const uint16_t *sXh = reinterpret_cast<const uint16_t *>(sX);
+#pragma unroll
+                    for (int j = 0; j < NTV; ++j) {
+                        const int nt = dh * NTV + j;
+                        // this lane's column of D (value perm_dv(nt, l16)), rows klo.. and khi..
+                        const int colq = 32 * (nt >> 1) + 8 * qd + 4 * (nt & 1);
+                        const bf16x8 dhi = tr_operand_in<DSplitTile<XS>>(sXh, klo, khi, colq, lane);
+                        const bf16x8 dlo = tr_operand_in<DSplitTile<XS>>(sXh + 16, klo, khi, colq, lane);
+                        acc[j] = mfma16x16x32(dhi, bhi, acc[j]);
+                        acc[j] = mfma16x16x32(dlo, bhi, acc[j]);
+                        acc[j] = mfma16x16x32(dhi, blo, acc[j]);
+                    }
+                }
+            }
+            store_grad_rows<DV, NTV, kScaleNone, PHI>(acc, dh * NTV, nullptr, tq,
+                                                      o + (row0 + (size_t)c * kChunk + tq) * DV, tq < valid, g);
+        };
+        switch (blk_w) {
+        case 0: chunk_rest(std::integral_constant<int, 0>{}); break;
+        case 1: chunk_rest(std::integral_constant<int, 1>{}); break;
+        case 2: chunk_rest(std::integral_constant<int, 2>{}); break;
+        default: chunk_rest(std::integral_constant<int, 3>{}); break;
+        }
+        {
+            const int lane = lane_in_loop(tid & 63);
             // S <- g_C S + Kh^T D (rows decayed to the chunk's end; rows past the
             // end have zero keys; z is not used)
             if (GATED) state8_scale<DK, DV>(st, gam(valid - 1));
