@@ -174,24 +174,25 @@ template <> struct StateIO<uint8_t> {
 // product-order page warns about in "What a summary can't do"): the update is
 // computed in fp32 from the stored values, rounded once to SS, and the read
 // uses the value as stored.
-// One workgroup of 256 threads per (b, h).  Thread -> (row group, 4-element
+// One workgroup of NT threads (NT >= Dk, Dv) per (b, h).  Thread -> (row group, 4-element
 // column unit): the DV/4 units of a row are covered by consecutive threads,
 // so every pass of the workgroup reads and writes whole rows (coalesced), and
 // all passes are issued before any is consumed.
-template <typename T, int DK, int DV, typename SS = float>
-__global__ __launch_bounds__(256) void decode_step_kernel(const T *__restrict__ q, const T *__restrict__ k,
+template <typename T, int DK, int DV, typename SS = float, int NT = 256>
+__global__ __launch_bounds__(NT) void decode_step_kernel(const T *__restrict__ q, const T *__restrict__ k,
                                                           const T *__restrict__ v, SS *__restrict__ s,
                                                           SS *__restrict__ z, const float *__restrict__ alpha,
                                                           T *__restrict__ o, int phi_mode, float eps) {
     using IO = StateIO<SS>;
     constexpr int C4 = DV / 4;                 // float4 columns per row
-    constexpr int RPP = 256 / C4;              // rows one pass of the workgroup covers
+    constexpr int RPP = NT / C4;               // rows one pass of the workgroup covers
     constexpr int ROWS = DK < RPP ? DK : RPP;  // rows per pass actually used
     constexpr int PASSES = DK / ROWS;
     constexpr int ACTIVE = ROWS * C4;          // threads holding state
     __shared__ float sq[DK], sk[DK], sv[DV];
     __shared__ __attribute__((aligned(16))) float red[ROWS][DV];
-    __shared__ float sden[4];
+    constexpr int NW = NT / 64;
+    __shared__ float sden[NW];
 
     const int bh = blockIdx.x;
     const int tid = threadIdx.x;
@@ -244,7 +245,9 @@ __global__ __launch_bounds__(256) void decode_step_kernel(const T *__restrict__ 
         float acc = 0.f;
 #pragma unroll 8
         for (int r = 0; r < ROWS; ++r) acc += red[r][tid];
-        const float den = sden[0] + sden[1] + sden[2] + sden[3];
+        float den = 0.f;
+#pragma unroll
+        for (int i = 0; i < NW; ++i) den += sden[i];
         store_elem<T>(o, (size_t)bh * DV + tid, acc / (den + eps));
     }
 }
