@@ -13,10 +13,12 @@
 //   O = Q S_0 + tril(Q Kh^T) D      (diagonal included)
 //   S_C = S_0 + Kh^T D.
 // The unit lower-triangular system is solved in 16-row blocks: the inverses of
-// the diagonal blocks by forward substitution in fp32, the rest as MFMA
+// the diagonal blocks by forward substitution in fp32 (one block per wave of
+// the light query blocks, as soon as the wave has formed it), the rest as MFMA
 // products on bf16 high/low parts; everything else is bf16 MFMA with fp32
 // accumulation, in the tile layouts and wave pairing of fwd8_bf16.hpp.  One
-// workgroup carries one (b, h) through its chunks in order.
+// workgroup carries one (b, h) through its chunks in order; four barriers per
+// chunk (staged, coupled, solved, carried).
 #pragma once
 
 #include "bwd8_bf16.hpp"
@@ -53,12 +55,15 @@ __device__ __forceinline__ f32x4 mfma16x16x16(s16x4 a, s16x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
-// a b + c from the bf16 high and low parts of both factors (three products;
-// the low parts' product is below the fp32 accumulation's resolution).
-__device__ __forceinline__ f32x4 mfma16_hl(s16x4 ahi, s16x4 alo, s16x4 bhi, s16x4 blo, f32x4 c) {
-    c = mfma16x16x16(ahi, bhi, c);
-    c = mfma16x16x16(alo, bhi, c);
-    return mfma16x16x16(ahi, blo, c);
+// Sum over the 16 lanes of a DPP row (lanes 16 r .. 16 r + 15), the same in
+// each of them: rotations by 8, 4, 2 and 1 within the row (every step adds two
+// values that the row's lanes pair symmetrically, so all lanes round alike).
+__device__ __forceinline__ float row16_sum(float x) {
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xf, 0xf, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x122, 0xf, 0xf, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x121, 0xf, 0xf, false));
+    return x;
 }
 
 // One value's high and low bf16 parts, as split_bf16x4 forms them.
@@ -159,8 +164,12 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8_bf16(
                     f[2 * e + 1] = phi_fast(bf_hi(kw[e]), PHI);
                     nrm = fmaf(f[2 * e], f[2 * e], fmaf(f[2 * e + 1], f[2 * e + 1], nrm));
                 }
+                if constexpr (CG == 16) {
+                    nrm = row16_sum(nrm);
+                } else {
 #pragma unroll
-                for (int m = 1; m < CG; m <<= 1) nrm += __shfl_xor(nrm, m, 64);
+                    for (int m = 1; m < CG; m <<= 1) nrm += __shfl_xor(nrm, m, 64);
+                }
                 // a zero key (or a row past the end) writes nothing
                 const float inv = (row < valid && nrm > 0.f) ? 1.f / sqrtf(nrm) : 0.f;
                 *reinterpret_cast<uint4 *>(sK + TK::off(row, col)) =
@@ -216,66 +225,94 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8_bf16(
                     make_float4(b * (bf_lo(vv.x) - r[0]), b * (bf_hi(vv.x) - r[1]), b * (bf_lo(vv.y) - r[2]),
                                 b * (bf_hi(vv.y) - r[3]));
             }
-            // Gram blocks (row block blk_w, column blocks dh, dh + 2 at or below it)
+            // coupling blocks: a block (rb, cb) = diag(beta) Kh_rb Kh_cb^T masked
+            // below the diagonal; rb = blk_w uses the keys already loaded
+            auto gram = [&](int rb, int cb, const bf16x8(&kr)[KSK]) {
+                const int tr = 16 * rb + l16;
+                f32x4 gr = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int cb2 = 0; cb2 < 2; ++cb2) {
-                const int cb = dh + 2 * cb2;
-                if (cb <= blk_w) {
-                    f32x4 gr = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int ks = 0; ks < KSK; ++ks)
+                    gr = mfma16x16x32(*reinterpret_cast<const bf16x8 *>(sK + TK::off(16 * cb + l16, 32 * ks + 8 * g)),
+                                      kr[ks], gr);
+                // gr[i] = Kh[16 cb + 4 g + i] . Kh[tr]: the coupling A[tr][j] for
+                // j = 16 cb + 4 g + i, strictly below the diagonal
+                const float b = sB[tr];
+                if (GATED) {
 #pragma unroll
-                    for (int ks = 0; ks < KSK; ++ks)
-                        gr = mfma16x16x32(
-                            *reinterpret_cast<const bf16x8 *>(sK + TK::off(16 * cb + l16, 32 * ks + 8 * g)), ka[ks],
-                            gr);
-                    // gr[i] = Kh[16 cb + 4 g + i] . Kh[tk]: the coupling A[tk][j] for
-                    // j = 16 cb + 4 g + i, strictly below the diagonal
-                    const float b = sB[tk];
-                    if (GATED) {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int j = 16 * cb + 4 * g + i;
-                            gr[i] *= j < tk ? dec(tk, j) : 0.f;
-                        }
+                    for (int i = 0; i < 4; ++i) {
+                        const int j = 16 * cb + 4 * g + i;
+                        gr[i] *= j < tr ? dec(tr, j) : 0.f;
                     }
-                    float4 a4;
-                    a4.x = 16 * cb + 4 * g + 0 < tk ? b * gr[0] : 0.f;
-                    a4.y = 16 * cb + 4 * g + 1 < tk ? b * gr[1] : 0.f;
-                    a4.z = 16 * cb + 4 * g + 2 < tk ? b * gr[2] : 0.f;
-                    a4.w = 16 * cb + 4 * g + 3 < tk ? b * gr[3] : 0.f;
-                    if (cb == blk_w) {
-                        *reinterpret_cast<float4 *>(sA + tk * AS + 16 * cb + 4 * g) = a4;
-                    } else {
-                        s16x4 hi, lo;
-                        split_bf16x4(-a4.x, -a4.y, -a4.z, -a4.w, hi, lo);
-                        const uint2 h2 = __builtin_bit_cast(uint2, hi), l2 = __builtin_bit_cast(uint2, lo);
-                        *reinterpret_cast<uint4 *>(sA + tk * AS + 16 * cb + 4 * g) = make_uint4(h2.x, h2.y, l2.x, l2.y);
-                    }
+                }
+                float4 a4;
+                a4.x = 16 * cb + 4 * g + 0 < tr ? b * gr[0] : 0.f;
+                a4.y = 16 * cb + 4 * g + 1 < tr ? b * gr[1] : 0.f;
+                a4.z = 16 * cb + 4 * g + 2 < tr ? b * gr[2] : 0.f;
+                a4.w = 16 * cb + 4 * g + 3 < tr ? b * gr[3] : 0.f;
+                if (cb == rb) {
+                    *reinterpret_cast<float4 *>(sA + tr * AS + 16 * cb + 4 * g) = a4;
                 } else {
-                    *reinterpret_cast<float4 *>(sA + tk * AS + 16 * cb + 4 * g) = make_float4(0.f, 0.f, 0.f, 0.f);
+                    s16x4 hi, lo;
+                    split_bf16x4(-a4.x, -a4.y, -a4.z, -a4.w, hi, lo);
+                    const uint2 h2 = __builtin_bit_cast(uint2, hi), l2 = __builtin_bit_cast(uint2, lo);
+                    *reinterpret_cast<uint4 *>(sA + tr * AS + 16 * cb + 4 * g) = make_uint4(h2.x, h2.y, l2.x, l2.y);
+                }
+            };
+            // waves 0..3 (the light query blocks) take diagonal block w and
+            // invert I + A_ww right away, in the wave (lane = column: forward
+            // substitution on a unit vector, all four lane groups alike; group
+            // g then writes rows 4 g .. 4 g + 3); the six blocks below the
+            // diagonal go to waves 2 and 4..7
+            if (w < 4) {
+                const int b = w;
+                bf16x8 kd[KSK];
+#pragma unroll
+                for (int ks = 0; ks < KSK; ++ks)
+                    kd[ks] = *reinterpret_cast<const bf16x8 *>(sK + TK::off(16 * b + l16, 32 * ks + 8 * g));
+                gram(b, b, kd);
+                // this wave wrote the whole block; its LDS accesses stay in order
+                const float *ab = sA + 16 * b * AS + 16 * b;
+                const int cc = l16;
+                float t[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    // four partial sums: a short dependency chain per row
+                    float x[4] = {r == cc ? 1.f : 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int j4 = 0; j4 < r; j4 += 4) {
+                        const float4 a = *reinterpret_cast<const float4 *>(ab + r * AS + j4);
+                        const float av[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (j4 + e < r) x[e] = fmaf(-av[e], t[j4 + e], x[e]);
+                    }
+                    t[r] = (x[0] + x[1]) + (x[2] + x[3]);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 4 * g + i;
+                    float tr = t[0];
+#pragma unroll
+                    for (int rr = 1; rr < 16; ++rr) tr = r == rr ? t[rr] : tr;
+                    split_bf16x1(tr, sTh[(16 * b + r) * 16 + cc], sTl[(16 * b + r) * 16 + cc]);
+                }
+                if (w == 2) gram(1, 0, ka); // blk_w = 1
+            } else {
+                // w = 4, 5: row block 3; w = 6, 7: row block 2
+                if (w == 4) {
+                    gram(3, 0, ka);
+                    gram(3, 1, ka);
+                } else if (w == 5) {
+                    gram(3, 2, ka);
+                } else {
+                    gram(2, w - 6, ka);
                 }
             }
         }
         __syncthreads();
 
-        // ---- wave 0 inverts the four 16 x 16 diagonal blocks of I + A (lane =
-        // block * 16 + column: forward substitution on a unit vector).  Meanwhile
-        // (wave 0: afterwards) each wave forms the parts of its outputs that do
-        // not depend on D: Q S_0 and the masked scores Kh . phi(q).
-        if (w == 0) {
-            const int lane = tid & 63;
-            const int b = lane >> 4, cc = lane & 15;
-            const float *ab = sA + 16 * b * AS + 16 * b;
-            float t[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float x = r == cc ? 1.f : 0.f;
-#pragma unroll
-                for (int j = 0; j < r; ++j) x = fmaf(-ab[r * AS + j], t[j], x);
-                t[r] = x;
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) split_bf16x1(t[r], sTh[(16 * b + r) * 16 + cc], sTl[(16 * b + r) * 16 + cc]);
-        }
+        // ---- each wave forms the parts of its outputs that do not depend on D
+        // (Q S_0 and the masked scores Kh . phi(q)), then solves
         auto chunk_rest = [&](auto blk_c) {
             constexpr int qblk = decltype(blk_c)::value;
             const int lane = lane_in_loop(tid & 63);
@@ -319,7 +356,6 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8_bf16(
                     }
                 }
             }
-            __syncthreads();
 
             // ---- solve (I + A) D = X: each wave takes 16 value columns through
             // the blocks in order, Y_b = X_b - sum_{k < b} A_bk D_k and
@@ -332,21 +368,28 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8_bf16(
                 s16x4 dh4[4], dl4[4];
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
-                    f32x4 y;
+                    // three independent accumulators (high x high, low x high,
+                    // high x low), so the products issue back to back
+                    f32x4 y, y1 = f32x4{0.f, 0.f, 0.f, 0.f}, y2 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int i = 0; i < 4; ++i) y[i] = sX[(16 * b + 4 * g + i) * XS + col];
 #pragma unroll
                     for (int kb = 0; kb < b; ++kb) {
                         const uint4 a = *reinterpret_cast<const uint4 *>(sA + (16 * b + l16) * AS + 16 * kb + 4 * g);
-                        y = mfma16_hl(__builtin_bit_cast(s16x4, make_uint2(a.x, a.y)),
-                                      __builtin_bit_cast(s16x4, make_uint2(a.z, a.w)), dh4[kb], dl4[kb], y);
+                        const s16x4 ah = __builtin_bit_cast(s16x4, make_uint2(a.x, a.y));
+                        const s16x4 al = __builtin_bit_cast(s16x4, make_uint2(a.z, a.w));
+                        y = mfma16x16x16(ah, dh4[kb], y);
+                        y1 = mfma16x16x16(al, dh4[kb], y1);
+                        y2 = mfma16x16x16(ah, dl4[kb], y2);
                     }
+                    if (b > 0) y += y1 + y2;
                     const uint2 th = *reinterpret_cast<const uint2 *>(sTh + (16 * b + l16) * 16 + 4 * g);
                     const uint2 tl = *reinterpret_cast<const uint2 *>(sTl + (16 * b + l16) * 16 + 4 * g);
                     s16x4 yh, yl;
                     split_bf16x4(y[0], y[1], y[2], y[3], yh, yl);
-                    dblk[b] = mfma16_hl(__builtin_bit_cast(s16x4, th), __builtin_bit_cast(s16x4, tl), yh, yl,
-                                        f32x4{0.f, 0.f, 0.f, 0.f});
+                    const s16x4 t_h = __builtin_bit_cast(s16x4, th), t_l = __builtin_bit_cast(s16x4, tl);
+                    const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
+                    dblk[b] = mfma16x16x16(t_h, yh, zero) + (mfma16x16x16(t_l, yh, zero) + mfma16x16x16(t_h, yl, zero));
                     split_bf16x4(dblk[b][0], dblk[b][1], dblk[b][2], dblk[b][3], dh4[b], dl4[b]);
                 }
                 // every read of this wave's right-hand side columns comes before

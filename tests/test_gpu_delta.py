@@ -54,6 +54,14 @@ def test_delta(shape):
     check(*make(*shape, seed=1200 + sum(shape)))
 
 
+def test_delta_full_length():
+    # the delta workload's length and head dims (64 chunks), two of its heads,
+    # its seed and unscaled inputs: the error of a long chunk chain
+    w = synth.WORKLOADS["delta_b16h16_n4096_d128"]
+    x = synth.Workload("t", 1, 2, w.N, w.Dk, w.Dv, BF, w.seed)
+    check(*synth.qkv(x))
+
+
 @pytest.mark.parametrize("shape", [(1, 2, 700, 128, 128), (2, 1, 130, 64, 64)])
 def test_delta_with_beta(shape):
     check(*make(*shape, seed=1220 + sum(shape), with_beta=True))
