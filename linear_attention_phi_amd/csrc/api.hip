@@ -231,12 +231,13 @@ int run_mfma_causal(const Plan &pl, const void *q, const void *k, const void *v,
     return launch(GATED ? "fwd_out_bf16_gated" : "fwd_out_bf16", st, [&] {
         if constexpr (kEight<DK, DV>)
             with_phi(phi, [&](auto PH) {
-                // the training forward (den given) is its own instantiation
-                if (den)
-                    fwd_out8_bf16<DK, DV, GATED, PH(), true><<<dim3(pl.P * BH), dim3(kThreads8), 0, st>>>(
-                        (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, alpha, (uint16_t *)o, start,
-                        sbh, sseg, start_z, zbh, s_final, z_final, N, pl.P, pl.seg_len, eps, den);
-                else
+                // the training forward (den given, never gated) is its own instantiation
+                if (den) {
+                    if constexpr (!GATED)
+                        fwd_out8_bf16<DK, DV, GATED, PH(), true><<<dim3(pl.P * BH), dim3(kThreads8), 0, st>>>(
+                            (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, alpha, (uint16_t *)o,
+                            start, sbh, sseg, start_z, zbh, s_final, z_final, N, pl.P, pl.seg_len, eps, den);
+                } else
                     fwd_out8_bf16<DK, DV, GATED, PH()><<<dim3(pl.P * BH), dim3(kThreads8), 0, st>>>(
                         (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, alpha, (uint16_t *)o, start,
                         sbh, sseg, start_z, zbh, s_final, z_final, N, pl.P, pl.seg_len, eps, nullptr);
