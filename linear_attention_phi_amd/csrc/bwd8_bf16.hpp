@@ -123,8 +123,12 @@ __device__ __forceinline__ void stage_dq(const BwdBuf<DK, DV, DD> &b, uint16_t *
         float x = 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) x += bf_lo(fw[e]) + bf_hi(fw[e]);
+        if constexpr (CG == 16) {
+            x = row16_sum(x);
+        } else {
 #pragma unroll
-        for (int m = 1; m < CG; m <<= 1) x += __shfl_xor(x, m, 64);
+            for (int m = 1; m < CG; m <<= 1) x += __shfl_xor(x, m, 64);
+        }
         if (col == 0) sSq[row] = x;
         *reinterpret_cast<uint4 *>(sK + Tile<DK>::off(row, col)) = phi_pack8(b.k.r[i], KF);
     }

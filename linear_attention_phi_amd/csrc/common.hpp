@@ -103,6 +103,17 @@ __device__ __forceinline__ uint4 buffer_load16(rsrc_t rs, int voff) {
 __device__ __forceinline__ float xor_shfl(float v, int mask) {
     return __shfl_xor(v, mask, 64);
 }
+// Sum over the 16 lanes of a DPP row (lanes 16 r .. 16 r + 15), the same in
+// each of them: rotations by 8, 4, 2 and 1 within the row (every step adds two
+// values that the row's lanes pair symmetrically, so all lanes round alike).
+__device__ __forceinline__ float row16_sum(float x) {
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xf, 0xf, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x122, 0xf, 0xf, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x121, 0xf, 0xf, false));
+    return x;
+}
+
 // Sum over the four 16-lane groups (lanes l, l^16, l^32, l^48).
 __device__ __forceinline__ float sum_over_groups(float v) {
     v += xor_shfl(v, 16);
@@ -125,18 +136,27 @@ __device__ __forceinline__ float decay_between(float to_lsum, int to_zeros, floa
 __device__ __forceinline__ bool gate_is_zero(float a) { return a < 1.17549435e-38f; }  // NaN stays NaN
 __device__ __forceinline__ float gate_log2(float a) { return gate_is_zero(a) ? 0.f : __builtin_amdgcn_logf(a); }
 
-// Inclusive scan over the 64 lanes of a wave (lane order = token order).
+// Inclusive scan over the 64 lanes of a wave (lane order = token order), on
+// DPP: shifts by 1, 2, 4 and 8 within each 16-lane row (lanes shifted in from
+// outside the row add 0), then the last lane of row 0 added to row 1 and of
+// row 2 to row 3 (row_bcast:15), then lane 31 added to rows 2 and 3
+// (row_bcast:31).  Rows not selected by a step's row mask add 0.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_or_zero(int x) {
+    return __builtin_amdgcn_update_dpp(0, x, CTRL, ROWS, 0xf, false);
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ void scan_step(float &lsum, int &zeros) {
+    lsum += __builtin_bit_cast(float, dpp_or_zero<CTRL, ROWS>(__builtin_bit_cast(int, lsum)));
+    zeros += dpp_or_zero<CTRL, ROWS>(zeros);
+}
 __device__ __forceinline__ void wave_inclusive_scan(float &lsum, int &zeros) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        float ls = __shfl_up(lsum, d, 64);
-        int zs = __shfl_up(zeros, d, 64);
-        if (lane >= d) {
-            lsum += ls;
-            zeros += zs;
-        }
-    }
+    scan_step<0x111, 0xf>(lsum, zeros); // row_shr:1
+    scan_step<0x112, 0xf>(lsum, zeros); // row_shr:2
+    scan_step<0x114, 0xf>(lsum, zeros); // row_shr:4
+    scan_step<0x118, 0xf>(lsum, zeros); // row_shr:8
+    scan_step<0x142, 0xa>(lsum, zeros); // row_bcast:15 into rows 1, 3
+    scan_step<0x143, 0xc>(lsum, zeros); // row_bcast:31 into rows 2, 3
 }
 
 } // namespace linattn

@@ -55,17 +55,6 @@ __device__ __forceinline__ f32x4 mfma16x16x16(s16x4 a, s16x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
-// Sum over the 16 lanes of a DPP row (lanes 16 r .. 16 r + 15), the same in
-// each of them: rotations by 8, 4, 2 and 1 within the row (every step adds two
-// values that the row's lanes pair symmetrically, so all lanes round alike).
-__device__ __forceinline__ float row16_sum(float x) {
-    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
-    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xf, 0xf, false));
-    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x122, 0xf, 0xf, false));
-    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x121, 0xf, 0xf, false));
-    return x;
-}
-
 // One value's high and low bf16 parts, as split_bf16x4 forms them.
 __device__ __forceinline__ void split_bf16x1(float x, uint16_t &hi, uint16_t &lo) {
     const uint32_t h = f32_to_bf16_bits(x);
