@@ -357,8 +357,7 @@ __global__ __launch_bounds__(kThreads8, 1) void bwd_dq8_bf16(
                     for (int e = 0; e < 8; ++e) vdy = fmaf((float)dya[ks][e], vb[e], vdy);
                 }
             }
-            vdy += __shfl_xor(vdy, 16, 64);
-            vdy += __shfl_xor(vdy, 32, 64);
+            vdy = sum_over_groups(vdy);
 
             // A = E_t dY_t and zeta_t over this wave's key dims (tiles permuted as perm_dv)
             f32x4 acc[NTK], zt[NTK];
@@ -421,10 +420,8 @@ __global__ __launch_bounds__(kThreads8, 1) void bwd_dq8_bf16(
                     pz = fmaf(fq[j][i], zt[j][i], pz);
                 }
             }
-            pa += __shfl_xor(pa, 16, 64);
-            pa += __shfl_xor(pa, 32, 64);
-            pz += __shfl_xor(pz, 16, 64);
-            pz += __shfl_xor(pz, 32, 64);
+            pa = sum_over_groups(pa);
+            pz = sum_over_groups(pz);
             if (g == 0) {
                 sRed[(dh * 2 + 0) * kChunk + tq] = pa;
                 sRed[(dh * 2 + 1) * kChunk + tq] = pz;

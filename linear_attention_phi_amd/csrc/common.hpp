@@ -115,10 +115,17 @@ __device__ __forceinline__ float row16_sum(float x) {
 }
 
 // Sum over the four 16-lane groups (lanes l, l^16, l^32, l^48).
+// On the gfx950 row swaps (VALU, no LDS round trip): with both operands v,
+// v_permlane16_swap returns rows (0, 0, 2, 2) and (1, 1, 3, 3) of v, and
+// v_permlane32_swap its lower and upper halves each twice, so the two adds
+// are (v0 + v1) + (v2 + v3) in every lane, in the same order everywhere.
 __device__ __forceinline__ float sum_over_groups(float v) {
-    v += xor_shfl(v, 16);
-    v += xor_shfl(v, 32);
-    return v;
+    const unsigned u = __builtin_bit_cast(unsigned, v);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    v = __builtin_bit_cast(float, (unsigned)a[0]) + __builtin_bit_cast(float, (unsigned)a[1]);
+    const unsigned w = __builtin_bit_cast(unsigned, v);
+    const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    return __builtin_bit_cast(float, (unsigned)b[0]) + __builtin_bit_cast(float, (unsigned)b[1]);
 }
 
 // ---------------------------------------------------------------- gating
