@@ -283,10 +283,15 @@ __device__ __forceinline__ void add_bf16x8(float (&vsum)[8], uint4 u) {
 template <int D>
 __device__ __forceinline__ void colsum_to_lds(float (&vsum)[8], float *red, int w, int lane) {
     constexpr int CG = D / 8;
+    if constexpr (CG == 16) {
 #pragma unroll
-    for (int m = CG; m < 64; m <<= 1) {
+        for (int e = 0; e < 8; ++e) vsum[e] = sum_over_groups(vsum[e]);
+    } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) vsum[e] += __shfl_xor(vsum[e], m, 64);
+        for (int m = CG; m < 64; m <<= 1) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vsum[e] += __shfl_xor(vsum[e], m, 64);
+        }
     }
     if (lane < CG) {
         float4 *r = reinterpret_cast<float4 *>(red + w * D + 8 * lane);
