@@ -1,9 +1,11 @@
 """GPU parity on the five measured workloads at full size, in the launch
-configuration the benchmark times.
+configuration the benchmark times, and on the backward as the benchmark times
+it (over the 131072-token workload).
 
 Where the oracle is too slow for every output (the 131072-token workload), it
-checks whole heads (every output row of the first and last head) and the final
-state of every head; elsewhere every output is checked.
+checks whole heads (every output row of the first and last head, and their
+gradients) and the final state of every head; elsewhere every output is
+checked.
 """
 import time
 
@@ -67,6 +69,29 @@ def test_long_n131072_d128_sampled():
     ro, rsh, _ = oracle.forward(q[:, hs], k[:, hs], v[:, hs])
     assert_close(f"O heads {hs}", o[:, hs], ro, TOL[w.dtype])
     assert_close(f"S heads {hs}", s[:, hs], rsh, TOL[w.dtype], per="head")
+
+
+def test_backward_on_the_long_workload_sampled():
+    # the backward as the benchmark times it (all 16 heads of the 131072-token
+    # workload in one call, dO seeded N(0, 1)); the gradients of the first and
+    # last head against the oracle's adjoint recurrence
+    w = synth.WORKLOADS["long_n131072_d128"]
+    stamp("generating inputs")
+    q, k, v = synth.qkv(w)
+    g = synth.dout(w)
+    stamp("GPU training forward and backward")
+    d = [x.to(DEV) for x in (q, k, v, g)]
+    _, den, _, _ = la.linattn_forward_train(d[0], d[1], d[2])
+    dq, dk, dv = la.linattn_backward(d[0], d[1], d[2], den, d[3])
+    torch.cuda.synchronize()
+    hs = [0, w.H - 1]
+    got = [x[:, hs].cpu() for x in (dq, dk, dv)]
+    del d, den, dq, dk, dv
+    stamp(f"oracle: gradients of heads {hs}")
+    rq, rk, rv, _, _ = oracle.backward(q[:, hs], k[:, hs], v[:, hs], g[:, hs])
+    for name, x, r in zip(("dq", "dk", "dv"), got, (rq, rk, rv)):
+        assert torch.isfinite(x.float()).all()
+        assert_close(f"{name} heads {hs}", x, r, TOL[w.dtype], per="head")
 
 
 def test_gated_b2h16_n16384_d128():
