@@ -94,6 +94,30 @@ def test_backward_on_the_long_workload_sampled():
         assert_close(f"{name} heads {hs}", x, r, TOL[w.dtype], per="head")
 
 
+def test_snapshots_on_the_long_workload_sampled():
+    # the snapshot forward as the benchmark times it: 8 prefix-cache points at
+    # 16384 m - 1 and the last 8 tokens of the 131072-token workload; the states
+    # of the first and last head at every position against the prefix sum
+    w = synth.WORKLOADS["long_n131072_d128"]
+    stamp("generating inputs")
+    q, k, v = synth.qkv(w)
+    pos = sorted({16384 * m - 1 for m in range(1, 9) if 16384 * m - 1 < w.N} | {w.N - 1 - i for i in range(8)})
+    stamp("GPU forward with snapshots")
+    d = [x.to(DEV) for x in (q, k, v)]
+    o, ss, zs, sf, zf = la.linattn_forward_snapshots(*d, pos)
+    o2, _, _ = la.linattn_forward(*d)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2)
+    hs = [0, w.H - 1]
+    ss, zs = ss[:, hs].cpu(), zs[:, hs].cpu()
+    del d, o, o2
+    stamp(f"oracle: heads {hs} at {len(pos)} positions")
+    for i, p in enumerate(pos):
+        rs, rz = oracle.state_from_prefix(k[0, hs, :p + 1], v[0, hs, :p + 1])
+        assert_close(f"S after token {p}", ss[:, :, i], rs[None], TOL[w.dtype], per="head")
+        assert_close(f"z after token {p}", zs[:, :, i], rz[None], TOL[w.dtype], per="head")
+
+
 def test_gated_b2h16_n16384_d128():
     w = synth.WORKLOADS["gated_b2h16_n16384_d128"]
     q, k, v = synth.qkv(w)
