@@ -73,15 +73,11 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast
 // column sums.
 __device__ __forceinline__ bf16x8 bf16_ones8() { return as_bf16x8(make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u)); }
 
-// Streaming (non-temporal) 16-byte global load and store: every input row is
-// read once and every output row written once, so neither should displace
-// cache lines that are reused.
+// Streaming (non-temporal) 16-byte global load: every input row is read once,
+// so it should not displace cache lines that are reused.
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 load_stream16(const void *p) {
     return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p)));
-}
-__device__ __forceinline__ void store_stream16(void *p, uint4 v) {
-    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4 *>(p));
 }
 __device__ __forceinline__ uint4 as_u4(bf16x8 v) { return __builtin_bit_cast(uint4, v); }
 
@@ -100,9 +96,6 @@ __device__ __forceinline__ uint4 buffer_load16(rsrc_t rs, int voff) {
 }
 
 // ---------------------------------------------------------------- cross-lane
-__device__ __forceinline__ float xor_shfl(float v, int mask) {
-    return __shfl_xor(v, mask, 64);
-}
 // Sum over the 16 lanes of a DPP row (lanes 16 r .. 16 r + 15), the same in
 // each of them: rotations by 8, 4, 2 and 1 within the row (every step adds two
 // values that the row's lanes pair symmetrically, so all lanes round alike).
