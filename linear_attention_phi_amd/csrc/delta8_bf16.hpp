@@ -251,7 +251,7 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8_bf16(
             // invert I + A_ww right away, in the wave (lane = column: forward
             // substitution on a unit vector, all four lane groups alike; group
             // g then writes rows 4 g .. 4 g + 3); the six blocks below the
-            // diagonal go to waves 2 and 4..7
+            // diagonal go to waves 4..7
             if (w < 4) {
                 const int b = w;
                 bf16x8 kd[KSK];
@@ -285,9 +285,9 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8_bf16(
                     for (int rr = 1; rr < 16; ++rr) tr = r == rr ? t[rr] : tr;
                     split_bf16x1(tr, sTh[(16 * b + r) * 16 + cc], sTl[(16 * b + r) * 16 + cc]);
                 }
-                if (w == 2) gram(1, 0, ka); // blk_w = 1
             } else {
-                // w = 4, 5: row block 3; w = 6, 7: row block 2
+                // w = 4, 5: row block 3; w = 6, 7: row block 2 (and w = 7 also
+                // block (1, 0), with row block 1's keys)
                 if (w == 4) {
                     gram(3, 0, ka);
                     gram(3, 1, ka);
@@ -295,13 +295,21 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8_bf16(
                     gram(3, 2, ka);
                 } else {
                     gram(2, w - 6, ka);
+                    if (w == 7) {
+                        bf16x8 k1[KSK];
+#pragma unroll
+                        for (int ks = 0; ks < KSK; ++ks)
+                            k1[ks] = *reinterpret_cast<const bf16x8 *>(sK + TK::off(16 + l16, 32 * ks + 8 * g));
+                        gram(1, 0, k1);
+                    }
                 }
             }
         }
-        __syncthreads();
 
         // ---- each wave forms the parts of its outputs that do not depend on D
-        // (Q S_0 and the masked scores Kh . phi(q)), then solves
+        // (Q S_0 and the masked scores Kh . phi(q); the tiles they read were
+        // staged before the last barrier) while the coupling is completed, then
+        // solves
         auto chunk_rest = [&](auto blk_c) {
             constexpr int qblk = decltype(blk_c)::value;
             const int lane = lane_in_loop(tid & 63);
@@ -345,6 +353,7 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8_bf16(
                     }
                 }
             }
+            __syncthreads();
 
             // ---- solve (I + A) D = X: each wave takes 16 value columns through
             // the blocks in order, Y_b = X_b - sum_{k < b} A_bk D_k and
