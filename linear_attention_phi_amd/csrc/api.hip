@@ -36,7 +36,7 @@ struct Plan {
     int P = 1;        // output segments per (b, h)
     int seg_len = 0;  // tokens per output segment
     int R = 1;        // state sub-segments per output segment
-    int Ps = 1;       // state cells per (b, h) = P * R
+    int Ps = 1;       // state cells per (b, h): P * R (+ 1 for the forward kinds)
     int sub_len = 0;  // tokens per state sub-segment
     int nvb = 1;      // 64-column value blocks (recurrence path)
     size_t E = 0;     // floats of one state (Dk * Dv + Dk)
@@ -71,6 +71,9 @@ Plan make_plan(int kind, int B, int H, int N, int Dk, int Dv, int dtype) {
             }
     }
     p.Ps = p.P * p.R;
+    // the forward kinds keep one more cell per (b, h): the state at the end of
+    // the sequence, which snapshots near the end are taken back from
+    if ((kind == LINATTN_KIND_FORWARD || kind == LINATTN_KIND_GATED) && p.P > 1) p.Ps += 1;
     p.sub_len = p.seg_len / p.R;
     p.E = (size_t)Dk * Dv + Dk;
     p.Eb = p.E + Dv;
@@ -181,9 +184,9 @@ int run_mfma_causal(const Plan &pl, const void *q, const void *k, const void *v,
         float *states = reinterpret_cast<float *>(ws);
         float *gam = GATED ? reinterpret_cast<float *>(ws + pl.ws_states) : nullptr;
         // the sub-segments of the last output segment are never needed by
-        // the output pass; snapshots use all but the very last, so that no
-        // snapshot runs over more than one sub-segment
-        const int P_run = snap ? pl.P * pl.R - 1 : (pl.P - 1) * pl.R;
+        // the output pass; snapshots use them all, so that every snapshot lies
+        // between two cells, the last one being the state at the end
+        const int P_run = snap ? pl.P * pl.R : (pl.P - 1) * pl.R;
         LA_TRY(launch("seg_state_bf16", st, [&] {
             if constexpr (kEight<DK, DV>)
                 with_phi(phi, [&](auto PH) {

@@ -436,10 +436,14 @@ struct SnapList {
 // State snapshots: (S, z) after token p for each listed p, written to
 // s_snap [BH][n][Dk][Dv] and z_snap [BH][n][Dk].  Each workgroup starts from
 // the last prefix cell at or before token p + 1 (cells of cell_len tokens,
-// the last one usable is max_cell; null cells: the initial state or zero at
-// token 0) and carries the state over the tokens from there through p, the
-// forward's own algebra (gated: the decays of those tokens apply to the
-// cell's state).  A snapshot just before a cell edge is a copy of the cell.
+// the last one usable is max_cell, which may be the end of the sequence;
+// null cells: the initial state or zero at token 0) and carries the state
+// over the tokens from there through p, the forward's own algebra (gated: the
+// decays of those tokens apply to the cell's state).  Without gates, when the
+// next cell is nearer, it takes that cell's state less the sums of the tokens
+// after p instead (the sums are additive; negating the cell, adding the
+// tokens and negating again is exact up to the additions' rounding).  A
+// snapshot just before a cell edge is a copy of the cell.
 template <int DK, int DV, bool GATED, int PHI>
 __global__ __launch_bounds__(kThreads8, 4) void snap_state8_bf16(
     const uint16_t *__restrict__ k, const uint16_t *__restrict__ v, const float *__restrict__ alpha,
@@ -452,8 +456,19 @@ __global__ __launch_bounds__(kThreads8, 4) void snap_state8_bf16(
     const int i = blockIdx.x % snaps.n, bh = blockIdx.x / snaps.n;
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
     const int p = snaps.pos[i];
-    const int cell = cells ? min((p + 1) / cell_len, max_cell) : 0;
-    const int t_begin = cell * cell_len;
+    int cell = cells ? min((p + 1) / cell_len, max_cell) : 0;
+    int t_begin = cell * cell_len, t_end = p + 1;
+    // the next cell and its token, when it is nearer (ungated only)
+    bool back = false;
+    if (!GATED && cells && cell + 1 <= max_cell) {
+        const int hi_tok = min((cell + 1) * cell_len, N);
+        if (hi_tok - (p + 1) < (p + 1) - t_begin) {
+            back = true;
+            cell += 1;
+            t_begin = p + 1;
+            t_end = hi_tok;
+        }
+    }
 
     State8<DK, DV> st;
     if (cells) {
@@ -463,11 +478,13 @@ __global__ __launch_bounds__(kThreads8, 4) void snap_state8_bf16(
         state8_load<DK, DV>(st, s_init ? s_init + (size_t)bh * DK * DV : nullptr,
                             z_init ? z_init + (size_t)bh * DK : nullptr, w, lane);
     }
+    if (back) state8_scale<DK, DV>(st, -1.f);
     float seg_lsum = 0.f;
     int seg_zeros = 0;
     float vsum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    range_state8<DK, DV, GATED, PHI, false>(k, v, alpha, bh, N, t_begin, p + 1, st, sK, sV, vsum, seg_lsum,
+    range_state8<DK, DV, GATED, PHI, false>(k, v, alpha, bh, N, t_begin, t_end, st, sK, sV, vsum, seg_lsum,
                                             seg_zeros);
+    if (back) state8_scale<DK, DV>(st, -1.f);
     const size_t o = (size_t)bh * snaps.n + i;
     state8_store<DK, DV>(st, s_snap + o * DK * DV, w, lane);
     state8_store_z<DK, DV>(st, z_snap + o * DK, w, lane);
