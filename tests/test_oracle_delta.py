@@ -11,7 +11,11 @@ oracle.delta is checked against things other than itself:
 - with beta = 1 every write is an exact overwrite: reading right after with
   the same unit key returns the value; with beta in (0, 1) it returns
   (1 - beta) times the old read plus beta times the value;
-- the key enters only through its direction (scaling it changes nothing).
+- the key enters only through its direction (scaling it changes nothing);
+- the feature map comes before the unit length: on inputs of one sign elu + 1
+  is x + 1 or exp(x), so the elu + 1 run equals the identity-map run fed those
+  values, and one token from a zero summary gives o = (kh . phi(q)) v with phi
+  evaluated branch by branch.
 """
 import json
 import os
@@ -140,3 +144,49 @@ def test_gated_orthogonal_unit_keys_are_the_decayed_sum():
     _, s = oracle.delta(k, k, v, alpha=a, phi_mode=ID)
     ref = sum(np.prod(a[0, 0, j + 1:]) * np.outer(k[0, 0, j], v[0, 0, j]) for j in range(D))
     np.testing.assert_allclose(s[0, 0], ref, rtol=1e-12, atol=1e-12)
+
+
+# ---- the feature map inside the delta rule: phi first, then the unit length
+# (product-order page, "The summary runs out of room": the key the summary is
+# read and written with is the feature-mapped key; it has unit length, which is
+# what makes the re-read return the value).  elu + 1 is x + 1 on x >= 0 and
+# exp(x) on x < 0, so on inputs of one sign the elu + 1 run must equal the
+# identity-map run fed those values directly; applying phi after the
+# normalization (or to the query differently) breaks it.
+
+def test_elu_mode_on_nonnegative_inputs_is_the_identity_run_on_x_plus_one():
+    r = np.random.default_rng(42)
+    q, k, v = (np.abs(x) for x in rand(2, 2, 30, 6, 4, seed=43))
+    v = v * r.choice([-1.0, 1.0], v.shape)  # values keep both signs (phi never touches them)
+    beta = r.uniform(0.2, 1.0, (2, 2, 30))
+    a = r.uniform(0.6, 1.0, (2, 2, 30))
+    s0 = r.standard_normal((2, 2, 6, 4))
+    o1, s1 = oracle.delta(q, k, v, beta=beta, s_init=s0, alpha=a)
+    o2, s2 = oracle.delta(q + 1.0, k + 1.0, v, beta=beta, s_init=s0, alpha=a, phi_mode=ID)
+    np.testing.assert_allclose(o1, o2, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(s1, s2, rtol=1e-12, atol=1e-12)
+
+
+def test_elu_mode_on_negative_inputs_is_the_identity_run_on_exp():
+    r = np.random.default_rng(44)
+    q, k, v = rand(1, 3, 25, 5, 3, seed=45)
+    q, k = -np.abs(q) - 1e-3, -np.abs(k) - 1e-3
+    beta = r.uniform(0.2, 1.0, (1, 3, 25))
+    o1, s1 = oracle.delta(q, k, v, beta=beta)
+    o2, s2 = oracle.delta(np.exp(q), np.exp(k), v, beta=beta, phi_mode=ID)
+    np.testing.assert_allclose(o1, o2, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(s1, s2, rtol=1e-12, atol=1e-12)
+
+
+def test_elu_mode_one_token_closed_form():
+    # from a zero summary one full write leaves kh v^T, so o = (kh . phi(q)) v with
+    # kh = phi(k) / |phi(k)|; phi here is evaluated branch by branch by hand
+    k = arr([[[[0.5, -1.0, 2.0, -0.25]]]])
+    q = arr([[[[-0.5, 0.0, 1.5, -2.0]]]])
+    v = arr([[[[3.0, -1.0]]]])
+    fk = np.array([1.5, np.exp(-1.0), 3.0, np.exp(-0.25)])
+    fq = np.array([np.exp(-0.5), 1.0, 2.5, np.exp(-2.0)])
+    kh = fk / np.sqrt((fk ** 2).sum())
+    o, s = oracle.delta(q, k, v)
+    np.testing.assert_allclose(s[0, 0], np.outer(kh, v[0, 0, 0]), rtol=1e-14)
+    np.testing.assert_allclose(o[0, 0, 0], (kh @ fq) * v[0, 0, 0], rtol=1e-14)

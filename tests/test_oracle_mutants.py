@@ -44,6 +44,11 @@ DELTA_MUTANTS = {
     "delta_beta_ignored": ("const double b = beta ? beta[t] : 1.0;", "const double b = 1.0;"),
     "delta_gate_ignored": ("s[e] *= alpha[t];", "s[e] *= 1.0;"),
     "delta_read_with_query": ("acc += s[(int64_t)i * Dv + j] * kh[i];", "acc += s[(int64_t)i * Dv + j] * phi(q[t * Dk + i], mode);"),
+    # normalize the raw key first, then apply the feature map
+    "delta_normalize_then_phi": ("kh[i] = phi(kt[i], mode);\n            nrm += kh[i] * kh[i];\n        }\n        nrm = sqrt(nrm);\n"
+                                 "        for (int i = 0; i < Dk; ++i)\n            kh[i] = nrm > 0.0 ? kh[i] / nrm : 0.0;",
+                                 "kh[i] = kt[i];\n            nrm += kh[i] * kh[i];\n        }\n        nrm = sqrt(nrm);\n"
+                                 "        for (int i = 0; i < Dk; ++i)\n            kh[i] = phi(nrm > 0.0 ? kh[i] / nrm : 0.0, mode);"),
 }
 LOWP_MUTANTS = {
     "lowp_truncates": ("return nearbyint(x / q) * q;", "return trunc(x / q) * q;"),
