@@ -23,7 +23,10 @@
  * ---------------------------------------
  * - Pointers to tensors are DEVICE pointers (hipMalloc'd or torch CUDA
  *   memory), contiguous, row-major, owned by the caller.  The library
- *   allocates and frees nothing and keeps no state between calls.
+ *   allocates and frees nothing.  Results depend only on the arguments: the
+ *   library's only state across calls is the optional timing record of
+ *   linattn_profile_enable / linattn_profile_read (see there; not
+ *   thread-safe).
  * - Shapes follow the pages' [batch, heads, tokens, head_dim] layout:
  *   q, k [B][H][N][Dk], v [B][H][N][Dv], o [B][H][N][Dv]; the state
  *   S [B][H][Dk][Dv] (row = key component, column = value component) and
@@ -55,7 +58,7 @@
 extern "C" {
 #endif
 
-#define LINATTN_ABI_VERSION 2
+#define LINATTN_ABI_VERSION 3
 #define LINATTN_MAX_SNAPSHOTS 256
 
 enum linattn_dtype { LINATTN_F32 = 0, LINATTN_BF16 = 1, LINATTN_FP8_E4M3 = 2 /* state storage only */ };
@@ -119,6 +122,37 @@ int linattn_forward_gated(const void *q, const void *k, const void *v,
                           int B, int H, int N, int Dk, int Dv, int dtype,
                           int phi, float eps, void *workspace,
                           size_t workspace_bytes, void *hip_stream);
+
+/*
+ * Causal forward (gated when alpha is non-NULL) with the split of each
+ * sequence chosen by the caller.  The result is the same quantity as
+ * linattn_forward(_gated): the sum of outer products does not depend on how
+ * the tokens are grouped ("Linear Attention: accumulating KV into a
+ * fixed-size state", section "Adding to the same state in turn"), so any split
+ * gives the same outputs up to the order of the fp32 additions.
+ *
+ *   segments     >= 1: each sequence is cut into output segments of
+ *                ceil(chunks / segments) chunks of 64 tokens (so at most
+ *                `segments` of them), processed in parallel from the prefix
+ *                of the earlier segments' states (1 = one sequential pass).
+ *   subsegments  >= 1: each output segment's state is summed over this many
+ *                parts (the largest divisor of its chunk count not above
+ *                the request); only the bf16 matrix-core path uses it.
+ *   workspace    at least linattn_workspace_size_planned(kind, ...,
+ *                segments, subsegments) bytes, kind LINATTN_KIND_GATED when
+ *                alpha is given, else LINATTN_KIND_FORWARD.
+ * Other arguments as linattn_forward(_gated); LINATTN_EINVAL when segments
+ * or subsegments is below 1.  linattn_forward uses a split chosen to fill the
+ * GPU.
+ */
+int linattn_forward_planned(const void *q, const void *k, const void *v,
+                            const float *alpha, void *o,
+                            const float *s_init, const float *z_init,
+                            float *s_final, float *z_final,
+                            int B, int H, int N, int Dk, int Dv, int dtype,
+                            int phi, float eps, int segments, int subsegments,
+                            void *workspace, size_t workspace_bytes,
+                            void *hip_stream);
 
 /*
  * Causal forward for training: linattn_forward that also keeps, for the
@@ -290,6 +324,11 @@ int linattn_decode_step_lowp(const void *q, const void *k, const void *v,
  * call needs none).  Pure host arithmetic; returns 0 for invalid arguments.
  */
 size_t linattn_workspace_size(int kind, int B, int H, int N, int Dk, int Dv, int dtype);
+
+/* Workspace bytes of linattn_forward_planned (kind LINATTN_KIND_FORWARD or
+ * LINATTN_KIND_GATED) for the requested split; 0 for invalid arguments. */
+size_t linattn_workspace_size_planned(int kind, int B, int H, int N, int Dk, int Dv, int dtype,
+                                      int segments, int subsegments);
 
 /* Static string naming a status code. */
 const char *linattn_status_string(int status);

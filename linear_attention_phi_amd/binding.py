@@ -4,6 +4,12 @@ Argument marshalling only: shapes and dtypes are checked, device pointers and
 the current HIP stream are handed to the C ABI, and every step of the method
 runs in the HIP library.  There is no fallback: if ``liblinattn.so`` is
 missing, or a call returns an error status, a RuntimeError is raised.
+
+The C ABI receives bare pointers and cannot see a tensor's size, so every
+tensor a caller passes (inputs, initial states and preallocated outputs alike)
+is checked here against the shape the call implies, before anything is
+launched: first the shapes and dtypes of all of them (ValueError / TypeError),
+then that each is a contiguous tensor on the GPU.
 """
 from __future__ import annotations
 
@@ -32,6 +38,7 @@ _SZ = ctypes.c_size_t
 SIGNATURES = {
     "linattn_forward": ([_P] * 8 + [_I] * 7 + [_F, _P, _SZ, _P], _I),
     "linattn_forward_gated": ([_P] * 9 + [_I] * 7 + [_F, _P, _SZ, _P], _I),
+    "linattn_forward_planned": ([_P] * 9 + [_I] * 7 + [_F, _I, _I, _P, _SZ, _P], _I),
     "linattn_forward_train": ([_P] * 9 + [_I] * 7 + [_F, _P, _SZ, _P], _I),
     "linattn_backward": ([_P] * 10 + [_I] * 7 + [_F, _P, _SZ, _P], _I),
     "linattn_decode_step_lowp": ([_P] * 5 + [_I] + [_P] * 2 + [_I] * 6 + [_F, _P], _I),
@@ -40,6 +47,7 @@ SIGNATURES = {
     "linattn_forward_noncausal": ([_P] * 6 + [_I] * 7 + [_F, _P, _SZ, _P], _I),
     "linattn_decode_step": ([_P] * 7 + [_I] * 6 + [_F, _P], _I),
     "linattn_workspace_size": ([_I] * 7, _SZ),
+    "linattn_workspace_size_planned": ([_I] * 9, _SZ),
     "linattn_status_string": ([_I], ctypes.c_char_p),
     "linattn_abi_version": ([], _I),
     "linattn_profile_enable": ([_I], _I),
@@ -79,16 +87,43 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
 
 
-def _dev(t, name, dtype=None):
-    if t is None:
-        return None
-    if not isinstance(t, torch.Tensor) or not t.is_cuda:
-        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
-    if dtype is not None and t.dtype != dtype:
-        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-    return t
+def _dims(t, name, ndim):
+    """The shape of the tensor that fixes a call's sizes (q), checked for rank only."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    return tuple(t.shape)
+
+
+def _validate(specs):
+    """specs: (tensor or None, name, expected shape, expected dtype or None).
+
+    Shapes and dtypes of every given tensor first, then device and layout, so
+    that a wrong size is reported whatever device the tensors are on and
+    nothing reaches the GPU before all of it has passed.
+    """
+    for t, name, shape, dtype in specs:
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a tensor")
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+        if dtype is not None and t.dtype != dtype:
+            raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    for t, name, _, _ in specs:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+
+def _pair(a, b, what):
+    if (a is None) != (b is None):
+        raise ValueError(f"pass both {what} or neither")
 
 
 def _ptr(t):
@@ -103,63 +138,90 @@ def workspace_size(kind, B, H, N, Dk, Dv, dtype_code) -> int:
     return int(lib().linattn_workspace_size(kind, B, H, N, Dk, Dv, dtype_code))
 
 
-def _workspace(kind, B, H, N, Dk, Dv, code, device, workspace):
-    need = workspace_size(kind, B, H, N, Dk, Dv, code)
+def workspace_size_planned(kind, B, H, N, Dk, Dv, dtype_code, segments, subsegments) -> int:
+    return int(lib().linattn_workspace_size_planned(kind, B, H, N, Dk, Dv, dtype_code, segments, subsegments))
+
+
+def _workspace(need, device, workspace):
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
-    return workspace, need
+        return torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    _validate([(workspace, "workspace", tuple(workspace.shape), None)])
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} bytes, needs {need}")
+    return workspace
+
+
+def _ws_bytes(ws):
+    return ws.numel() * ws.element_size()
+
+
+def _qkv_specs(q, k, v):
+    """Sizes fixed by q and v, and the specs of q, k, v themselves."""
+    B, H, N, Dk = _dims(q, "q", 4)
+    Dv = _dims(v, "v", 4)[3]
+    code = _dtype_code(q)
+    return (B, H, N, Dk, Dv, code), [(q, "q", (B, H, N, Dk), None), (k, "k", (B, H, N, Dk), q.dtype),
+                                     (v, "v", (B, H, N, Dv), q.dtype)]
 
 
 def linattn_forward(q, k, v, s_init=None, z_init=None, *, eps=1e-6, phi=PHI_ELU1, want_state=True,
                     out=None, s_final=None, z_final=None, workspace=None):
     """Causal forward.  q, k [B, H, N, Dk]; v [B, H, N, Dv] -> (o, s_final, z_final)."""
-    return _forward(False, q, k, v, None, s_init, z_init, eps, phi, want_state, out, s_final, z_final, workspace)
+    return _forward(None, q, k, v, None, s_init, z_init, eps, phi, want_state, out, s_final, z_final, workspace)
 
 
 def linattn_forward_gated(q, k, v, alpha, s_init=None, z_init=None, *, eps=1e-6, phi=PHI_ELU1,
                           want_state=True, out=None, s_final=None, z_final=None, workspace=None):
     """Gated causal forward with alpha [B, H, N] fp32 -> (o, s_final, z_final)."""
-    return _forward(True, q, k, v, alpha, s_init, z_init, eps, phi, want_state, out, s_final, z_final, workspace)
+    if alpha is None:
+        raise ValueError("alpha is required")
+    return _forward(None, q, k, v, alpha, s_init, z_init, eps, phi, want_state, out, s_final, z_final, workspace)
 
 
-def _forward(gated, q, k, v, alpha, s_init, z_init, eps, phi, want_state, out, s_final, z_final, workspace):
-    _dev(q, "q")
-    code = _dtype_code(q)
-    _dev(k, "k", q.dtype)
-    _dev(v, "v", q.dtype)
-    B, H, N, Dk = q.shape
-    Dv = v.shape[-1]
-    if tuple(k.shape) != (B, H, N, Dk) or tuple(v.shape[:3]) != (B, H, N):
-        raise ValueError("q, k, v shapes do not match")
-    if gated:
-        _dev(alpha, "alpha", torch.float32)
-        if tuple(alpha.shape) != (B, H, N):
-            raise ValueError("alpha must be [B, H, N]")
-    if (s_init is None) != (z_init is None):
-        raise ValueError("pass both s_init and z_init or neither")
-    _dev(s_init, "s_init", torch.float32)
-    _dev(z_init, "z_init", torch.float32)
+def linattn_forward_planned(q, k, v, segments, subsegments, alpha=None, s_init=None, z_init=None, *, eps=1e-6,
+                            phi=PHI_ELU1, want_state=True, out=None, s_final=None, z_final=None, workspace=None):
+    """Causal forward (gated if alpha is given) with the sequence split into at most `segments` output
+    segments of `subsegments` state parts each -> (o, s_final, z_final)."""
+    return _forward((int(segments), int(subsegments)), q, k, v, alpha, s_init, z_init, eps, phi, want_state, out,
+                    s_final, z_final, workspace)
+
+
+def _forward(plan, q, k, v, alpha, s_init, z_init, eps, phi, want_state, out, s_final, z_final, workspace):
+    (B, H, N, Dk, Dv, code), specs = _qkv_specs(q, k, v)
+    _pair(s_init, z_init, "s_init and z_init")
+    _pair(s_final, z_final, "s_final and z_final")
+    _validate(specs + [(alpha, "alpha", (B, H, N), torch.float32),
+                       (s_init, "s_init", (B, H, Dk, Dv), torch.float32),
+                       (z_init, "z_init", (B, H, Dk), torch.float32),
+                       (out, "out", (B, H, N, Dv), q.dtype),
+                       (s_final, "s_final", (B, H, Dk, Dv), torch.float32),
+                       (z_final, "z_final", (B, H, Dk), torch.float32)])
     o = out if out is not None else torch.empty((B, H, N, Dv), dtype=q.dtype, device=q.device)
-    _dev(o, "out", q.dtype)
     if want_state:
-        s_final = s_final if s_final is not None else torch.empty((B, H, Dk, Dv), dtype=torch.float32,
-                                                                   device=q.device)
-        z_final = z_final if z_final is not None else torch.empty((B, H, Dk), dtype=torch.float32,
-                                                                   device=q.device)
-        _dev(s_final, "s_final", torch.float32)
-        _dev(z_final, "z_final", torch.float32)
+        if s_final is None:
+            s_final = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device)
+            z_final = torch.empty((B, H, Dk), dtype=torch.float32, device=q.device)
     else:
         s_final = z_final = None
+    gated = alpha is not None
     kind = KIND_GATED if gated else KIND_FORWARD
-    ws, need = _workspace(kind, B, H, N, Dk, Dv, code, q.device, workspace)
     L = lib()
+    if plan is not None:
+        need = workspace_size_planned(kind, B, H, N, Dk, Dv, code, *plan)
+        ws = _workspace(need, q.device, workspace)
+        rc = L.linattn_forward_planned(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(o), _ptr(s_init), _ptr(z_init),
+                                       _ptr(s_final), _ptr(z_final), B, H, N, Dk, Dv, code, phi, float(eps),
+                                       plan[0], plan[1], _ptr(ws), _ws_bytes(ws), _stream(q))
+        _check(rc, "linattn_forward_planned")
+        return o, s_final, z_final
+    ws = _workspace(workspace_size(kind, B, H, N, Dk, Dv, code), q.device, workspace)
     if gated:
         rc = L.linattn_forward_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(o), _ptr(s_init), _ptr(z_init),
                                      _ptr(s_final), _ptr(z_final), B, H, N, Dk, Dv, code, phi, float(eps),
-                                     _ptr(ws), ws.numel(), _stream(q))
+                                     _ptr(ws), _ws_bytes(ws), _stream(q))
     else:
         rc = L.linattn_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(s_init), _ptr(z_init), _ptr(s_final),
-                               _ptr(z_final), B, H, N, Dk, Dv, code, phi, float(eps), _ptr(ws), ws.numel(),
+                               _ptr(z_final), B, H, N, Dk, Dv, code, phi, float(eps), _ptr(ws), _ws_bytes(ws),
                                _stream(q))
     _check(rc, "linattn_forward_gated" if gated else "linattn_forward")
     return o, s_final, z_final
@@ -170,26 +232,18 @@ def linattn_forward_train(q, k, v, s_init=None, z_init=None, *, eps=1e-6, phi=PH
 
     bf16 with Dk, Dv in {64, 128}; den [B, H, N] fp32 feeds linattn_backward.
     """
-    _dev(q, "q")
-    code = _dtype_code(q)
-    _dev(k, "k", q.dtype)
-    _dev(v, "v", q.dtype)
-    B, H, N, Dk = q.shape
-    Dv = v.shape[-1]
-    if tuple(k.shape) != (B, H, N, Dk) or tuple(v.shape[:3]) != (B, H, N):
-        raise ValueError("q, k, v shapes do not match")
-    if (s_init is None) != (z_init is None):
-        raise ValueError("pass both s_init and z_init or neither")
-    _dev(s_init, "s_init", torch.float32)
-    _dev(z_init, "z_init", torch.float32)
+    (B, H, N, Dk, Dv, code), specs = _qkv_specs(q, k, v)
+    _pair(s_init, z_init, "s_init and z_init")
+    _validate(specs + [(s_init, "s_init", (B, H, Dk, Dv), torch.float32),
+                       (z_init, "z_init", (B, H, Dk), torch.float32)])
     o = torch.empty((B, H, N, Dv), dtype=q.dtype, device=q.device)
     den = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     s_final = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device)
     z_final = torch.empty((B, H, Dk), dtype=torch.float32, device=q.device)
-    ws, _ = _workspace(KIND_FORWARD, B, H, N, Dk, Dv, code, q.device, workspace)
+    ws = _workspace(workspace_size(KIND_FORWARD, B, H, N, Dk, Dv, code), q.device, workspace)
     rc = lib().linattn_forward_train(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(den), _ptr(s_init), _ptr(z_init),
                                      _ptr(s_final), _ptr(z_final), B, H, N, Dk, Dv, code, phi, float(eps), _ptr(ws),
-                                     ws.numel(), _stream(q))
+                                     _ws_bytes(ws), _stream(q))
     _check(rc, "linattn_forward_train")
     return o, den, s_final, z_final
 
@@ -201,30 +255,24 @@ def linattn_backward(q, k, v, den, dout, s_init=None, z_init=None, *, eps=1e-6, 
     den is the output of linattn_forward_train on the same q, k, v (and
     initial state, eps, phi).  ``out`` may pass preallocated (dq, dk, dv).
     """
-    _dev(q, "q")
-    code = _dtype_code(q)
-    for name, t in (("k", k), ("v", v), ("dout", dout)):
-        _dev(t, name, q.dtype)
-    _dev(den, "den", torch.float32)
-    B, H, N, Dk = q.shape
-    Dv = v.shape[-1]
-    if (tuple(k.shape) != (B, H, N, Dk) or tuple(v.shape) != (B, H, N, Dv) or tuple(dout.shape) != (B, H, N, Dv)
-            or tuple(den.shape) != (B, H, N)):
-        raise ValueError("q, k, v, den, dout shapes do not match")
-    if (s_init is None) != (z_init is None):
-        raise ValueError("pass both s_init and z_init or neither")
-    _dev(s_init, "s_init", torch.float32)
-    _dev(z_init, "z_init", torch.float32)
+    (B, H, N, Dk, Dv, code), specs = _qkv_specs(q, k, v)
+    _pair(s_init, z_init, "s_init and z_init")
+    if out is not None and len(out) != 3:
+        raise ValueError("out must be (dq, dk, dv)")
+    dq, dk, dv = out if out is not None else (None, None, None)
+    _validate(specs + [(den, "den", (B, H, N), torch.float32), (dout, "dout", (B, H, N, Dv), q.dtype),
+                       (s_init, "s_init", (B, H, Dk, Dv), torch.float32),
+                       (z_init, "z_init", (B, H, Dk), torch.float32),
+                       (dq, "dq", (B, H, N, Dk), q.dtype), (dk, "dk", (B, H, N, Dk), q.dtype),
+                       (dv, "dv", (B, H, N, Dv), q.dtype)])
+    if den is None or dout is None:
+        raise ValueError("den and dout are required")
     if out is None:
-        out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
-    dq, dk, dv = out
-    _dev(dq, "dq", q.dtype)
-    _dev(dk, "dk", q.dtype)
-    _dev(dv, "dv", q.dtype)
-    ws, _ = _workspace(KIND_BACKWARD, B, H, N, Dk, Dv, code, q.device, workspace)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = _workspace(workspace_size(KIND_BACKWARD, B, H, N, Dk, Dv, code), q.device, workspace)
     rc = lib().linattn_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(den), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
                                 _ptr(s_init), _ptr(z_init), B, H, N, Dk, Dv, code, phi, float(eps), _ptr(ws),
-                                ws.numel(), _stream(q))
+                                _ws_bytes(ws), _stream(q))
     _check(rc, "linattn_backward")
     return dq, dk, dv
 
@@ -235,19 +283,10 @@ def linattn_forward_delta(q, k, v, beta=None, s_init=None, *, alpha=None, phi=PH
     phi(k)/|phi(k)|, write beta times the difference, o = S^T phi(q).  alpha, beta [B, H, N]
     fp32 or None (ones) -> (o, s_final or None).  bf16 with Dk, Dv in {64, 128}.
     """
-    _dev(q, "q")
-    code = _dtype_code(q)
-    _dev(k, "k", q.dtype)
-    _dev(v, "v", q.dtype)
-    B, H, N, Dk = q.shape
-    Dv = v.shape[-1]
-    if tuple(k.shape) != (B, H, N, Dk) or tuple(v.shape[:3]) != (B, H, N):
-        raise ValueError("q, k, v shapes do not match")
-    for name, t in (("beta", beta), ("alpha", alpha)):
-        _dev(t, name, torch.float32)
-        if t is not None and tuple(t.shape) != (B, H, N):
-            raise ValueError(f"{name} must be [B, H, N]")
-    _dev(s_init, "s_init", torch.float32)
+    (B, H, N, Dk, Dv, code), specs = _qkv_specs(q, k, v)
+    _validate(specs + [(beta, "beta", (B, H, N), torch.float32), (alpha, "alpha", (B, H, N), torch.float32),
+                       (s_init, "s_init", (B, H, Dk, Dv), torch.float32),
+                       (out, "out", (B, H, N, Dv), q.dtype)])
     o = out if out is not None else torch.empty((B, H, N, Dv), dtype=q.dtype, device=q.device)
     s_final = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device) if want_state else None
     rc = lib().linattn_forward_delta(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(o), _ptr(s_init),
@@ -267,25 +306,17 @@ def linattn_forward_snapshots(q, k, v, positions, alpha=None, s_init=None, z_ini
     z_snap [B, H, n, Dk], s_final, z_final).  alpha [B, H, N] fp32 or None.
     bf16 with Dk, Dv in {64, 128}.
     """
-    _dev(q, "q")
-    code = _dtype_code(q)
-    _dev(k, "k", q.dtype)
-    _dev(v, "v", q.dtype)
-    B, H, N, Dk = q.shape
-    Dv = v.shape[-1]
-    if tuple(k.shape) != (B, H, N, Dk) or tuple(v.shape[:3]) != (B, H, N):
-        raise ValueError("q, k, v shapes do not match")
-    if (s_init is None) != (z_init is None):
-        raise ValueError("pass both s_init and z_init or neither")
-    _dev(s_init, "s_init", torch.float32)
-    _dev(z_init, "z_init", torch.float32)
-    _dev(alpha, "alpha", torch.float32)
-    if alpha is not None and tuple(alpha.shape) != (B, H, N):
-        raise ValueError("alpha must be [B, H, N]")
+    (B, H, N, Dk, Dv, code), specs = _qkv_specs(q, k, v)
+    _pair(s_init, z_init, "s_init and z_init")
     pos = [int(p) for p in positions]
     n = len(pos)
     if not 1 <= n <= MAX_SNAPSHOTS:
         raise ValueError(f"1 to {MAX_SNAPSHOTS} positions")
+    if not all(0 <= p < N for p in pos):
+        raise ValueError(f"positions must lie in [0, {N})")
+    _validate(specs + [(alpha, "alpha", (B, H, N), torch.float32),
+                       (s_init, "s_init", (B, H, Dk, Dv), torch.float32),
+                       (z_init, "z_init", (B, H, Dk), torch.float32)])
     parr = (ctypes.c_int * n)(*pos)
     o = torch.empty((B, H, N, Dv), dtype=q.dtype, device=q.device)
     s_snap = torch.empty((B, H, n, Dk, Dv), dtype=torch.float32, device=q.device)
@@ -293,54 +324,46 @@ def linattn_forward_snapshots(q, k, v, positions, alpha=None, s_init=None, z_ini
     s_final = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device)
     z_final = torch.empty((B, H, Dk), dtype=torch.float32, device=q.device)
     kind = KIND_GATED if alpha is not None else KIND_FORWARD
-    ws, _ = _workspace(kind, B, H, N, Dk, Dv, code, q.device, workspace)
+    ws = _workspace(workspace_size(kind, B, H, N, Dk, Dv, code), q.device, workspace)
     rc = lib().linattn_forward_snapshots(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(o), _ptr(s_init),
                                          _ptr(z_init), _ptr(s_final), _ptr(z_final),
                                          ctypes.cast(parr, ctypes.c_void_p), n, _ptr(s_snap), _ptr(z_snap), B, H, N,
-                                         Dk, Dv, code, phi, float(eps), _ptr(ws), ws.numel(), _stream(q))
+                                         Dk, Dv, code, phi, float(eps), _ptr(ws), _ws_bytes(ws), _stream(q))
     _check(rc, "linattn_forward_snapshots")
     return o, s_snap, z_snap, s_final, z_final
 
 
 def linattn_forward_noncausal(q, k, v, *, eps=1e-6, phi=PHI_ELU1, want_state=True, out=None, workspace=None):
     """Non-causal form -> (o, s, z) with the global state s [B, H, Dk, Dv], z [B, H, Dk]."""
-    _dev(q, "q")
-    code = _dtype_code(q)
-    _dev(k, "k", q.dtype)
-    _dev(v, "v", q.dtype)
-    B, H, N, Dk = q.shape
-    Dv = v.shape[-1]
-    if tuple(k.shape) != (B, H, N, Dk) or tuple(v.shape[:3]) != (B, H, N):
-        raise ValueError("q, k, v shapes do not match")
+    (B, H, N, Dk, Dv, code), specs = _qkv_specs(q, k, v)
+    _validate(specs + [(out, "out", (B, H, N, Dv), q.dtype)])
     o = out if out is not None else torch.empty((B, H, N, Dv), dtype=q.dtype, device=q.device)
-    _dev(o, "out", q.dtype)
     s = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device) if want_state else None
     z = torch.empty((B, H, Dk), dtype=torch.float32, device=q.device) if want_state else None
-    ws, need = _workspace(KIND_NONCAUSAL, B, H, N, Dk, Dv, code, q.device, workspace)
+    ws = _workspace(workspace_size(KIND_NONCAUSAL, B, H, N, Dk, Dv, code), q.device, workspace)
     rc = lib().linattn_forward_noncausal(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(s), _ptr(z), B, H, N, Dk, Dv,
-                                         code, phi, float(eps), _ptr(ws), ws.numel(), _stream(q))
+                                         code, phi, float(eps), _ptr(ws), _ws_bytes(ws), _stream(q))
     _check(rc, "linattn_forward_noncausal")
     return o, s, z
 
 
+def _decode_specs(q, k, v, s, z, alpha, out, state_dtype):
+    B, H, Dk = _dims(q, "q", 3)
+    Dv = _dims(v, "v", 3)[2]
+    code = _dtype_code(q)
+    specs = [(q, "q", (B, H, Dk), None), (k, "k", (B, H, Dk), q.dtype), (v, "v", (B, H, Dv), q.dtype),
+             (s, "s", (B, H, Dk, Dv), state_dtype), (z, "z", (B, H, Dk), state_dtype),
+             (alpha, "alpha", (B, H), torch.float32), (out, "out", (B, H, Dv), q.dtype)]
+    if s is None or z is None:
+        raise ValueError("s and z are required")
+    _validate(specs)
+    return B, H, Dk, Dv, code
+
+
 def linattn_decode_step(q, k, v, s, z, alpha=None, *, eps=1e-6, phi=PHI_ELU1, out=None):
     """One token per (b, h): q, k [B, H, Dk], v [B, H, Dv]; s, z updated in place; returns o [B, H, Dv]."""
-    _dev(q, "q")
-    code = _dtype_code(q)
-    _dev(k, "k", q.dtype)
-    _dev(v, "v", q.dtype)
-    B, H, Dk = q.shape
-    Dv = v.shape[-1]
-    _dev(s, "s", torch.float32)
-    _dev(z, "z", torch.float32)
-    if tuple(s.shape) != (B, H, Dk, Dv) or tuple(z.shape) != (B, H, Dk) or tuple(k.shape) != (B, H, Dk):
-        raise ValueError("decode shapes do not match")
-    if alpha is not None:
-        _dev(alpha, "alpha", torch.float32)
-        if tuple(alpha.shape) != (B, H):
-            raise ValueError("alpha must be [B, H]")
+    B, H, Dk, Dv, code = _decode_specs(q, k, v, s, z, alpha, out, torch.float32)
     o = out if out is not None else torch.empty((B, H, Dv), dtype=q.dtype, device=q.device)
-    _dev(o, "out", q.dtype)
     rc = lib().linattn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(s), _ptr(z), _ptr(alpha), _ptr(o), B, H, Dk,
                                    Dv, code, phi, float(eps), _stream(q))
     _check(rc, "linattn_decode_step")
@@ -352,24 +375,10 @@ _STATE_CODES = {torch.float32: F32, torch.bfloat16: BF16, torch.float8_e4m3fn: F
 
 def linattn_decode_step_lowp(q, k, v, s, z, alpha=None, *, eps=1e-6, phi=PHI_ELU1, out=None):
     """linattn_decode_step with S, z stored as float32, bfloat16 or float8_e4m3fn (their dtype decides)."""
-    _dev(q, "q")
-    code = _dtype_code(q)
-    _dev(k, "k", q.dtype)
-    _dev(v, "v", q.dtype)
-    B, H, Dk = q.shape
-    Dv = v.shape[-1]
-    if s.dtype not in _STATE_CODES or z.dtype != s.dtype:
-        raise TypeError("s and z must share one of float32, bfloat16, float8_e4m3fn")
-    _dev(s, "s", s.dtype)
-    _dev(z, "z", s.dtype)
-    if tuple(s.shape) != (B, H, Dk, Dv) or tuple(z.shape) != (B, H, Dk) or tuple(k.shape) != (B, H, Dk):
-        raise ValueError("decode shapes do not match")
-    if alpha is not None:
-        _dev(alpha, "alpha", torch.float32)
-        if tuple(alpha.shape) != (B, H):
-            raise ValueError("alpha must be [B, H]")
+    if not isinstance(s, torch.Tensor) or s.dtype not in _STATE_CODES:
+        raise TypeError("s must be float32, bfloat16 or float8_e4m3fn")
+    B, H, Dk, Dv, code = _decode_specs(q, k, v, s, z, alpha, out, s.dtype)
     o = out if out is not None else torch.empty((B, H, Dv), dtype=q.dtype, device=q.device)
-    _dev(o, "out", q.dtype)
     rc = lib().linattn_decode_step_lowp(_ptr(q), _ptr(k), _ptr(v), _ptr(s), _ptr(z), _STATE_CODES[s.dtype],
                                         _ptr(alpha), _ptr(o), B, H, Dk, Dv, code, phi, float(eps), _stream(q))
     _check(rc, "linattn_decode_step_lowp")

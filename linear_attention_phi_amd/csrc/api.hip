@@ -48,13 +48,19 @@ bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-Plan make_plan(int kind, int B, int H, int N, int Dk, int Dv, int dtype) {
+// seg_req, sub_req > 0 replace the automatic choice of the number of output
+// segments and of state sub-segments per output segment (linattn_forward_planned):
+// the sequence is cut into segments of ceil(chunks / seg_req) chunks (so at most
+// seg_req of them), each into the largest divisor of its chunk count that does
+// not exceed sub_req.
+Plan make_plan(int kind, int B, int H, int N, int Dk, int Dv, int dtype, int seg_req = 0, int sub_req = 0) {
     Plan p;
     p.mfma = dtype == LINATTN_BF16 && Dk >= 32 && Dv >= 32;
     p.nvb = (Dv + 63) / 64;
     const long long BH = (long long)B * H;
     const int nch = (N + kChunk - 1) / kChunk;
     long long want = p.mfma ? (kTargetGroupsMfma + BH - 1) / BH : (kTargetWavesRecur + BH * p.nvb - 1) / (BH * p.nvb);
+    if (seg_req > 0) want = seg_req;
     if (want < 1) want = 1;
     if (want > nch) want = nch;
     const int cps = (int)((nch + want - 1) / want);
@@ -63,7 +69,8 @@ Plan make_plan(int kind, int B, int H, int N, int Dk, int Dv, int dtype) {
     // The state pass streams only K and V and fits two workgroups per compute
     // unit: split each output segment into R sub-segments (R divides cps).
     if (p.mfma) {
-        const long long want_r = (kTargetGroupsState + (long long)p.P * BH - 1) / ((long long)p.P * BH);
+        long long want_r = (kTargetGroupsState + (long long)p.P * BH - 1) / ((long long)p.P * BH);
+        if (sub_req > 0) want_r = sub_req;
         for (int r = (int)(want_r < cps ? want_r : cps); r >= 1; --r)
             if (cps % r == 0) {
                 p.R = r;
@@ -458,7 +465,8 @@ template <typename T, typename... A> int recur_noncausal_dk(int Dk, A &&...a) {
 int forward_impl(bool gated, const void *q, const void *k, const void *v, const float *alpha, void *o,
                  const float *s_init, const float *z_init, float *s_final, float *z_final, int B, int H, int N,
                  int Dk, int Dv, int dtype, int phi, float eps, void *workspace, size_t workspace_bytes,
-                 void *hip_stream, float *den = nullptr, const SnapRequest *snap = nullptr) {
+                 void *hip_stream, float *den = nullptr, const SnapRequest *snap = nullptr, int seg_req = 0,
+                 int sub_req = 0) {
     LA_TRY(check_common(B, H, N, Dk, Dv, dtype, phi, eps));
     if (!q || !k || !v || !o || (gated && !alpha)) return LINATTN_EINVAL;
     if ((s_init == nullptr) != (z_init == nullptr)) return LINATTN_EINVAL;
@@ -466,7 +474,8 @@ int forward_impl(bool gated, const void *q, const void *k, const void *v, const 
     const size_t es = dtype == LINATTN_BF16 ? 2 : 4;
     const size_t nq = (size_t)B * H * N * Dk * es, nv = (size_t)B * H * N * Dv * es;
     if (overlaps(o, nv, q, nq) || overlaps(o, nv, k, nq) || overlaps(o, nv, v, nv)) return LINATTN_EINVAL;
-    const Plan pl = make_plan(gated ? LINATTN_KIND_GATED : LINATTN_KIND_FORWARD, B, H, N, Dk, Dv, dtype);
+    const Plan pl =
+        make_plan(gated ? LINATTN_KIND_GATED : LINATTN_KIND_FORWARD, B, H, N, Dk, Dv, dtype, seg_req, sub_req);
     if (pl.ws_bytes && (!workspace || workspace_bytes < pl.ws_bytes)) return LINATTN_EWORKSPACE;
     hipStream_t st = (hipStream_t)hip_stream;
     char *ws = (char *)workspace;
@@ -535,6 +544,24 @@ int linattn_forward_gated(const void *q, const void *k, const void *v, const flo
                           size_t workspace_bytes, void *hip_stream) {
     return forward_impl(true, q, k, v, alpha, o, s_init, z_init, s_final, z_final, B, H, N, Dk, Dv, dtype, phi, eps,
                         workspace, workspace_bytes, hip_stream);
+}
+
+int linattn_forward_planned(const void *q, const void *k, const void *v, const float *alpha, void *o,
+                            const float *s_init, const float *z_init, float *s_final, float *z_final, int B, int H,
+                            int N, int Dk, int Dv, int dtype, int phi, float eps, int segments, int subsegments,
+                            void *workspace, size_t workspace_bytes, void *hip_stream) {
+    if (segments < 1 || subsegments < 1) return LINATTN_EINVAL;
+    return forward_impl(alpha != nullptr, q, k, v, alpha, o, s_init, z_init, s_final, z_final, B, H, N, Dk, Dv,
+                        dtype, phi, eps, workspace, workspace_bytes, hip_stream, nullptr, nullptr, segments,
+                        subsegments);
+}
+
+size_t linattn_workspace_size_planned(int kind, int B, int H, int N, int Dk, int Dv, int dtype, int segments,
+                                      int subsegments) {
+    if (kind != LINATTN_KIND_FORWARD && kind != LINATTN_KIND_GATED) return 0;
+    if (segments < 1 || subsegments < 1) return 0;
+    if (check_common(B, H, N, Dk, Dv, dtype, LINATTN_PHI_ELU1, 0.f) != LINATTN_OK) return 0;
+    return make_plan(kind, B, H, N, Dk, Dv, dtype, segments, subsegments).ws_bytes;
 }
 
 // The training forward and the backward run the chunked bf16 kernels only.

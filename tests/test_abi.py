@@ -27,7 +27,16 @@ def declared_functions():
 
 @pytest.fixture(scope="module")
 def L():
-    return b.lib()
+    # LINATTN_ABI_LIB: another build of the same library (the sanitizer run
+    # in test_sanitizers.py points it at a host-instrumented one)
+    path = os.environ.get("LINATTN_ABI_LIB")
+    if not path:
+        return b.lib()
+    h = ctypes.CDLL(path)
+    for name, (args, res) in b.SIGNATURES.items():
+        getattr(h, name).argtypes = args
+        getattr(h, name).restype = res
+    return h
 
 
 def test_every_declared_symbol_is_exported(L):
@@ -141,6 +150,96 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(1, 1, 4, 16)
     with pytest.raises(TypeError):
         b.linattn_forward(x, x, x)
+
+
+def _shape_cases():
+    """Calls through the binding, each with one caller tensor of a wrong size.
+
+    The tensors live on the CPU: the binding checks every shape before it
+    looks at devices, so each call must raise ValueError and nothing can be
+    launched.
+    """
+    import torch
+    B, H, N, D = 1, 2, 8, 16
+    bf = torch.bfloat16
+    q = torch.zeros(B, H, N, D, dtype=bf)
+    s = torch.zeros(B, H, D, D)
+    z = torch.zeros(B, H, D)
+    a = torch.ones(B, H, N)
+    bad_s, bad_z = torch.zeros(B, H, D, D + 1), torch.zeros(B, H, D + 1)
+    bad_o = torch.zeros(B, H, N - 1, D, dtype=bf)
+    qd = torch.zeros(B, H, D, dtype=bf)
+    return {
+        "forward s_init": lambda: b.linattn_forward(q, q, q, bad_s, z),
+        "forward z_init": lambda: b.linattn_forward(q, q, q, s, bad_z),
+        "forward out": lambda: b.linattn_forward(q, q, q, out=bad_o),
+        "forward s_final": lambda: b.linattn_forward(q, q, q, s_final=bad_s, z_final=z),
+        "forward z_final": lambda: b.linattn_forward(q, q, q, s_final=s, z_final=bad_z),
+        "forward k": lambda: b.linattn_forward(q, bad_o, q),
+        "forward v": lambda: b.linattn_forward(q, q, bad_o),
+        "gated alpha": lambda: b.linattn_forward_gated(q, q, q, torch.ones(B, H, N + 1)),
+        "planned out": lambda: b.linattn_forward_planned(q, q, q, 2, 1, out=bad_o),
+        "train s_init": lambda: b.linattn_forward_train(q, q, q, bad_s, z),
+        "backward den": lambda: b.linattn_backward(q, q, q, torch.zeros(B, H, N + 1), q),
+        "backward dout": lambda: b.linattn_backward(q, q, q, a, bad_o),
+        "backward z_init": lambda: b.linattn_backward(q, q, q, a, q, s, bad_z),
+        "backward dq": lambda: b.linattn_backward(q, q, q, a, q, out=(bad_o, q, q)),
+        "backward dk": lambda: b.linattn_backward(q, q, q, a, q, out=(q, bad_o, q)),
+        "backward dv": lambda: b.linattn_backward(q, q, q, a, q, out=(q, q, bad_o)),
+        "snapshots s_init": lambda: b.linattn_forward_snapshots(q, q, q, [0], s_init=bad_s, z_init=z),
+        "snapshots alpha": lambda: b.linattn_forward_snapshots(q, q, q, [0], alpha=torch.ones(B, H + 1, N)),
+        "snapshots position": lambda: b.linattn_forward_snapshots(q, q, q, [N]),
+        "delta s_init": lambda: b.linattn_forward_delta(q, q, q, s_init=bad_s),
+        "delta out": lambda: b.linattn_forward_delta(q, q, q, out=bad_o),
+        "delta beta": lambda: b.linattn_forward_delta(q, q, q, beta=torch.ones(B, H, N - 1)),
+        "noncausal out": lambda: b.linattn_forward_noncausal(q, q, q, out=bad_o),
+        "decode v": lambda: b.linattn_decode_step(qd, qd, torch.zeros(B, H + 1, D, dtype=bf), s, z),
+        "decode s": lambda: b.linattn_decode_step(qd, qd, qd, bad_s, z),
+        "decode out": lambda: b.linattn_decode_step(qd, qd, qd, s, z, out=torch.zeros(B, H, D + 1, dtype=bf)),
+        "decode alpha": lambda: b.linattn_decode_step(qd, qd, qd, s, z, torch.ones(B, H, 1)),
+        "decode lowp z": lambda: b.linattn_decode_step_lowp(qd, qd, qd, s.to(bf), torch.zeros(B, H, D + 1, dtype=bf)),
+    }
+
+
+@pytest.mark.parametrize("case", sorted(_shape_cases()))
+def test_binding_checks_every_tensor_shape_before_any_launch(case):
+    with pytest.raises(ValueError):
+        _shape_cases()[case]()
+
+
+def test_binding_checks_dtype_before_device():
+    import torch
+    q = torch.zeros(1, 1, 8, 16, dtype=torch.bfloat16)
+    with pytest.raises(TypeError, match="float32"):
+        b.linattn_forward(q, q, q, torch.zeros(1, 1, 16, 16, dtype=torch.float64), torch.zeros(1, 1, 16))
+    with pytest.raises(TypeError, match="bfloat16"):
+        b.linattn_forward(q, q.float(), q)
+
+
+def planned(L, segments=2, subsegments=1, B=1, H=1, N=8192, Dk=64, Dv=64, dtype=1, ws=None, wsb=0, alpha=None):
+    return L.linattn_forward_planned(FAKE[0], FAKE[1], FAKE[2], alpha, FAKE[3], None, None, None, None, B, H, N,
+                                     Dk, Dv, dtype, 0, 1e-6, segments, subsegments, ws, wsb, None)
+
+
+def test_planned_forward_rejects_bad_arguments_and_sizes_its_workspace(L):
+    assert planned(L, segments=0) == EINVAL
+    assert planned(L, subsegments=0) == EINVAL
+    assert planned(L, Dk=48) == ESHAPE
+    wsp = L.linattn_workspace_size_planned
+    cell = (64 * 64 + 64) * 4
+    # one segment: no prefix, no workspace, even for a long sequence
+    assert wsp(0, 1, 1, 8192, 64, 64, 1, 1, 1) == 0
+    # 8192 tokens = 128 chunks: 4 segments of 32 chunks, 2 parts each, plus the end state
+    assert wsp(0, 1, 1, 8192, 64, 64, 1, 4, 2) >= (4 * 2 + 1) * cell
+    # a part count that does not divide the segment's chunks falls to a divisor: 32 chunks, 3 -> 2
+    assert wsp(0, 1, 1, 8192, 64, 64, 1, 4, 3) == wsp(0, 1, 1, 8192, 64, 64, 1, 4, 2)
+    # more segments than chunks: one chunk each
+    assert wsp(0, 1, 1, 8192, 64, 64, 1, 1000, 1) == wsp(0, 1, 1, 8192, 64, 64, 1, 128, 1)
+    assert wsp(1, 1, 1, 8192, 64, 64, 1, 4, 2) > wsp(0, 1, 1, 8192, 64, 64, 1, 4, 2)  # gate products
+    assert wsp(2, 1, 1, 8192, 64, 64, 1, 4, 2) == 0    # kinds other than the causal forward
+    assert wsp(0, 1, 1, 8192, 64, 64, 1, 0, 1) == 0
+    need = wsp(0, 1, 1, 8192, 64, 64, 1, 4, 2)
+    assert planned(L, segments=4, subsegments=2, ws=FAKE[6], wsb=need - 1) == EWORKSPACE
 
 
 def train(L, q=FAKE[0], k=FAKE[1], v=FAKE[2], o=FAKE[3], den=FAKE[4], B=1, H=1, N=64, Dk=64, Dv=64, dtype=1,

@@ -185,3 +185,49 @@ def test_noncausal(shape, dtype):
     _, sc, zc = la.linattn_forward(q.to(DEV), k.to(DEV), v.to(DEV))
     torch.cuda.synchronize()
     assert_close("S vs causal", s.cpu(), sc.cpu(), tol, per="head")
+
+
+# ---- independence from the split of the sequence (the fixed-size-state page,
+# "Adding to the same state in turn": the state is the sum of the outer
+# products, whatever way the tokens are grouped).  One input, run with one
+# sequential pass, with 16 and with 256 parallel segments (one chunk each):
+# every plan within tolerance of the oracle, and the plans within rounding of
+# one another.
+
+PLANS = [(1, 1), (16, 2), (256, 1)]
+
+
+@pytest.mark.parametrize("gated", [False, True])
+@pytest.mark.parametrize("D", [128, 64])
+def test_results_do_not_depend_on_the_segment_plan(gated, D):
+    q, k, v, a = make(1, 2, 256 * 64 - 37, D, D, torch.bfloat16, seed=130 + D + gated, gated=gated)
+    args = [x.to(DEV) for x in (q, k, v)]
+    ad = None if a is None else a.to(DEV)
+    runs = {}
+    for P, R in PLANS:
+        runs[(P, R)] = [x.cpu() for x in la.linattn_forward_planned(*args, P, R, alpha=ad)]
+    torch.cuda.synchronize()
+    ro, rs, rz = oracle.forward(q, k, v, alpha=a)
+    tol = TOL[torch.bfloat16]
+    for plan, (o, s, z) in runs.items():
+        assert_close(f"O, plan {plan}", o, ro, tol)
+        assert_close(f"S, plan {plan}", s, rs, tol, per="head")
+        assert_close(f"z, plan {plan}", z, rz, tol, per="head")
+    # the fp32 states differ only by the order of their additions; the bf16
+    # outputs by that and a last-bit rounding
+    o0, s0, z0 = runs[PLANS[0]]
+    for plan in PLANS[1:]:
+        o, s, z = runs[plan]
+        assert_close(f"O, plan {plan} vs {PLANS[0]}", o, o0, 1e-2)
+        assert_close(f"S, plan {plan} vs {PLANS[0]}", s, s0, 1e-5, per="head")
+        assert_close(f"z, plan {plan} vs {PLANS[0]}", z, z0, 1e-5, per="head")
+
+
+def test_default_plan_is_one_of_the_planned_ones():
+    # B1 H2 N16384: the library picks 128 segments of 2 chunks, one state part each chunk
+    q, k, v, _ = make(1, 2, 16384, 128, 128, torch.bfloat16, seed=140)
+    args = [x.to(DEV) for x in (q, k, v)]
+    o1, s1, z1 = la.linattn_forward(*args)
+    o2, s2, z2 = la.linattn_forward_planned(*args, 128, 2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2) and torch.equal(z1, z2)

@@ -2,7 +2,9 @@
 
 linattn_forward_snapshots runs through the C ABI; its o and final state must
 equal the plain forward's bit for bit (same kernels), and every snapshot is
-compared per head with oracle.snapshots on the same seeded inputs.  Positions
+compared on its own, normwise per (b, h, position), with oracle.snapshots on
+the same seeded inputs (z grows with the position, so one early snapshot must
+not be judged against the size of a later one).  Positions
 sit on and next to chunk (64) and state-cell boundaries, at the first and
 last token, repeated and out of order; the one-segment plan (many heads) runs
 every snapshot from the initial state.
@@ -40,8 +42,8 @@ def check(q, k, v, positions, a=None, s0=None, z0=None):
     assert torch.equal(o, o2) and torch.equal(sf, sf2) and torch.equal(zf, zf2)
     rs, rz = oracle.snapshots(q, k, v, positions, s0, z0, alpha=a)
     tol = TOL[torch.bfloat16]
-    assert_close("S snapshots", ss.cpu(), rs, tol, per="head")
-    assert_close("z snapshots", zs.cpu(), rz, tol, per="head")
+    assert_close("S snapshots", ss.cpu(), rs, tol, per="item")
+    assert_close("z snapshots", zs.cpu(), rz, tol, per="item")
     return ss, zs, sf, zf
 
 

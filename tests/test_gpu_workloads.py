@@ -2,10 +2,10 @@
 configuration the benchmark times, and on the backward as the benchmark times
 it (over the 131072-token workload).
 
-Where the oracle is too slow for every output (the 131072-token workload), it
-checks whole heads (every output row of the first and last head, and their
-gradients) and the final state of every head; elsewhere every output is
-checked.
+On the 131072-token workload the forward's outputs are compared on every row
+of every head; its backward and snapshot forwards on four heads spread over
+the sixteen (every gradient row, every snapshot position); elsewhere every
+output is checked.
 """
 import time
 
@@ -16,7 +16,7 @@ import torch
 import oracle
 from linear_attention_phi_amd import binding as la
 from linear_attention_phi_amd import synth
-from parity import TOL, assert_close
+from parity import TOL, assert_close, dq_term_size, head_rel_err
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -64,11 +64,13 @@ def test_long_n131072_d128_sampled():
     rs, rz = oracle.state_from_prefix(k[0], v[0])
     assert_close("S (all heads)", s, rs[None], TOL[w.dtype], per="head")
     assert_close("z (all heads)", z, rz[None], TOL[w.dtype], per="head")
-    hs = [0, w.H - 1]
-    stamp(f"oracle: heads {hs}, all {w.N} rows")
-    ro, rsh, _ = oracle.forward(q[:, hs], k[:, hs], v[:, hs])
-    assert_close(f"O heads {hs}", o[:, hs], ro, TOL[w.dtype])
-    assert_close(f"S heads {hs}", s[:, hs], rsh, TOL[w.dtype], per="head")
+    stamp(f"oracle: all {w.H} heads, all {w.N} rows")
+    ro, rsh, _ = oracle.forward(q, k, v)
+    assert_close("O (all heads)", o, ro, TOL[w.dtype])
+    assert_close("S (all heads, recurrence)", s, rsh, TOL[w.dtype], per="head")
+
+
+SPREAD_HEADS = [0, 5, 10, 15]
 
 
 def test_backward_on_the_long_workload_sampled():
@@ -84,20 +86,24 @@ def test_backward_on_the_long_workload_sampled():
     _, den, _, _ = la.linattn_forward_train(d[0], d[1], d[2])
     dq, dk, dv = la.linattn_backward(d[0], d[1], d[2], den, d[3])
     torch.cuda.synchronize()
-    hs = [0, w.H - 1]
+    hs = SPREAD_HEADS
     got = [x[:, hs].cpu() for x in (dq, dk, dv)]
     del d, den, dq, dk, dv
     stamp(f"oracle: gradients of heads {hs}")
-    rq, rk, rv, _, _ = oracle.backward(q[:, hs], k[:, hs], v[:, hs], g[:, hs])
+    qh, kh, vh, gh = (x[:, hs] for x in (q, k, v, g))
+    rq, rk, rv, _, _ = oracle.backward(qh, kh, vh, gh)
+    ro, _, _ = oracle.forward(qh, kh, vh)
+    floor = dq_term_size(qh, kh, gh, ro)
     for name, x, r in zip(("dq", "dk", "dv"), got, (rq, rk, rv)):
         assert torch.isfinite(x.float()).all()
-        assert_close(f"{name} heads {hs}", x, r, TOL[w.dtype], per="head")
+        print(f"  {name}: per-head error {head_rel_err(x, r):.3e} (information)")
+        assert_close(f"{name} rows, heads {hs}", x, r, TOL[w.dtype], floor=floor if name == "dq" else None)
 
 
 def test_snapshots_on_the_long_workload_sampled():
     # the snapshot forward as the benchmark times it: 8 prefix-cache points at
     # 16384 m - 1 and the last 8 tokens of the 131072-token workload; the states
-    # of the first and last head at every position against the prefix sum
+    # of four spread heads at every position against the prefix sum
     w = synth.WORKLOADS["long_n131072_d128"]
     stamp("generating inputs")
     q, k, v = synth.qkv(w)
@@ -108,7 +114,7 @@ def test_snapshots_on_the_long_workload_sampled():
     o2, _, _ = la.linattn_forward(*d)
     torch.cuda.synchronize()
     assert torch.equal(o, o2)
-    hs = [0, w.H - 1]
+    hs = SPREAD_HEADS
     ss, zs = ss[:, hs].cpu(), zs[:, hs].cpu()
     del d, o, o2
     stamp(f"oracle: heads {hs} at {len(pos)} positions")
