@@ -5,15 +5,26 @@
 One step is one causal forward over the long-context workload (B=1, H=16,
 N=131072, Dk=Dv=128, bf16 in and out, fp32 state): the segment-state pass, the
 prefix over segments and the chunked output pass, with inputs resident in HBM.
-Prints ONE JSON line: tokens/s (B*N per step), the roofline fraction of the
-dominant kernel (timed with HIP events recorded by the library around each of
-its launches), the fp64 oracle timed on a bounded sample on the host cores,
-and, under "paths", the decode step, the gated forward and the non-causal form
-on their own workloads.
+Prints ONE JSON line:
+
+* ``value``: tokens/s (B*N per step) from a loop of exactly K timed steps;
+* ``roofline``: the dominant kernel's algorithmic bytes over its average launch
+  time (HIP events the library records around each of its launches, in a
+  second loop of K steps whose own ms/step is reported beside them), with the
+  HBM bytes the rocprofv3 counters measured for it (``profiles/counters.json``,
+  used only while the kernel sources still hash to what was profiled) and the
+  MFMA work the counters saw;
+* ``path_roofline``: the same for the whole call (every kernel of one step);
+* ``cpu_baseline``: the fp64 oracle timed on a bounded sample of the same
+  workload on the host cores this process may use;
+* ``paths``: the other workloads (the 4096-token, 64-dim forward over rotated
+  input sets, the gated forward, the decode step with an fp32 and a bf16 state,
+  the non-causal form, the forward with snapshots, the backward, the delta
+  rule), each with the same fields and its own short oracle timing.
 
 Also: ``--copy-calibration`` runs only a plain device copy of a known size
-(for scaling the FETCH_SIZE / WRITE_SIZE counters), ``--path`` picks a single
-workload to run (profiling runs).
+(for scaling the FETCH_SIZE / WRITE_SIZE counters), ``--path`` runs a single
+workload (profiling runs).
 """
 from __future__ import annotations
 
@@ -21,6 +32,7 @@ import argparse
 import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
@@ -35,7 +47,10 @@ from linear_attention_phi_amd import synth  # noqa: E402
 
 METRIC = "causal linear-attn fwd Mtokens/s at N=128K,D=128; % of MFMA/HBM roofline"
 HEADLINE = "long_n131072_d128"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
+# c2's inputs (67.6 MB) fit the 256 MB Infinity Cache; cycling this many sets
+# (405 MB) keeps every step's reads coming from HBM
+C2_INPUT_SETS = 6
 
 
 def log(*a):
@@ -79,6 +94,7 @@ def timed(fn, steps, warmup, stream):
     warm(fn, warmup)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     e0.record(stream)
     for _ in range(steps):
         fn()
@@ -87,49 +103,64 @@ def timed(fn, steps, warmup, stream):
     return e0.elapsed_time(e1) / steps
 
 
-def kernel_times(fn, steps):
-    """Average device ms per launch of each library kernel, from the library's own HIP events."""
+def kernel_times(fn, steps, stream):
+    """Per library kernel: launches per step and average device ms per launch, from the library's
+    own HIP events; and the ms per step of that same loop (events add a little per launch)."""
     la.linattn_profile_enable(True)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
     for _ in range(steps):
         fn()
+    e1.record(stream)
     torch.cuda.synchronize()
     rec = la.linattn_profile_read()
     la.linattn_profile_enable(False)
-    return {k: {"launches": n, "avg_ms": ms / n} for k, (n, ms) in rec.items()}
+    kt = {k: {"launches_per_step": n / steps, "avg_ms": ms / n} for k, (n, ms) in rec.items()}
+    return kt, e0.elapsed_time(e1) / steps
 
 
-def stored_traffic(kernel, workload):
-    """HBM bytes per launch from the committed counter runs, if taken on the current kernel source."""
+def stored_counters(kernel, workload):
+    """Counter figures of one launch from the committed rocprofv3 runs, if taken on the current sources."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(COUNTERS_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    e = t.get(kernel, {}).get(workload)
+    e = t.get("kernels", {}).get(kernel, {}).get(workload)
     if not e or e.get("source_hash") != kernel_source_hash():
         return None
-    return e.get("bytes_per_launch")
+    return e
 
 
 # ------------------------------------------------------------------ workloads
-def forward_case(name, dev):
+def forward_case(name, dev, sets=1):
+    """Causal (or gated) forward over `sets` independent input sets, one set per step in turn."""
     w = synth.WORKLOADS[name]
-    q, k, v = (x.to(dev) for x in synth.qkv(w))
-    a = synth.alpha(w).to(dev) if w.gated else None
+    data = []
+    for i in range(sets):
+        wi = w if i == 0 else synth.Workload(w.name, w.B, w.H, w.N, w.Dk, w.Dv, w.dtype, w.seed + 7919 * i,
+                                             w.q_scale, w.k_scale, w.v_scale, w.gated)
+        q, k, v = (x.to(dev) for x in synth.qkv(wi))
+        a = synth.alpha(wi).to(dev) if w.gated else None
+        data.append((q, k, v, a))
     kind = la.KIND_GATED if w.gated else la.KIND_FORWARD
     ws = torch.empty(max(1, la.workspace_size(kind, w.B, w.H, w.N, w.Dk, w.Dv, la.BF16)), dtype=torch.uint8,
                      device=dev)
     o = torch.empty((w.B, w.H, w.N, w.Dv), dtype=w.dtype, device=dev)
     s = torch.empty((w.B, w.H, w.Dk, w.Dv), dtype=torch.float32, device=dev)
     z = torch.empty((w.B, w.H, w.Dk), dtype=torch.float32, device=dev)
-    if w.gated:
-        def fn():
+    turn = [0]
+
+    def fn():
+        q, k, v, a = data[turn[0] % sets]
+        turn[0] += 1
+        if w.gated:
             la.linattn_forward_gated(q, k, v, a, out=o, s_final=s, z_final=z, workspace=ws)
-    else:
-        def fn():
+        else:
             la.linattn_forward(q, k, v, out=o, s_final=s, z_final=z, workspace=ws)
     nbytes = rf.forward_bytes(w.B, w.H, w.N, w.Dk, w.Dv, 2, gated=w.gated)
-    return w, fn, nbytes, (q, k, v, a)
+    return w, fn, nbytes, data[0]
 
 
 def backward_case(name, dev, inputs=None):
@@ -247,7 +278,7 @@ def decode_case(dev):
         s.copy_(s0)
         z.copy_(z0)
     nbytes = rf.decode_bytes(w.B, w.H, w.Dk, w.Dv, 2)
-    return w, fn, nbytes, reset
+    return w, fn, nbytes, reset, (q, k, v, s0, z0)
 
 
 def decode_lowp_case(dev, state_dtype):
@@ -273,38 +304,149 @@ def decode_prefix_gpu(w, b, dev):
 
 
 # ------------------------------------------------------------------ CPU baseline
-def cpu_baseline(w, q, k, v, budget_s=12.0):
-    """The fp64 oracle on a bounded sample of the workload: all heads, the first n tokens."""
-    import oracle
-    threads = max(1, min(16, os.cpu_count() or 1, w.B * w.H))
-    n = 256
+def host_cores():
+    """Threads the oracle may use here: OMP_NUM_THREADS if set (the GPU machine sets it to its per-GPU CPU
+    share), else the CPUs this process is allowed to run on."""
+    try:
+        allowed = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        allowed = os.cpu_count() or 1
+    env = os.environ.get("OMP_NUM_THREADS")
+    return max(1, min(allowed, int(env))) if env and env.isdigit() else allowed, allowed
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def host_info(threads, allowed):
+    return {"cores": threads, "host_logical_cpus": os.cpu_count(), "allowed_cpus": allowed,
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS"), "cpu_model": cpu_model()}
+
+
+def by_value_columns(q, k, v, parts):
+    """The same recurrences as extra heads: each head's value columns cut into `parts` blocks, q and k
+    repeated (o_t's columns depend on their own value columns and on the shared denominator only)."""
+    B, H, N, Dv = v.shape
+    cb = Dv // parts
+    qs = torch.cat([q] * parts, dim=1)
+    ks = torch.cat([k] * parts, dim=1)
+    vs = torch.cat([v[..., j * cb:(j + 1) * cb] for j in range(parts)], dim=1).contiguous()
+    return qs, ks, vs
+
+
+def bounded_sample(run, total, budget_s, first=256):
+    """Time run(n) on growing prefixes of n units until it takes a quarter of the budget (or covers all)."""
+    n = min(first, total)
     while True:
-        qs, ks, vs = (x[:, :, :n] for x in (q, k, v))
         t0 = time.perf_counter()
-        oracle.forward(qs, ks, vs, nthreads=threads)
+        run(n)
         dt = time.perf_counter() - t0
-        if dt > budget_s / 4 or n >= w.N:
-            break
-        n = min(w.N, int(n * max(2.0, min(16.0, budget_s / 2 / max(dt, 1e-3)))))
-    tokens = w.B * n
-    return {"value": tokens / dt / 1e6, "unit": "Mtokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"all {w.B * w.H} heads, first {n} of {w.N} tokens, fp64 recurrence (OpenMP over heads), "
-                      f"{dt:.1f} s"}
+        if dt > budget_s / 4 or n >= total:
+            return n, dt
+        n = min(total, int(n * max(2.0, min(16.0, budget_s / 2 / max(dt, 1e-3)))))
 
 
-# ------------------------------------------------------------------ main
+def cpu_baseline(w, q, k, v, budget_s=12.0):
+    """The fp64 oracle on a bounded sample of the workload: all heads, the first n tokens, every host
+    core this process may use (heads split further by value columns when there are more cores than heads)."""
+    import oracle
+    threads, allowed = host_cores()
+    parts = 1
+    while w.B * w.H * parts < threads and w.Dv % (2 * parts) == 0 and parts < 16:
+        parts *= 2
+
+    def run(n):
+        qs, ks, vs = (x[:, :, :n] for x in (q, k, v))
+        if parts > 1:
+            qs, ks, vs = by_value_columns(qs, ks, vs, parts)
+        oracle.forward(qs, ks, vs, nthreads=threads)
+    n, dt = bounded_sample(run, w.N, budget_s)
+    out = {"value": w.B * n / dt / 1e6, "unit": "Mtokens/s", "kind": "oracle",
+           "sample": f"all {w.B * w.H} heads{f' in {parts} value-column blocks' if parts > 1 else ''}, first {n} "
+                     f"of {w.N} tokens, fp64 recurrence (OpenMP over heads), {dt:.1f} s"}
+    out.update(host_info(threads, allowed))
+    return out
+
+
+def cpu_oracle_path(kind, w, inputs, budget_s=4.0):
+    """Short oracle timing of another path on a prefix of its workload: tokens (or steps) per second."""
+    import oracle
+    threads, allowed = host_cores()
+    if kind == "decode":
+        q, k, v, s0, z0 = (x.cpu() for x in inputs)
+        n, dt = bounded_sample(lambda m: oracle.decode_step(q[:m], k[:m], v[:m], s0[:m], z0[:m], nthreads=threads),
+                               w.B, budget_s, first=4)
+        # one new token for each of n sequences (all heads): n tokens per step
+        return {"value": n / dt / 1e6, "unit": "Mtokens/s", "sequences": n, "seconds": round(dt, 2),
+                "cores": threads, "kind": "oracle"}
+    q, k, v = (x.cpu() for x in inputs[:3])
+    a = inputs[3].cpu() if len(inputs) > 3 and inputs[3] is not None else None
+    fns = {
+        "forward": lambda n: oracle.forward(q[:, :, :n], k[:, :, :n], v[:, :, :n], alpha=None if a is None else
+                                            a[:, :, :n], nthreads=threads),
+        "noncausal": lambda n: oracle.noncausal(q[:, :, :n], k[:, :, :n], v[:, :, :n], nthreads=threads),
+        "delta": lambda n: oracle.delta(q[:, :, :n], k[:, :, :n], v[:, :, :n], nthreads=threads),
+    }
+    n, dt = bounded_sample(fns[kind], w.N, budget_s, first=64)
+    return {"value": w.B * n / dt / 1e6, "unit": "Mtokens/s", "tokens": w.B * n, "seconds": round(dt, 2),
+            "cores": threads, "kind": "oracle"}
+
+
+# ------------------------------------------------------------------ reporting
+def mfma_from_counters(c, avg_ms):
+    """MFMA work one launch issued, as the counters saw it: bf16 MFMA ops (512 flops each) over the launch
+    time against the bf16 peak, and the matrix cores' busy cycles over the launch's GPU cycles."""
+    if not c or c.get("mfma_mops_bf16") is None:
+        return None
+    flops = c["mfma_mops_bf16"] * 512
+    out = {"flops": flops, "tflops": round(flops / (avg_ms * 1e-3) / 1e12, 1),
+           "frac_of_bf16_peak": round(flops / (avg_ms * 1e-3) / rf.MFMA_BF16_FLOPS, 4)}
+    if c.get("mfma_busy_frac") is not None:
+        out["busy_frac"] = round(c["mfma_busy_frac"], 4)
+    return out
+
+
 def roofline_entry(kernel, avg_ms, nbytes, workload, flops=None):
     """nbytes: algorithmic bytes of ONE launch of this kernel."""
     achieved = nbytes / (avg_ms * 1e-3) / 1e9
     peak = rf.HBM_BYTES_PER_S / 1e9
-    tr = stored_traffic(kernel, workload)
+    c = stored_counters(kernel, workload)
     out = {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1), "peak": peak, "unit": "GB/s",
-           "frac": round(achieved / peak, 4), "traffic": tr, "algorithmic_bytes": nbytes,
-           "avg_ms": round(avg_ms, 4)}
+           "frac": round(achieved / peak, 4), "traffic": c.get("bytes_per_launch") if c else None,
+           "algorithmic_bytes": nbytes, "avg_ms": round(avg_ms, 4)}
     if flops is not None:
         out["mfma_tflops"] = round(flops / (avg_ms * 1e-3) / 1e12, 1)
         out["mfma_frac"] = round(flops / (avg_ms * 1e-3) / rf.MFMA_BF16_FLOPS, 4)
+    m = mfma_from_counters(c, avg_ms)
+    if m is not None:
+        out["mfma_util_counter"] = m
     return out
+
+
+def path_roofline_entry(ms, nbytes, kt, workload):
+    """The whole call: algorithmic bytes of one step over the step time; traffic = the counted HBM bytes
+    of every kernel the step launches (null unless every one of them was counted on the current sources)."""
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    peak = rf.HBM_BYTES_PER_S / 1e9
+    traffic = 0.0
+    for k, e in kt.items():
+        c = stored_counters(k, workload)
+        if c is None:
+            traffic = None
+            break
+        traffic += c["bytes_per_launch"] * e["launches_per_step"]
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": peak, "unit": "GB/s",
+            "frac": round(achieved / peak, 4), "traffic": None if traffic is None else int(traffic),
+            "traffic_over_algorithmic": None if traffic is None else round(traffic / nbytes, 3),
+            "algorithmic_bytes": nbytes}
 
 
 def copy_calibration(dev, steps):
@@ -318,6 +460,24 @@ def copy_calibration(dev, steps):
     print(json.dumps({"copy_bytes": n, "launches": steps}), flush=True)
 
 
+def path_entry(w, fn, nbytes, stream, args, tokens, reset=None, flops=None, key=None, kernel_nbytes=None):
+    ms = timed(fn, args.steps, args.warmup, stream)
+    if reset:
+        reset()
+    kt, prof_ms = kernel_times(fn, args.steps, stream)
+    if reset:
+        reset()
+    dom = max(kt, key=lambda n: kt[n]["avg_ms"] * kt[n]["launches_per_step"])
+    key = key or w.name
+    return {"workload": key, "ms_per_step": round(ms, 4), "Mtokens_per_s": round(tokens / (ms * 1e-3) / 1e6, 3),
+            "path_roofline_frac": round(rf.hbm_time_s(nbytes) / (ms * 1e-3), 4),
+            "path_roofline": path_roofline_entry(ms, nbytes, kt, key),
+            "roofline": roofline_entry(dom, kt[dom]["avg_ms"], kernel_nbytes or kernel_bytes(dom, w), key,
+                                       kernel_flops(dom, w, flops)),
+            "kernels_ms": {n: round(e["avg_ms"], 4) for n, e in kt.items()},
+            "profiled_ms_per_step": round(prof_ms, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -325,9 +485,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-paths", action="store_true")
-    ap.add_argument("--path", choices=["forward", "gated", "decode", "decode_bf16_state", "noncausal", "backward",
-                                       "snapshots", "delta"],
-                    default=None)
+    ap.add_argument("--path", choices=["forward", "c2", "gated", "decode", "decode_bf16_state", "noncausal",
+                                       "backward", "snapshots", "delta"], default=None)
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -341,17 +500,17 @@ def main():
         copy_calibration(dev, args.steps)
         return
 
-    if args.path in ("decode", "decode_bf16_state", "gated", "noncausal", "backward", "snapshots", "delta"):
+    if args.path not in (None, "forward"):
         # single-path run (used for counter collection); prints its own line
-        run_single_path(args, dev, stream)
+        print(json.dumps(single_path(args.path, args, dev, stream)), flush=True)
         return
 
     log(f"[bench] building inputs for {HEADLINE}")
     w, fn, nbytes, (q, k, v, _) = forward_case(HEADLINE, dev)
     log(f"[bench] warmup {args.warmup}, timing {args.steps} steps")
     ms = timed(fn, args.steps, args.warmup, stream)
-    kt = kernel_times(fn, args.steps)
-    dom = max(kt, key=lambda n: kt[n]["avg_ms"] * kt[n]["launches"])
+    kt, prof_ms = kernel_times(fn, args.steps, stream)
+    dom = max(kt, key=lambda n: kt[n]["avg_ms"] * kt[n]["launches_per_step"])
     flops = rf.chunked_flops(w.B, w.H, w.N, w.Dk, w.Dv, 64)
     tokens = w.B * w.N
     value = tokens / (ms * 1e-3) / 1e6
@@ -362,8 +521,11 @@ def main():
         "config": {"workload": HEADLINE, "B": w.B, "H": w.H, "N": w.N, "Dk": w.Dk, "Dv": w.Dv,
                    "inputs": "bf16 N(0,1)/sqrt(128) for q, k, v; fp32 state; eps 1e-6"},
         "roofline": roofline_entry(dom, kt[dom]["avg_ms"], kernel_bytes(dom, w), HEADLINE, flops),
+        "path_roofline": path_roofline_entry(ms, nbytes, kt, HEADLINE),
         "path_roofline_frac": round(rf.hbm_time_s(nbytes) / (ms * 1e-3), 4),
         "kernels_ms": {n: round(e["avg_ms"], 4) for n, e in kt.items()},
+        "profiled_ms_per_step": round(prof_ms, 4),
+        "counters_source_hash": kernel_source_hash(),
     }
     log(f"[bench] forward {ms:.3f} ms/step, {value:.1f} Mtok/s")
     if not args.no_paths:
@@ -376,85 +538,66 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def path_entry(w, fn, nbytes, stream, args, tokens, reset=None, flops=None, key=None, kernel_nbytes=None):
-    ms = timed(fn, args.steps, args.warmup, stream)
-    if reset:
-        reset()
-    kt = kernel_times(fn, args.steps)
-    if reset:
-        reset()
-    dom = max(kt, key=lambda n: kt[n]["avg_ms"] * kt[n]["launches"])
-    key = key or w.name
-    return {"workload": key, "ms_per_step": round(ms, 4), "Mtokens_per_s": round(tokens / (ms * 1e-3) / 1e6, 3),
-            "path_roofline_frac": round(rf.hbm_time_s(nbytes) / (ms * 1e-3), 4),
-            "roofline": roofline_entry(dom, kt[dom]["avg_ms"], kernel_nbytes or kernel_bytes(dom, w), key,
-                                       kernel_flops(dom, w, flops)),
-            "kernels_ms": {n: round(e["avg_ms"], 4) for n, e in kt.items()}}
+def single_path(name, args, dev, stream, headline_inputs=None, cpu=False):
+    """One path's entry (and, with cpu=True, a short oracle timing on its workload)."""
+    if name == "c2":
+        w, fn, nbytes, first = forward_case("b4h8_n4096_d64", dev, sets=C2_INPUT_SETS)
+        r = path_entry(w, fn, nbytes, stream, args, w.B * w.N,
+                       flops=rf.chunked_flops(w.B, w.H, w.N, w.Dk, w.Dv, 64))
+        r["input_sets"] = f"{C2_INPUT_SETS} sets in turn, {C2_INPUT_SETS * nbytes / 1e6:.0f} MB (Infinity Cache 256 MB)"
+        cpu_in, cpu_kind = first, "forward"
+    elif name == "gated":
+        w, fn, nbytes, first = forward_case("gated_b2h16_n16384_d128", dev)
+        r = path_entry(w, fn, nbytes, stream, args, w.B * w.N,
+                       flops=rf.chunked_flops(w.B, w.H, w.N, w.Dk, w.Dv, 64))
+        cpu_in, cpu_kind = first, "forward"
+    elif name == "decode":
+        w, fn, nbytes, reset, dec_in = decode_case(dev)
+        r = path_entry(w, fn, nbytes, stream, args, w.B, reset=reset)
+        r["steps_per_s"] = round(1e3 / r["ms_per_step"], 1)
+        cpu_in, cpu_kind = dec_in, "decode"
+    elif name == "decode_bf16_state":
+        w, fn, nbytes, reset = decode_lowp_case(dev, torch.bfloat16)
+        r = path_entry(w, fn, nbytes, stream, args, w.B, reset=reset, key="decode_bf16_state", kernel_nbytes=nbytes)
+        r["steps_per_s"] = round(1e3 / r["ms_per_step"], 1)
+        cpu = False
+    elif name == "noncausal":
+        w, fn, nbytes = noncausal_case(HEADLINE, dev, headline_inputs)
+        r = path_entry(w, fn, nbytes, stream, args, w.B * w.N, key="noncausal_" + w.name)
+        cpu_in, cpu_kind = headline_inputs, "noncausal"
+    elif name == "snapshots":
+        w, fn, nbytes, _ = snapshots_case(HEADLINE, dev, headline_inputs)
+        r = path_entry(w, fn, nbytes, stream, args, w.B * w.N, key="snapshots_" + w.name)
+        r["positions"] = SNAP_POSITIONS
+        cpu = False
+    elif name == "backward":
+        w, fn, nbytes = backward_case(HEADLINE, dev, headline_inputs)
+        r = path_entry(w, fn, nbytes, stream, args, w.B * w.N, key="backward_" + w.name,
+                       flops=rf.backward_flops(w.B, w.H, w.N, w.Dk, w.Dv))
+        cpu = False
+    elif name == "delta":
+        w, fn, nbytes = delta_case("delta_b16h16_n4096_d128", dev)
+        r = path_entry(w, fn, nbytes, stream, args, w.B * w.N, flops=rf.delta_flops(w.B, w.H, w.N, w.Dk, w.Dv))
+        cpu = False
+    else:
+        raise ValueError(name)
+    del fn
+    if cpu and cpu_in is not None:
+        r["cpu_oracle"] = cpu_oracle_path(cpu_kind, w, cpu_in)
+        r["gpu_over_oracle"] = round(r["Mtokens_per_s"] / r["cpu_oracle"]["value"], 1)
+    return r
 
 
 def other_paths(args, dev, stream, headline_inputs):
     out = {}
-    log("[bench] gated forward")
-    w, fn, nbytes, _ = forward_case("gated_b2h16_n16384_d128", dev)
-    out["gated"] = path_entry(w, fn, nbytes, stream, args, w.B * w.N,
-                              flops=rf.chunked_flops(w.B, w.H, w.N, w.Dk, w.Dv, 64))
-    del fn
-    log("[bench] decode step")
-    w, fn, nbytes, reset = decode_case(dev)
-    out["decode"] = path_entry(w, fn, nbytes, stream, args, w.B, reset=reset)
-    out["decode"]["steps_per_s"] = round(1e3 / out["decode"]["ms_per_step"], 1)
-    del fn
-    log("[bench] decode step, bf16 state")
-    w, fn, nbytes, reset = decode_lowp_case(dev, torch.bfloat16)
-    out["decode_bf16_state"] = path_entry(w, fn, nbytes, stream, args, w.B, reset=reset, key="decode_bf16_state",
-                                          kernel_nbytes=nbytes)
-    out["decode_bf16_state"]["steps_per_s"] = round(1e3 / out["decode_bf16_state"]["ms_per_step"], 1)
-    del fn
-    log("[bench] non-causal form")
-    w, fn, nbytes = noncausal_case(HEADLINE, dev, headline_inputs)
-    out["noncausal"] = path_entry(w, fn, nbytes, stream, args, w.B * w.N, key="noncausal_" + w.name)
-    del fn
-    log("[bench] forward with state snapshots")
-    w, fn, nbytes, pos = snapshots_case(HEADLINE, dev, headline_inputs)
-    out["snapshots"] = path_entry(w, fn, nbytes, stream, args, w.B * w.N, key="snapshots_" + w.name)
-    out["snapshots"]["positions"] = SNAP_POSITIONS
-    del fn
-    log("[bench] backward")
-    w, fn, nbytes = backward_case(HEADLINE, dev, headline_inputs)
-    out["backward"] = path_entry(w, fn, nbytes, stream, args, w.B * w.N, key="backward_" + w.name,
-                                 flops=rf.backward_flops(w.B, w.H, w.N, w.Dk, w.Dv))
-    del fn
-    log("[bench] delta rule")
-    w, fn, nbytes = delta_case("delta_b16h16_n4096_d128", dev)
-    out["delta"] = path_entry(w, fn, nbytes, stream, args, w.B * w.N,
-                              flops=rf.delta_flops(w.B, w.H, w.N, w.Dk, w.Dv))
+    cpu = not args.no_cpu_baseline
+    for key, name in (("b4h8_n4096_d64", "c2"), ("gated", "gated"), ("decode", "decode"),
+                      ("decode_bf16_state", "decode_bf16_state"), ("noncausal", "noncausal"),
+                      ("snapshots", "snapshots"), ("backward", "backward"), ("delta", "delta")):
+        log(f"[bench] {key}")
+        out[key] = single_path(name, args, dev, stream, headline_inputs, cpu=cpu)
+        torch.cuda.empty_cache()
     return out
-
-
-def run_single_path(args, dev, stream):
-    if args.path == "gated":
-        w, fn, nbytes, _ = forward_case("gated_b2h16_n16384_d128", dev)
-        r = path_entry(w, fn, nbytes, stream, args, w.B * w.N)
-    elif args.path == "decode":
-        w, fn, nbytes, reset = decode_case(dev)
-        r = path_entry(w, fn, nbytes, stream, args, w.B, reset=reset)
-    elif args.path == "decode_bf16_state":
-        w, fn, nbytes, reset = decode_lowp_case(dev, torch.bfloat16)
-        r = path_entry(w, fn, nbytes, stream, args, w.B, reset=reset, key="decode_bf16_state", kernel_nbytes=nbytes)
-    elif args.path == "delta":
-        w, fn, nbytes = delta_case("delta_b16h16_n4096_d128", dev)
-        r = path_entry(w, fn, nbytes, stream, args, w.B * w.N, flops=rf.delta_flops(w.B, w.H, w.N, w.Dk, w.Dv))
-    elif args.path == "snapshots":
-        w, fn, nbytes, _ = snapshots_case(HEADLINE, dev)
-        r = path_entry(w, fn, nbytes, stream, args, w.B * w.N, key="snapshots_" + w.name)
-    elif args.path == "backward":
-        w, fn, nbytes = backward_case(HEADLINE, dev)
-        r = path_entry(w, fn, nbytes, stream, args, w.B * w.N, key="backward_" + w.name,
-                       flops=rf.backward_flops(w.B, w.H, w.N, w.Dk, w.Dv))
-    else:
-        w, fn, nbytes = noncausal_case(HEADLINE, dev)
-        r = path_entry(w, fn, nbytes, stream, args, w.B * w.N, key="noncausal_" + w.name)
-    print(json.dumps(r), flush=True)
 
 
 if __name__ == "__main__":

@@ -12,7 +12,16 @@ dq is a difference of two terms that cancel along phi(q): phi(q_t) . dphi(q_t)
 exact dq there is eps-sized.  Each dq row's reference size is therefore floored
 by the size of one of the two terms it is the difference of, |dd_t z_t phi'(q_t)|
 (dd_t = -(dO_t . o_t) / den_t, z_t the running key sum), formed from the
-oracle's forward.  Shapes span several chunks and segments (the reverse segment
+oracle's forward.  A dk row is a double sum,
+phi'(k_t) sum_{u >= t} phi(q_u) sum_j dY_u,j (v_t,j - o_u,j), whose columns
+share every scalar factor (phi(q) is near one): the whole row can be a sum of
+products of either sign that ends near zero (at the last token it is a single
+dot product over the value columns), and its rounding error scales with the
+products, not with the row.  Each dk row is therefore floored by the
+root-sum-square of those products (parity.dk_term_size; a dropped or doubled
+chunk of 64 tokens is still about 15x above that floor at 2e-2).  dv rows have
+independent columns and are compared plainly.  Every gradient must also meet
+the tolerance head-normwise.  Shapes span several chunks and segments (the reverse segment
 sums), ragged tails, both head dims and their mix.  Sequences of one token get
 their own test: there every row of dq and dk is eps-sized.
 """
@@ -23,7 +32,7 @@ import torch
 import oracle
 from linear_attention_phi_amd import binding as la
 from linear_attention_phi_amd import synth
-from parity import TOL, assert_close, dq_term_size, head_rel_err
+from parity import TOL, assert_close, dk_term_size, dq_term_size
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -55,9 +64,10 @@ def check(q, k, v, g, phi=la.PHI_ELU1, s0=None, z0=None):
     ro, _, _ = oracle.forward(q, k, v, s0, z0, phi_mode=phi)
     tol = TOL[torch.bfloat16]
     for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
-        print(f"  {name}: per-head error {head_rel_err(got, ref):.3e} (information)")
+        assert_close(f"{name} heads", got, ref, tol, per="head")
     assert_close("dq rows (floored by the term size)", dq, rq, tol, floor=dq_term_size(q, k, g, ro, s0, z0, phi))
-    assert_close("dk rows", dk, rk, tol)
+    assert_close("dk rows (floored by the terms' root-sum-square)", dk, rk, tol,
+                 floor=dk_term_size(q, k, v, g, ro, s0, z0, phi))
     assert_close("dv rows", dv, rv, tol)
 
 
