@@ -60,6 +60,8 @@ extern "C" {
 
 #define LINATTN_ABI_VERSION 3
 #define LINATTN_MAX_SNAPSHOTS 256
+/* Bytes of the fixed device scratch of linattn_forward_noalloc (48 MiB). */
+#define LINATTN_NOALLOC_SCRATCH_BYTES 50331648u
 
 enum linattn_dtype { LINATTN_F32 = 0, LINATTN_BF16 = 1, LINATTN_FP8_E4M3 = 2 /* state storage only */ };
 enum linattn_phi { LINATTN_PHI_ELU1 = 0, LINATTN_PHI_IDENTITY = 1 };
@@ -122,6 +124,36 @@ int linattn_forward_gated(const void *q, const void *k, const void *v,
                           int B, int H, int N, int Dk, int Dv, int dtype,
                           int phi, float eps, void *workspace,
                           size_t workspace_bytes, void *hip_stream);
+
+/*
+ * linattn_forward for callers that cannot allocate device memory: code under
+ * HIP graph capture, serving loops and harnesses that forbid allocation.  It
+ * takes no workspace and calls no hipMalloc, hipFree or other allocating
+ * routine; the segment states that linattn_forward keeps in the workspace
+ * live in a fixed device array inside the library of
+ * LINATTN_NOALLOC_SCRATCH_BYTES (one per GPU, held from the library's first
+ * use on that GPU until the process ends).  The caller still passes every
+ * input and output, as for linattn_forward.
+ *
+ * - Sizes whose linattn_workspace_size(LINATTN_KIND_FORWARD, ...) exceeds
+ *   LINATTN_NOALLOC_SCRATCH_BYTES are rejected with LINATTN_EWORKSPACE before
+ *   anything runs (the 131072-token, 16-head, Dk = Dv = 128 case needs 35 MB).
+ * - Every call on one GPU uses that GPU's one array, and the array keeps the
+ *   last call's contents (nothing in it needs to start cleared: every state
+ *   cell is written before it is read).  Calls that overlap in time on one GPU
+ *   (on different streams, or from different host threads without ordering)
+ *   race on it: the caller serializes them.
+ * - The GPU is the one the stream belongs to (the current device for the
+ *   NULL stream); the array's address there is looked up on the first call
+ *   and kept.  LINATTN_ELAUNCH if that lookup fails.
+ * - These launches are not recorded by linattn_profile_enable.
+ * Results are identical to linattn_forward's on the same arguments.
+ */
+int linattn_forward_noalloc(const void *q, const void *k, const void *v, void *o,
+                            const float *s_init, const float *z_init,
+                            float *s_final, float *z_final,
+                            int B, int H, int N, int Dk, int Dv, int dtype, int phi,
+                            float eps, void *hip_stream);
 
 /*
  * Causal forward (gated when alpha is non-NULL) with the split of each

@@ -38,6 +38,7 @@ _SZ = ctypes.c_size_t
 SIGNATURES = {
     "linattn_forward": ([_P] * 8 + [_I] * 7 + [_F, _P, _SZ, _P], _I),
     "linattn_forward_gated": ([_P] * 9 + [_I] * 7 + [_F, _P, _SZ, _P], _I),
+    "linattn_forward_noalloc": ([_P] * 8 + [_I] * 7 + [_F, _P], _I),
     "linattn_forward_planned": ([_P] * 9 + [_I] * 7 + [_F, _I, _I, _P, _SZ, _P], _I),
     "linattn_forward_train": ([_P] * 9 + [_I] * 7 + [_F, _P, _SZ, _P], _I),
     "linattn_backward": ([_P] * 10 + [_I] * 7 + [_F, _P, _SZ, _P], _I),
@@ -184,6 +185,38 @@ def linattn_forward_planned(q, k, v, segments, subsegments, alpha=None, s_init=N
     segments of `subsegments` state parts each -> (o, s_final, z_final)."""
     return _forward((int(segments), int(subsegments)), q, k, v, alpha, s_init, z_init, eps, phi, want_state, out,
                     s_final, z_final, workspace)
+
+
+NOALLOC_SCRATCH_BYTES = 48 << 20
+
+
+def linattn_forward_noalloc(q, k, v, s_init=None, z_init=None, *, eps=1e-6, phi=PHI_ELU1, out=None,
+                            s_final=None, z_final=None):
+    """linattn_forward without a workspace: the library's fixed device scratch holds the segment states.
+
+    The C call allocates nothing; pass ``out`` (and ``s_final``, ``z_final``
+    to receive the state) to allocate nothing here either.  Calls that overlap
+    in time on one GPU share the scratch and race.  Raises if the sizes need
+    more than NOALLOC_SCRATCH_BYTES of segment states.
+    """
+    (B, H, N, Dk, Dv, code), specs = _qkv_specs(q, k, v)
+    _pair(s_init, z_init, "s_init and z_init")
+    _pair(s_final, z_final, "s_final and z_final")
+    need = workspace_size(KIND_FORWARD, B, H, N, Dk, Dv, code)
+    if need > NOALLOC_SCRATCH_BYTES:
+        raise ValueError(f"these sizes need {need} bytes of segment states; the fixed scratch holds "
+                         f"{NOALLOC_SCRATCH_BYTES} (use linattn_forward with a workspace)")
+    _validate(specs + [(s_init, "s_init", (B, H, Dk, Dv), torch.float32),
+                       (z_init, "z_init", (B, H, Dk), torch.float32),
+                       (out, "out", (B, H, N, Dv), q.dtype),
+                       (s_final, "s_final", (B, H, Dk, Dv), torch.float32),
+                       (z_final, "z_final", (B, H, Dk), torch.float32)])
+    o = out if out is not None else torch.empty((B, H, N, Dv), dtype=q.dtype, device=q.device)
+    rc = lib().linattn_forward_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(s_init), _ptr(z_init),
+                                       _ptr(s_final), _ptr(z_final), B, H, N, Dk, Dv, code, phi, float(eps),
+                                       _stream(q))
+    _check(rc, "linattn_forward_noalloc")
+    return o, s_final, z_final
 
 
 def _forward(plan, q, k, v, alpha, s_init, z_init, eps, phi, want_state, out, s_final, z_final, workspace):

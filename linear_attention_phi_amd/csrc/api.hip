@@ -20,6 +20,13 @@
 
 using namespace linattn;
 
+// Fixed device scratch of linattn_forward_noalloc (the segment states that
+// linattn_forward keeps in the caller's workspace).  Each GPU the library runs
+// on holds its own copy until the process ends.  Host code never passes the
+// array's name to a kernel: its device address on the current GPU comes from
+// hipGetSymbolAddress (noalloc_scratch below).
+static __device__ __align__(256) unsigned char scratch[LINATTN_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 // ------------------------------------------------------------------ plan
@@ -117,17 +124,22 @@ hipEvent_t prof_event() {
     return g_events[g_event_next++];
 }
 
+// Set while linattn_forward_noalloc runs on this thread: its launches take
+// no part in the timing record (which would create events).
+thread_local bool t_noalloc = false;
+
 // Launch helper: records an event pair around the launch while profiling.
 template <typename F> int launch(const char *name, hipStream_t st, F &&fn) {
     ProfRec rec{name, nullptr, nullptr};
-    if (g_prof_on) {
+    const bool prof = g_prof_on && !t_noalloc;
+    if (prof) {
         rec.a = prof_event();
         rec.b = prof_event();
         if (rec.a) hipEventRecord(rec.a, st);
     }
     fn();
     const hipError_t err = hipGetLastError();
-    if (g_prof_on && rec.a && rec.b) {
+    if (prof && rec.a && rec.b) {
         hipEventRecord(rec.b, st);
         g_prof.push_back(rec);
     }
@@ -139,6 +151,32 @@ template <typename F> int launch(const char *name, hipStream_t st, F &&fn) {
         const int rc_ = (x);                                                                                           \
         if (rc_ != LINATTN_OK) return rc_;                                                                             \
     } while (0)
+
+// ------------------------------------------------------------------ no-alloc scratch
+// Device address of `scratch` on the GPU the stream belongs to, looked up once
+// per device with that device current, and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+int noalloc_scratch(hipStream_t st, void **out) {
+    int dev = -1;
+    if (st ? hipStreamGetDevice(st, &dev) != hipSuccess : hipGetDevice(&dev) != hipSuccess) return LINATTN_ELAUNCH;
+    if (dev < 0 || dev >= kMaxDevices) return LINATTN_ELAUNCH;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = -1;
+        if (hipGetDevice(&cur) != hipSuccess) return LINATTN_ELAUNCH;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) return LINATTN_ELAUNCH;
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev && hipSetDevice(cur) != hipSuccess) return LINATTN_ELAUNCH;
+        if (e != hipSuccess || !p) return LINATTN_ELAUNCH;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return LINATTN_OK;
+}
 
 // ------------------------------------------------------------------ checks
 bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
@@ -562,6 +600,23 @@ size_t linattn_workspace_size_planned(int kind, int B, int H, int N, int Dk, int
     if (segments < 1 || subsegments < 1) return 0;
     if (check_common(B, H, N, Dk, Dv, dtype, LINATTN_PHI_ELU1, 0.f) != LINATTN_OK) return 0;
     return make_plan(kind, B, H, N, Dk, Dv, dtype, segments, subsegments).ws_bytes;
+}
+
+int linattn_forward_noalloc(const void *q, const void *k, const void *v, void *o, const float *s_init,
+                            const float *z_init, float *s_final, float *z_final, int B, int H, int N, int Dk, int Dv,
+                            int dtype, int phi, float eps, void *hip_stream) {
+    LA_TRY(check_common(B, H, N, Dk, Dv, dtype, phi, eps));
+    if (!q || !k || !v || !o) return LINATTN_EINVAL;
+    const Plan pl = make_plan(LINATTN_KIND_FORWARD, B, H, N, Dk, Dv, dtype);
+    if (pl.ws_bytes > (size_t)LINATTN_NOALLOC_SCRATCH_BYTES) return LINATTN_EWORKSPACE;
+    void *ws = nullptr;
+    if (pl.ws_bytes) LA_TRY(noalloc_scratch((hipStream_t)hip_stream, &ws));
+    // the segment states are written before they are read: nothing to clear
+    t_noalloc = true;
+    const int rc = forward_impl(false, q, k, v, nullptr, o, s_init, z_init, s_final, z_final, B, H, N, Dk, Dv, dtype,
+                                phi, eps, ws, pl.ws_bytes ? (size_t)LINATTN_NOALLOC_SCRATCH_BYTES : 0, hip_stream);
+    t_noalloc = false;
+    return rc;
 }
 
 // The training forward and the backward run the chunked bf16 kernels only.

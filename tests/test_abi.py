@@ -315,3 +315,35 @@ def test_snapshots_reject_bad_arguments(L):
     assert snaps(L, ss=None) == EINVAL
     assert snaps(L, ss=FAKE[0]) == EINVAL                           # s_snap overlaps q
     assert snaps(L, zs=FAKE[6]) == EINVAL                           # z_snap overlaps s_snap
+
+
+def noalloc(L, q=FAKE[0], k=FAKE[1], v=FAKE[2], o=FAKE[3], si=None, zi=None, sf=None, zf=None, B=1, H=1, N=64,
+            Dk=16, Dv=16, dtype=0, phi=0, eps=1e-6):
+    return L.linattn_forward_noalloc(q, k, v, o, si, zi, sf, zf, B, H, N, Dk, Dv, dtype, phi, eps, None)
+
+
+def test_noalloc_forward_rejects_bad_arguments_and_oversized_calls(L):
+    assert noalloc(L, q=None) == EINVAL
+    assert noalloc(L, o=None) == EINVAL
+    assert noalloc(L, B=0) == EINVAL
+    assert noalloc(L, Dk=48) == ESHAPE
+    assert noalloc(L, dtype=5) == EDTYPE
+    assert noalloc(L, si=FAKE[4]) == EINVAL            # s_init without z_init
+    assert noalloc(L, o=FAKE[0]) == EINVAL             # o overlaps q
+    # fp32 over 65536 tokens of one 128-dim head runs 1024 segments: 64.6 MiB of
+    # segment states, more than the fixed 48 MiB scratch -> refused, nothing runs
+    need = L.linattn_workspace_size(0, 1, 1, 65536, 128, 128, 0)
+    assert need > 48 << 20
+    assert noalloc(L, N=65536, Dk=128, Dv=128) == EWORKSPACE
+    # the long bf16 workload fits
+    assert L.linattn_workspace_size(0, 1, 16, 131072, 128, 128, 1) <= 48 << 20
+    assert b.NOALLOC_SCRATCH_BYTES == 48 << 20
+    m = re.search(r"#define LINATTN_NOALLOC_SCRATCH_BYTES (\d+)u", open(HEADER).read())
+    assert int(m.group(1)) == b.NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_binding_refuses_oversized_calls_before_any_launch():
+    import torch
+    q = torch.zeros(1, 1, 65536, 128)
+    with pytest.raises(ValueError, match="scratch"):
+        b.linattn_forward_noalloc(q, q, q)
