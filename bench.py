@@ -168,13 +168,14 @@ def backward_case(name, dev, inputs=None):
     w = synth.WORKLOADS[name]
     q, k, v = inputs if inputs is not None else (x.to(dev) for x in synth.qkv(w))
     g = synth.dout(w).to(dev)
-    _, den, _, _ = la.linattn_forward_train(q, k, v)
+    # the training forward's den and segment states (untimed), as a training step keeps them
+    _, den, _, _, saved = la.linattn_forward_train(q, k, v)
     ws = torch.empty(la.workspace_size(la.KIND_BACKWARD, w.B, w.H, w.N, w.Dk, w.Dv, la.BF16), dtype=torch.uint8,
                      device=dev)
     out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
 
     def fn():
-        la.linattn_backward(q, k, v, den, g, out=out, workspace=ws)
+        la.linattn_backward(q, k, v, den, g, saved=saved, out=out, workspace=ws)
     return w, fn, rf.backward_bytes(w.B, w.H, w.N, w.Dk, w.Dv, 2)
 
 

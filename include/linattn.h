@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define LINATTN_ABI_VERSION 3
+#define LINATTN_ABI_VERSION 4
 #define LINATTN_MAX_SNAPSHOTS 256
 /* Bytes of the fixed device scratch of linattn_forward_noalloc (48 MiB). */
 #define LINATTN_NOALLOC_SCRATCH_BYTES 50331648u
@@ -69,7 +69,8 @@ enum linattn_kind {
     LINATTN_KIND_FORWARD = 0,
     LINATTN_KIND_GATED = 1,
     LINATTN_KIND_NONCAUSAL = 2,
-    LINATTN_KIND_BACKWARD = 3
+    LINATTN_KIND_BACKWARD = 3,
+    LINATTN_KIND_TRAIN = 4 /* linattn_forward_train: its segment states, kept for linattn_backward */
 };
 
 enum linattn_status {
@@ -193,9 +194,18 @@ int linattn_forward_planned(const void *q, const void *k, const void *v,
  *   den       output [B][H][N] fp32.
  * o and den are required; den must not overlap q, k, v or o.
  * Restricted to the chunked bf16 path: dtype LINATTN_BF16 with Dk and Dv in
- * {64, 128} (LINATTN_ESHAPE / LINATTN_EDTYPE otherwise).  Other arguments and
- * the workspace (kind LINATTN_KIND_FORWARD) as linattn_forward; o is
- * identical to what linattn_forward writes.
+ * {64, 128} (LINATTN_ESHAPE / LINATTN_EDTYPE otherwise).  Other arguments as
+ * linattn_forward.  o is the same quantity as linattn_forward's; the segment
+ * states are summed in the backward's form (for elu + 1, elu(k) v^T, elu(k)
+ * and v apart, so that bf16 keeps elu's bits), so the two may differ in the
+ * last bit of a few outputs.
+ *
+ *   workspace  at least linattn_workspace_size(LINATTN_KIND_TRAIN, ...)
+ *              bytes (may be NULL when that is 0).  On return it holds the
+ *              forward state at the start of each segment of the sequence
+ *              (S, z and the running sum of v, fp32): pass it, unchanged, as
+ *              `saved` to linattn_backward on the same inputs, and the backward
+ *              does not recompute them.
  */
 int linattn_forward_train(const void *q, const void *k, const void *v, void *o,
                           float *den, const float *s_init, const float *z_init,
@@ -216,6 +226,11 @@ int linattn_forward_train(const void *q, const void *k, const void *v, void *o,
  *
  *   q, k, v   the forward's inputs; den its output from linattn_forward_train
  *             ([B][H][N] fp32) on the same inputs and initial state.
+ *   saved     NULL, or that linattn_forward_train call's workspace, unchanged
+ *             since (same q, k, v, s_init, z_init, phi and sizes): the segment
+ *             states are then read from it instead of being recomputed (one
+ *             pass over K and V less).  Must not overlap the outputs or the
+ *             workspace.
  *   dout      [B][H][N][Dv], dtype `dtype`.
  *   dq, dk    outputs [B][H][N][Dk]; dv output [B][H][N][Dv]; dtype `dtype`
  *             (bf16 round-to-nearest-even).  Must not overlap any input or
@@ -231,7 +246,7 @@ int linattn_forward_train(const void *q, const void *k, const void *v, void *o,
  * Workspace kind LINATTN_KIND_BACKWARD (always needed: it holds dd).
  */
 int linattn_backward(const void *q, const void *k, const void *v,
-                     const float *den, const void *dout,
+                     const float *den, const void *saved, const void *dout,
                      void *dq, void *dk, void *dv,
                      const float *s_init, const float *z_init,
                      int B, int H, int N, int Dk, int Dv, int dtype, int phi,

@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(_HERE, "liblinattn.so")
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
 PHI_ELU1, PHI_IDENTITY = 0, 1
-KIND_FORWARD, KIND_GATED, KIND_NONCAUSAL, KIND_BACKWARD = 0, 1, 2, 3
+KIND_FORWARD, KIND_GATED, KIND_NONCAUSAL, KIND_BACKWARD, KIND_TRAIN = 0, 1, 2, 3, 4
 
 _lib = None
 _lock = threading.Lock()
@@ -41,7 +41,7 @@ SIGNATURES = {
     "linattn_forward_noalloc": ([_P] * 8 + [_I] * 7 + [_F, _P], _I),
     "linattn_forward_planned": ([_P] * 9 + [_I] * 7 + [_F, _I, _I, _P, _SZ, _P], _I),
     "linattn_forward_train": ([_P] * 9 + [_I] * 7 + [_F, _P, _SZ, _P], _I),
-    "linattn_backward": ([_P] * 10 + [_I] * 7 + [_F, _P, _SZ, _P], _I),
+    "linattn_backward": ([_P] * 11 + [_I] * 7 + [_F, _P, _SZ, _P], _I),
     "linattn_decode_step_lowp": ([_P] * 5 + [_I] + [_P] * 2 + [_I] * 6 + [_F, _P], _I),
     "linattn_forward_delta": ([_P] * 8 + [_I] * 7 + [_P], _I),
     "linattn_forward_snapshots": ([_P] * 10 + [_I] + [_P] * 2 + [_I] * 7 + [_F, _P, _SZ, _P], _I),
@@ -261,9 +261,11 @@ def _forward(plan, q, k, v, alpha, s_init, z_init, eps, phi, want_state, out, s_
 
 
 def linattn_forward_train(q, k, v, s_init=None, z_init=None, *, eps=1e-6, phi=PHI_ELU1, workspace=None):
-    """Causal forward that also keeps each token's denominator -> (o, den, s_final, z_final).
+    """Causal forward that also keeps each token's denominator -> (o, den, s_final, z_final, saved).
 
-    bf16 with Dk, Dv in {64, 128}; den [B, H, N] fp32 feeds linattn_backward.
+    bf16 with Dk, Dv in {64, 128}; den [B, H, N] fp32 feeds linattn_backward,
+    and so may ``saved`` (the workspace, which then holds the forward state at
+    every segment start; pass it to linattn_backward unchanged).
     """
     (B, H, N, Dk, Dv, code), specs = _qkv_specs(q, k, v)
     _pair(s_init, z_init, "s_init and z_init")
@@ -273,20 +275,21 @@ def linattn_forward_train(q, k, v, s_init=None, z_init=None, *, eps=1e-6, phi=PH
     den = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     s_final = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device)
     z_final = torch.empty((B, H, Dk), dtype=torch.float32, device=q.device)
-    ws = _workspace(workspace_size(KIND_FORWARD, B, H, N, Dk, Dv, code), q.device, workspace)
+    ws = _workspace(workspace_size(KIND_TRAIN, B, H, N, Dk, Dv, code), q.device, workspace)
     rc = lib().linattn_forward_train(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(den), _ptr(s_init), _ptr(z_init),
                                      _ptr(s_final), _ptr(z_final), B, H, N, Dk, Dv, code, phi, float(eps), _ptr(ws),
                                      _ws_bytes(ws), _stream(q))
     _check(rc, "linattn_forward_train")
-    return o, den, s_final, z_final
+    return o, den, s_final, z_final, ws
 
 
-def linattn_backward(q, k, v, den, dout, s_init=None, z_init=None, *, eps=1e-6, phi=PHI_ELU1, out=None,
-                     workspace=None):
+def linattn_backward(q, k, v, den, dout, s_init=None, z_init=None, *, saved=None, eps=1e-6, phi=PHI_ELU1,
+                     out=None, workspace=None):
     """Gradients of a loss through the causal forward, given dout = dL/dO -> (dq, dk, dv).
 
     den is the output of linattn_forward_train on the same q, k, v (and
-    initial state, eps, phi).  ``out`` may pass preallocated (dq, dk, dv).
+    initial state, eps, phi); ``saved``, its workspace (optional: without it
+    the segment states are recomputed).  ``out`` may pass preallocated (dq, dk, dv).
     """
     (B, H, N, Dk, Dv, code), specs = _qkv_specs(q, k, v)
     _pair(s_init, z_init, "s_init and z_init")
@@ -300,10 +303,16 @@ def linattn_backward(q, k, v, den, dout, s_init=None, z_init=None, *, eps=1e-6, 
                        (dv, "dv", (B, H, N, Dv), q.dtype)])
     if den is None or dout is None:
         raise ValueError("den and dout are required")
+    if saved is not None:
+        need = workspace_size(KIND_TRAIN, B, H, N, Dk, Dv, code)
+        if not isinstance(saved, torch.Tensor) or saved.numel() * saved.element_size() < need:
+            raise ValueError(f"saved must be the training forward's workspace ({need} bytes)")
+        _validate([(saved, "saved", tuple(saved.shape), None)])
     if out is None:
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws = _workspace(workspace_size(KIND_BACKWARD, B, H, N, Dk, Dv, code), q.device, workspace)
-    rc = lib().linattn_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(den), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+    rc = lib().linattn_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(den), _ptr(saved), _ptr(dout), _ptr(dq), _ptr(dk),
+                                _ptr(dv),
                                 _ptr(s_init), _ptr(z_init), B, H, N, Dk, Dv, code, phi, float(eps), _ptr(ws),
                                 _ws_bytes(ws), _stream(q))
     _check(rc, "linattn_backward")

@@ -94,8 +94,10 @@ Plan make_plan(int kind, int B, int H, int N, int Dk, int Dv, int dtype, int seg
     const bool backward = kind == LINATTN_KIND_BACKWARD;
     const bool need_states = kind == LINATTN_KIND_NONCAUSAL || p.P > 1;
     // the backward keeps the forward's segment states (cells of Eb floats),
-    // then the reverse sums of the later segments, then dd of every token
-    if (need_states) p.ws_states = align256((size_t)BH * p.Ps * (backward ? p.Eb : p.E) * sizeof(float));
+    // then the reverse sums of the later segments, then dd of every token; the
+    // training forward's cells also carry the column sums of V (Eb floats)
+    const bool wide = backward || kind == LINATTN_KIND_TRAIN;
+    if (need_states) p.ws_states = align256((size_t)BH * p.Ps * (wide ? p.Eb : p.E) * sizeof(float));
     if (backward && p.P > 1) p.ws_rev = align256((size_t)BH * p.Ps * p.E * sizeof(float));
     if (backward) p.ws_dd = align256((size_t)BH * N * sizeof(float));
     if (kind == LINATTN_KIND_GATED && p.P > 1) p.ws_gam = align256((size_t)BH * p.Ps * sizeof(float));
@@ -223,11 +225,15 @@ template <int DK, int DV, bool GATED>
 int run_mfma_causal(const Plan &pl, const void *q, const void *k, const void *v, const float *alpha, void *o,
                     const float *s_init, const float *z_init, float *s_final, float *z_final, float *den,
                     const SnapRequest *snap, int BH, int N, int phi, float eps, char *ws, hipStream_t st) {
-    const float *start = s_init, *start_z = z_init;
+    const float *start = s_init, *start_z = z_init, *start_vb = nullptr;
     size_t sbh = (size_t)DK * DV, sseg = 0, zbh = DK;
     if (pl.P > 1) {
         float *states = reinterpret_cast<float *>(ws);
         float *gam = GATED ? reinterpret_cast<float *>(ws + pl.ws_states) : nullptr;
+        // the training forward (den given) keeps its cells for the backward,
+        // with the column sums of V appended (cells of Eb floats)
+        const bool train = den != nullptr;
+        const size_t E = train ? pl.Eb : pl.E;
         // the sub-segments of the last output segment are never needed by
         // the output pass; snapshots use them all, so that every snapshot lies
         // between two cells, the last one being the state at the end
@@ -235,6 +241,17 @@ int run_mfma_causal(const Plan &pl, const void *q, const void *k, const void *v,
         LA_TRY(launch("seg_state_bf16", st, [&] {
             if constexpr (kEight<DK, DV>)
                 with_phi(phi, [&](auto PH) {
+                    if constexpr (!GATED) {
+                        if (train) {
+                            // the backward's form: for elu + 1, sums of elu(k) v^T
+                            // and elu(k) (full relative precision in bf16) and of v
+                            constexpr int FEAT = PH() == LINATTN_PHI_ELU1 ? kFeatElu : PH();
+                            seg_state8_bf16<DK, DV, false, FEAT, true><<<dim3(P_run * BH), dim3(kThreads8), 0, st>>>(
+                                (const uint16_t *)k, (const uint16_t *)v, alpha, states, gam, N, pl.Ps, P_run,
+                                pl.sub_len);
+                            return;
+                        }
+                    }
                     seg_state8_bf16<DK, DV, GATED, PH()><<<dim3(P_run * BH), dim3(kThreads8), 0, st>>>(
                         (const uint16_t *)k, (const uint16_t *)v, alpha, states, gam, N, pl.Ps, P_run, pl.sub_len);
                 });
@@ -242,9 +259,11 @@ int run_mfma_causal(const Plan &pl, const void *q, const void *k, const void *v,
                 seg_state_bf16<DK, DV, GATED><<<dim3(P_run * BH), dim3(kThreads), 0, st>>>(
                     (const uint16_t *)k, (const uint16_t *)v, alpha, states, gam, N, pl.Ps, P_run, pl.sub_len, phi);
         }));
+        // the output pass reads the cells at segment starts (every R-th);
+        // snapshots may start from any cell
         LA_TRY(launch("seg_prefix", st, [&] {
-            seg_prefix<<<dim3((unsigned)((pl.E + 255) / 256), BH), dim3(256), 0, st>>>(
-                states, gam, s_init, z_init, pl.Ps, P_run + 1, DK, DV, (int)pl.E);
+            seg_prefix<<<dim3((unsigned)((E + 255) / 256), BH), dim3(256), 0, st>>>(
+                states, gam, s_init, z_init, pl.Ps, P_run + 1, DK, DV, (int)E, snap ? 1 : pl.R);
         }));
         if (snap) {
             if constexpr (kEight<DK, DV>) {
@@ -260,9 +279,11 @@ int run_mfma_causal(const Plan &pl, const void *q, const void *k, const void *v,
         // output segment p starts from the prefix before state cell p * R
         start = states;
         start_z = states + (size_t)DK * DV;
-        sbh = (size_t)pl.Ps * pl.E;
-        sseg = (size_t)pl.R * pl.E;
-        zbh = (size_t)pl.Ps * pl.E;
+        // training cells for elu + 1: E, zeta and the column sums of V
+        if (train && phi == LINATTN_PHI_ELU1) start_vb = states + (size_t)DK * DV + DK;
+        sbh = (size_t)pl.Ps * E;
+        sseg = (size_t)pl.R * E;
+        zbh = (size_t)pl.Ps * E;
     }
     if (snap && pl.P == 1) {
         // one segment: every snapshot runs from the initial state at token 0
@@ -284,11 +305,12 @@ int run_mfma_causal(const Plan &pl, const void *q, const void *k, const void *v,
                     if constexpr (!GATED)
                         fwd_out8_bf16<DK, DV, GATED, PH(), true><<<dim3(pl.P * BH), dim3(kThreads8), 0, st>>>(
                             (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, alpha, (uint16_t *)o,
-                            start, sbh, sseg, start_z, zbh, s_final, z_final, N, pl.P, pl.seg_len, eps, den);
+                            start, sbh, sseg, start_z, zbh, s_final, z_final, N, pl.P, pl.seg_len, eps, den,
+                            start_vb);
                 } else
                     fwd_out8_bf16<DK, DV, GATED, PH()><<<dim3(pl.P * BH), dim3(kThreads8), 0, st>>>(
                         (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, alpha, (uint16_t *)o, start,
-                        sbh, sseg, start_z, zbh, s_final, z_final, N, pl.P, pl.seg_len, eps, nullptr);
+                        sbh, sseg, start_z, zbh, s_final, z_final, N, pl.P, pl.seg_len, eps, nullptr, nullptr);
             });
         else
             fwd_out_bf16<DK, DV, GATED><<<dim3(pl.P * BH), dim3(kThreads), 0, st>>>(
@@ -334,8 +356,8 @@ int run_mfma_noncausal(const Plan &pl, const void *q, const void *k, const void 
 // dd) forward in time, reverse segment sums, dK / dV backward in time.
 template <int DK, int DV>
 int run_mfma_backward(const Plan &pl, const void *q, const void *k, const void *v, const float *den,
-                      const void *dout, void *dq, void *dk, void *dv, const float *s_init, const float *z_init,
-                      int BH, int N, int phi, float eps, char *ws, hipStream_t st) {
+                      const float *saved, const void *dout, void *dq, void *dk, void *dv, const float *s_init,
+                      const float *z_init, int BH, int N, int phi, float eps, char *ws, hipStream_t st) {
     if constexpr (!kEight<DK, DV>) {
         return LINATTN_ESHAPE;
     } else {
@@ -346,20 +368,26 @@ int run_mfma_backward(const Plan &pl, const void *q, const void *k, const void *
         size_t sbh = (size_t)DK * DV, sseg = 0, zbh = DK;
         float *rev = nullptr;
         if (pl.P > 1) {
-            float *states = reinterpret_cast<float *>(ws);
+            const float *states = saved;
             rev = reinterpret_cast<float *>(ws + pl.ws_states);
             const int P_run = (pl.P - 1) * pl.R;
-            LA_TRY(launch("seg_state_bf16", st, [&] {
-                with_phi(phi, [&](auto PH) {
-                    constexpr int FEAT = PH() == LINATTN_PHI_ELU1 ? kFeatElu : PH();
-                    seg_state8_bf16<DK, DV, false, FEAT, true><<<dim3(P_run * BH), dim3(kThreads8), 0, st>>>(
-                        k16, v16, nullptr, states, nullptr, N, pl.Ps, P_run, pl.sub_len);
-                });
-            }));
-            LA_TRY(launch("seg_prefix", st, [&] {
-                seg_prefix<<<dim3((unsigned)((pl.Eb + 255) / 256), BH), dim3(256), 0, st>>>(
-                    states, nullptr, s_init, z_init, pl.Ps, P_run + 1, DK, DV, (int)pl.Eb);
-            }));
+            if (!saved) {
+                float *cells = reinterpret_cast<float *>(ws);
+                LA_TRY(launch("seg_state_bf16", st, [&] {
+                    with_phi(phi, [&](auto PH) {
+                        constexpr int FEAT = PH() == LINATTN_PHI_ELU1 ? kFeatElu : PH();
+                        seg_state8_bf16<DK, DV, false, FEAT, true><<<dim3(P_run * BH), dim3(kThreads8), 0, st>>>(
+                            k16, v16, nullptr, cells, nullptr, N, pl.Ps, P_run, pl.sub_len);
+                    });
+                }));
+                LA_TRY(launch("seg_prefix", st, [&] {
+                    seg_prefix<<<dim3((unsigned)((pl.Eb + 255) / 256), BH), dim3(256), 0, st>>>(
+                        cells, nullptr, s_init, z_init, pl.Ps, P_run + 1, DK, DV, (int)pl.Eb, pl.R);
+                }));
+                states = cells;
+            }
+            // else: the training forward's prefix cells, of the same plan and
+            // in the same form (E, zeta, column sums of V)
             start = states;
             start_z = states + (size_t)DK * DV;
             start_vb = states + (size_t)DK * DV + DK;
@@ -423,7 +451,7 @@ int run_recur_causal(const Plan &pl, const void *q, const void *k, const void *v
         }));
         LA_TRY(launch("seg_prefix", st, [&] {
             seg_prefix<<<dim3((unsigned)((E + 255) / 256), BH), dim3(256), 0, st>>>(states, gam, s_init, z_init, pl.P,
-                                                                                    pl.P, DK, Dv, (int)E);
+                                                                                    pl.P, DK, Dv, (int)E, 1);
         }));
         start = states;
         start_z = states + (size_t)DK * Dv;
@@ -504,7 +532,7 @@ int forward_impl(bool gated, const void *q, const void *k, const void *v, const 
                  const float *s_init, const float *z_init, float *s_final, float *z_final, int B, int H, int N,
                  int Dk, int Dv, int dtype, int phi, float eps, void *workspace, size_t workspace_bytes,
                  void *hip_stream, float *den = nullptr, const SnapRequest *snap = nullptr, int seg_req = 0,
-                 int sub_req = 0) {
+                 int sub_req = 0, int kind = -1) {
     LA_TRY(check_common(B, H, N, Dk, Dv, dtype, phi, eps));
     if (!q || !k || !v || !o || (gated && !alpha)) return LINATTN_EINVAL;
     if ((s_init == nullptr) != (z_init == nullptr)) return LINATTN_EINVAL;
@@ -512,8 +540,8 @@ int forward_impl(bool gated, const void *q, const void *k, const void *v, const 
     const size_t es = dtype == LINATTN_BF16 ? 2 : 4;
     const size_t nq = (size_t)B * H * N * Dk * es, nv = (size_t)B * H * N * Dv * es;
     if (overlaps(o, nv, q, nq) || overlaps(o, nv, k, nq) || overlaps(o, nv, v, nv)) return LINATTN_EINVAL;
-    const Plan pl =
-        make_plan(gated ? LINATTN_KIND_GATED : LINATTN_KIND_FORWARD, B, H, N, Dk, Dv, dtype, seg_req, sub_req);
+    if (kind < 0) kind = gated ? LINATTN_KIND_GATED : LINATTN_KIND_FORWARD;
+    const Plan pl = make_plan(kind, B, H, N, Dk, Dv, dtype, seg_req, sub_req);
     if (pl.ws_bytes && (!workspace || workspace_bytes < pl.ws_bytes)) return LINATTN_EWORKSPACE;
     hipStream_t st = (hipStream_t)hip_stream;
     char *ws = (char *)workspace;
@@ -637,7 +665,7 @@ int linattn_forward_train(const void *q, const void *k, const void *v, void *o, 
     if (overlaps(den, nd, q, nq) || overlaps(den, nd, k, nq) || overlaps(den, nd, v, nv) || overlaps(den, nd, o, nv))
         return LINATTN_EINVAL;
     return forward_impl(false, q, k, v, nullptr, o, s_init, z_init, s_final, z_final, B, H, N, Dk, Dv, dtype, phi,
-                        eps, workspace, workspace_bytes, hip_stream, den);
+                        eps, workspace, workspace_bytes, hip_stream, den, nullptr, 0, 0, LINATTN_KIND_TRAIN);
 }
 
 int linattn_forward_delta(const void *q, const void *k, const void *v, const float *alpha, const float *beta,
@@ -710,29 +738,31 @@ int linattn_forward_snapshots(const void *q, const void *k, const void *v, const
                         dtype, phi, eps, workspace, workspace_bytes, hip_stream, nullptr, &req);
 }
 
-int linattn_backward(const void *q, const void *k, const void *v, const float *den, const void *dout, void *dq,
-                     void *dk, void *dv, const float *s_init, const float *z_init, int B, int H, int N, int Dk,
-                     int Dv, int dtype, int phi, float eps, void *workspace, size_t workspace_bytes,
-                     void *hip_stream) {
+int linattn_backward(const void *q, const void *k, const void *v, const float *den, const void *saved,
+                     const void *dout, void *dq, void *dk, void *dv, const float *s_init, const float *z_init, int B,
+                     int H, int N, int Dk, int Dv, int dtype, int phi, float eps, void *workspace,
+                     size_t workspace_bytes, void *hip_stream) {
     LA_TRY(check_common(B, H, N, Dk, Dv, dtype, phi, eps));
     LA_TRY(check_train(Dk, Dv, dtype));
     if (!q || !k || !v || !den || !dout || !dq || !dk || !dv) return LINATTN_EINVAL;
     if ((s_init == nullptr) != (z_init == nullptr)) return LINATTN_EINVAL;
     const size_t nq = (size_t)B * H * N * Dk * 2, nv = (size_t)B * H * N * Dv * 2, nd = (size_t)B * H * N * 4;
-    const void *ins[5] = {q, k, v, den, dout};
-    const size_t insz[5] = {nq, nq, nv, nd, nv};
+    const size_t ns = make_plan(LINATTN_KIND_TRAIN, B, H, N, Dk, Dv, dtype).ws_bytes;
+    const void *ins[6] = {q, k, v, den, dout, saved};
+    const size_t insz[6] = {nq, nq, nv, nd, nv, ns};
     void *outs[3] = {dq, dk, dv};
     const size_t outsz[3] = {nq, nq, nv};
     for (int a = 0; a < 3; ++a) {
-        for (int b = 0; b < 5; ++b)
+        for (int b = 0; b < 6; ++b)
             if (overlaps(outs[a], outsz[a], ins[b], insz[b])) return LINATTN_EINVAL;
         for (int b = a + 1; b < 3; ++b)
             if (overlaps(outs[a], outsz[a], outs[b], outsz[b])) return LINATTN_EINVAL;
     }
     const Plan pl = make_plan(LINATTN_KIND_BACKWARD, B, H, N, Dk, Dv, dtype);
     if (!workspace || workspace_bytes < pl.ws_bytes) return LINATTN_EWORKSPACE;
-    return by_dims_mfma<MfmaBackward>(Dk, Dv, pl, q, k, v, den, dout, dq, dk, dv, s_init, z_init, B * H, N, phi,
-                                      eps, (char *)workspace, (hipStream_t)hip_stream);
+    if (overlaps(workspace, workspace_bytes, saved, ns)) return LINATTN_EINVAL;
+    return by_dims_mfma<MfmaBackward>(Dk, Dv, pl, q, k, v, den, (const float *)saved, dout, dq, dk, dv, s_init,
+                                      z_init, B * H, N, phi, eps, (char *)workspace, (hipStream_t)hip_stream);
 }
 
 int linattn_forward_noncausal(const void *q, const void *k, const void *v, void *o, float *s_out, float *z_out,
@@ -806,7 +836,7 @@ int linattn_decode_step_lowp(const void *q, const void *k, const void *v, void *
 }
 
 size_t linattn_workspace_size(int kind, int B, int H, int N, int Dk, int Dv, int dtype) {
-    if (kind < LINATTN_KIND_FORWARD || kind > LINATTN_KIND_BACKWARD) return 0;
+    if (kind < LINATTN_KIND_FORWARD || kind > LINATTN_KIND_TRAIN) return 0;
     if (check_common(B, H, N, Dk, Dv, dtype, LINATTN_PHI_ELU1, 0.f) != LINATTN_OK) return 0;
     return make_plan(kind, B, H, N, Dk, Dv, dtype).ws_bytes;
 }

@@ -229,7 +229,8 @@ __device__ __forceinline__ bf16x8 dd_operand(const float *sDD, int ks, int G) {
 // as E = sum elu(k) v^T, zeta = sum elu(k), Vbar = sum v and the token count
 // (start: E, zeta and Vbar of the segment's prefix cell; Vbar sits after zeta
 // and start_vb may be null for zero); for the identity map E, zeta are S, z.
-// Writes dq and dd_out (dd of every token, for the reverse passes).
+// The training forward keeps its cells in this same form, so they serve as
+// they are.  Writes dq and dd_out (dd of every token, for the reverse passes).
 template <int DK, int DV, int PHI>
 __global__ __launch_bounds__(kThreads8, 1) void bwd_dq8_bf16(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,

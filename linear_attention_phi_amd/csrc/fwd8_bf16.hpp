@@ -493,13 +493,17 @@ __global__ __launch_bounds__(kThreads8, 4) void snap_state8_bf16(
 // Causal output pass (see fwd_out_bf16): wave w serves query block w / 2 and
 // half w % 2 of the value columns; the state tiles are split 2 x 4.  TRAIN:
 // also keep, for the backward, each token's denominator phi(q).z + eps
-// (den_out).
+// (den_out).  start_vb non-null (training, elu + 1): the start cells hold the
+// backward's form, E = sum elu(k) v^T and zeta = sum elu(k) (plus any initial
+// state), with the column sums of V at start_vb; the state is then
+// S = E + 1 Vbar^T, z = zeta + n 1, n the tokens before the segment.
 template <int DK, int DV, bool GATED, int PHI, bool TRAIN = false>
 __global__ __launch_bounds__(kThreads8, 1) void fwd_out8_bf16(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const float *__restrict__ alpha, uint16_t *__restrict__ o, const float *__restrict__ start, size_t start_stride_bh,
     size_t start_stride_seg, const float *__restrict__ start_z, size_t start_z_stride_bh, float *__restrict__ s_final,
-    float *__restrict__ z_final, int N, int P, int seg_len, float eps, float *__restrict__ den_out) {
+    float *__restrict__ z_final, int N, int P, int seg_len, float eps, float *__restrict__ den_out,
+    const float *__restrict__ start_vb) {
     constexpr int phi_mode = PHI;
     using TK = Tile<DK>;
     using TV = Tile<DV>;
@@ -540,6 +544,20 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd_out8_bf16(
         const float *s0 = start ? start + bh * start_stride_bh + seg * start_stride_seg : nullptr;
         const float *z0 = start_z ? start_z + bh * start_z_stride_bh + seg * start_stride_seg : nullptr;
         state8_load<DK, DV>(st, s0, z0, w, lane);
+        if (TRAIN && start_vb) {
+            using S8 = State8<DK, DV>;
+            const float *vb0 = start_vb + bh * start_z_stride_bh + seg * start_stride_seg;
+            const int nt0 = (w & 3) * S8::NTW;
+#pragma unroll
+            for (int mi = 0; mi < S8::MTW; ++mi) {
+#pragma unroll
+                for (int ni = 0; ni < S8::NTW; ++ni) {
+                    const float4 vb = *reinterpret_cast<const float4 *>(vb0 + 16 * (nt0 + ni) + 4 * g);
+                    st.s[mi][ni] += f32x4{vb.x, vb.y, vb.z, vb.w};
+                }
+            }
+            if (S8::has_z(w)) st.z += (float)t_begin;
+        }
         state8_z_to_lds<DK, DV>(st, sZr, w, lane);
     }
     state8_to_lds<DK, DV>(st, sS, w, lane);

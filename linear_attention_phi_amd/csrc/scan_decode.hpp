@@ -15,13 +15,14 @@ namespace linattn {
 // G_p S_{<p} + dS_p where G_p is the product of segment p's gates.
 // The order over segments is fixed, so the result is bitwise reproducible.
 // Grid: x = element blocks of 256, y = bh.
-// Cells 0..cells-2 hold segment states on entry; cells 0..cells-1 receive the
-// prefix (cell p gets the state before segment p).  P is the number of cells
-// per (b, h); a cell is E floats (S, z, then any further sums, which start
-// from zero).
+// Cells 0..cells-2 hold segment states on entry; cells p = 0, every, 2 every,
+// ... (and the last, cells - 1) receive the prefix (cell p gets the state
+// before segment p); the others are left as they were.  P is the number of
+// cells per (b, h); a cell is E floats (S, z, then any further sums, which
+// start from zero).
 __global__ __launch_bounds__(256) void seg_prefix(float *__restrict__ ws, const float *__restrict__ gam,
                                                   const float *__restrict__ s_init, const float *__restrict__ z_init,
-                                                  int P, int cells, int DK, int DV, int E) {
+                                                  int P, int cells, int DK, int DV, int E, int every) {
     const int e = blockIdx.x * 256 + threadIdx.x;
     const int bh = blockIdx.y;
     if (e >= E) return;
@@ -45,7 +46,7 @@ __global__ __launch_bounds__(256) void seg_prefix(float *__restrict__ ws, const 
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
             if (j < nb) {
-                cell[(size_t)(p0 + j) * E] = run;
+                if ((p0 + j) % every == 0) cell[(size_t)(p0 + j) * E] = run;
                 run = gb ? fmaf(gm[j], run, d[j]) : run + d[j];
             }
         }

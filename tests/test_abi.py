@@ -75,8 +75,11 @@ def test_workspace_size_is_host_arithmetic(L):
     # segment states, and dd of every token
     assert ws(3, 1, 16, 131072, 128, 128, 1) >= 16 * 2 * (16 * 2) * cell + 16 * 131072 * 4
     assert ws(3, 1, 1, 64, 64, 64, 1) >= 64 * 4  # dd even with one segment
+    # the training forward keeps its segment states with the column sums of V
+    assert ws(4, 1, 16, 131072, 128, 128, 1) >= 16 * (16 - 1) * 2 * (cell + 128 * 4)
+    assert ws(4, 1, 1, 64, 64, 64, 1) == 0       # one segment: nothing to keep
     # invalid arguments -> 0
-    assert ws(4, 1, 1, 64, 16, 16, 0) == 0
+    assert ws(5, 1, 1, 64, 16, 16, 0) == 0
     assert ws(0, 0, 1, 64, 16, 16, 0) == 0
     assert ws(0, 1, 1, 64, 48, 16, 0) == 0
     assert ws(0, 1, 1, 64, 16, 16, 7) == 0
@@ -249,8 +252,9 @@ def train(L, q=FAKE[0], k=FAKE[1], v=FAKE[2], o=FAKE[3], den=FAKE[4], B=1, H=1, 
 
 
 def bwd(L, q=FAKE[0], k=FAKE[1], v=FAKE[2], den=FAKE[4], g=FAKE[5], dq=FAKE[6], dk=FAKE[7], dv=FAKE[8], si=None,
-        zi=None, B=1, H=1, N=64, Dk=64, Dv=64, dtype=1, phi=0, eps=1e-6, ws=FAKE[10], wsb=1 << 20):
-    return L.linattn_backward(q, k, v, den, g, dq, dk, dv, si, zi, B, H, N, Dk, Dv, dtype, phi, eps, ws, wsb, None)
+        zi=None, B=1, H=1, N=64, Dk=64, Dv=64, dtype=1, phi=0, eps=1e-6, ws=FAKE[10], wsb=1 << 20, saved=None):
+    return L.linattn_backward(q, k, v, den, saved, g, dq, dk, dv, si, zi, B, H, N, Dk, Dv, dtype, phi, eps, ws, wsb,
+                              None)
 
 
 def test_training_forward_and_backward_reject_bad_arguments(L):
@@ -273,6 +277,12 @@ def test_training_forward_and_backward_reject_bad_arguments(L):
     assert bwd(L, dk=FAKE[6]) == EINVAL            # outputs overlap each other
     assert bwd(L, B=0) == EINVAL
     assert bwd(L, phi=5) == EDTYPE
+    # 8192 tokens on one head run many segments: the saved states are read, and
+    # must not overlap an output or the workspace
+    need = L.linattn_workspace_size(3, 1, 1, 8192, 64, 64, 1)
+    assert L.linattn_workspace_size(4, 1, 1, 8192, 64, 64, 1) > 0
+    assert bwd(L, N=8192, wsb=need, saved=FAKE[6]) == EINVAL
+    assert bwd(L, N=8192, wsb=need, saved=FAKE[10]) == EINVAL
     # long sequence on one head: segment states needed, workspace missing
     assert bwd(L, N=131072) == EWORKSPACE
     need = L.linattn_workspace_size(3, 1, 1, 131072, 64, 64, 1)

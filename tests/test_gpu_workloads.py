@@ -83,12 +83,12 @@ def test_backward_on_the_long_workload_sampled():
     g = synth.dout(w)
     stamp("GPU training forward and backward")
     d = [x.to(DEV) for x in (q, k, v, g)]
-    _, den, _, _ = la.linattn_forward_train(d[0], d[1], d[2])
-    dq, dk, dv = la.linattn_backward(d[0], d[1], d[2], den, d[3])
+    _, den, _, _, saved = la.linattn_forward_train(d[0], d[1], d[2])
+    dq, dk, dv = la.linattn_backward(d[0], d[1], d[2], den, d[3], saved=saved)
     torch.cuda.synchronize()
     hs = SPREAD_HEADS
     got = [x[:, hs].cpu() for x in (dq, dk, dv)]
-    del d, den, dq, dk, dv
+    del d, den, saved, dq, dk, dv
     stamp(f"oracle: gradients of heads {hs}")
     qh, kh, vh, gh = (x[:, hs] for x in (q, k, v, g))
     rq, rk, rv, _, _ = oracle.backward(qh, kh, vh, gh)
