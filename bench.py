@@ -24,7 +24,8 @@ Prints ONE JSON line:
 
 Also: ``--copy-calibration`` runs only a plain device copy of a known size
 (for scaling the FETCH_SIZE / WRITE_SIZE counters), ``--path`` runs a single
-workload (profiling runs).
+workload (profiling runs), ``--sweep-plans`` times the headline forward under
+other splits of the sequence and as head groups.
 """
 from __future__ import annotations
 
@@ -479,6 +480,39 @@ def path_entry(w, fn, nbytes, stream, args, tokens, reset=None, flops=None, key=
             "profiled_ms_per_step": round(prof_ms, 4)}
 
 
+def sweep_plans(dev, stream, steps, warmup):
+    """The headline forward under other splits of the sequence (linattn_forward_planned), and run as
+    head groups whose K, V (64 MB a head) fit the 256 MB Infinity Cache between their state and output
+    passes: per variant, ms per step and each kernel's ms per step."""
+    w = synth.WORKLOADS[HEADLINE]
+    q, k, v = (x.to(dev) for x in synth.qkv(w))
+    o = torch.empty_like(v)
+    s = torch.empty((w.B, w.H, w.Dk, w.Dv), dtype=torch.float32, device=dev)
+    z = torch.empty((w.B, w.H, w.Dk), dtype=torch.float32, device=dev)
+    ws = torch.empty(128 << 20, dtype=torch.uint8, device=dev)
+    out = {}
+
+    def record(name, fn):
+        ms = timed(fn, steps, warmup, stream)
+        kt, _ = kernel_times(fn, steps, stream)
+        out[name] = {"ms_per_step": round(ms, 4),
+                     "kernels_ms_per_step": {n: round(e["avg_ms"] * e["launches_per_step"], 4) for n, e in kt.items()}}
+        log(f"[sweep] {name}: {ms:.4f} ms")
+
+    record("library plan", lambda: la.linattn_forward(q, k, v, out=o, s_final=s, z_final=z, workspace=ws))
+    for P, R in [(8, 2), (8, 4), (16, 1), (16, 2), (16, 4), (32, 1), (32, 2)]:
+        record(f"{P} segments x {R} state parts",
+               lambda P=P, R=R: la.linattn_forward_planned(q, k, v, P, R, out=o, s_final=s, z_final=z, workspace=ws))
+    for G in (1, 2, 4):
+        parts = [tuple(x[:, h:h + G] for x in (q, k, v, o, s, z)) for h in range(0, w.H, G)]
+
+        def fn(parts=parts, P=256 // G):
+            for qq, kk, vv, oo, ss, zz in parts:
+                la.linattn_forward_planned(qq, kk, vv, P, 2, out=oo, s_final=ss, z_final=zz, workspace=ws)
+        record(f"head groups of {G} ({256 // G} segments x 2)", fn)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -489,6 +523,7 @@ def main():
     ap.add_argument("--path", choices=["forward", "c2", "gated", "decode", "decode_bf16_state", "noncausal",
                                        "backward", "snapshots", "delta"], default=None)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--sweep-plans", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one MI355X: the method is built and timed on a single GPU only; "
@@ -499,6 +534,10 @@ def main():
     stream = torch.cuda.current_stream(dev)
     if args.copy_calibration:
         copy_calibration(dev, args.steps)
+        return
+    if args.sweep_plans:
+        print(json.dumps({"workload": HEADLINE, "sweep": sweep_plans(dev, stream, args.steps, args.warmup)}),
+              flush=True)
         return
 
     if args.path not in (None, "forward"):
