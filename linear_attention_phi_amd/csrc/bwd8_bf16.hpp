@@ -447,6 +447,10 @@ __global__ __launch_bounds__(kThreads8, 1) void bwd_dq8_bf16(
             store_grad_rows<DK, NTK, kScalePhi, PHI>(acc, dh * NTK, sQ, tq,
                                                      dq + (row0 + (size_t)c * kChunk + tq) * DK, ok, g);
         };
+        // chunk_work holds one workgroup barrier (the dd exchange), reached by
+        // each wave through its own case; as in the delta rule, gfx950's
+        // s_barrier counts arriving waves whatever the instruction, and every
+        // case executes exactly one.
         switch (qblk_w) {
         case 0: chunk_work(std::integral_constant<int, 0>{}); break;
         case 1: chunk_work(std::integral_constant<int, 1>{}); break;

@@ -446,6 +446,14 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8_bf16(
             store_grad_rows<DV, NTV, kScaleNone, PHI>(acc, dh * NTV, nullptr, tq,
                                                       o + (row0 + (size_t)c * kChunk + tq) * DV, tq < valid, g);
         };
+        // chunk_rest holds the chunk's two workgroup barriers, and each wave
+        // reaches them through its own case: different s_barrier instructions
+        // per wave.  gfx950's s_barrier counts the waves that arrive at any
+        // barrier, not a program point, and every case executes exactly two,
+        // in the same order relative to the shared LDS traffic, so the waves
+        // meet as if at one barrier.  Splitting the phases so that the
+        // barriers sit outside the switch measured 2.6% slower (A/B, one
+        // process), so the specialization keeps them inside.
         switch (blk_w) {
         case 0: chunk_rest(std::integral_constant<int, 0>{}); break;
         case 1: chunk_rest(std::integral_constant<int, 1>{}); break;
