@@ -133,6 +133,18 @@ __device__ __forceinline__ float sum_over_groups(float v) {
 __device__ __forceinline__ float decay_between(float to_lsum, int to_zeros, float from_lsum, int from_zeros) {
     return to_zeros > from_zeros ? 0.f : __builtin_amdgcn_exp2f(to_lsum - from_lsum);
 }
+// The same decay from one number per token, kappa = lsum - kZeroShift * zeros
+// (both prefixes still scanned exactly, then combined): across a zero gate the
+// exponent is below -kZeroShift, far under the smallest float, so exp2 gives
+// exactly 0; between tokens with the same zero count the shift cancels, up to
+// the rounding of kappa (for z zeros, about 2^-23 * 256 z of the exponent:
+// 3e-5 relative in the decay per zero before the pair).  The exponent is
+// positive only for pairs out of causal order, which callers mask after the
+// product (it can overflow to inf there).
+constexpr float kZeroShift = 256.f;
+__device__ __forceinline__ float decay_k(float to_kappa, float from_kappa) {
+    return __builtin_amdgcn_exp2f(to_kappa - from_kappa);
+}
 __device__ __forceinline__ bool gate_is_zero(float a) { return a < 1.17549435e-38f; }  // NaN stays NaN
 __device__ __forceinline__ float gate_log2(float a) { return gate_is_zero(a) ? 0.f : __builtin_amdgcn_logf(a); }
 

@@ -345,22 +345,19 @@ __device__ __forceinline__ void range_state8(const uint16_t *__restrict__ k, con
     };
     auto step = [&](Buf &b, int c) {
         const int valid = rows_in(c);
-        float dC = 1.f;
+        float dC = 1.f, ke = 0.f;
         ChunkGates cg;
         if (GATED) {
             cg.build(b.a, lane < valid);
-            const float le = cg.lsum_at(valid - 1);
-            const int ze = cg.zeros_at(valid - 1);
-            dC = decay_between(le, ze, 0.f, 0);
-            seg_lsum += le;
-            seg_zeros += ze;
+            seg_lsum += cg.lsum_at(valid - 1);
+            seg_zeros += cg.zeros_at(valid - 1);
+            ke = cg.kappa_at(valid - 1);
+            dC = decay_k(ke, 0.f);
         }
 #pragma unroll
         for (int i = 0; i < Units<DK>::N; ++i) {
             const int row = Units<DK>::row_of(tid, i);
-            const float sc = GATED ? decay_between(cg.lsum_at(valid - 1), cg.zeros_at(valid - 1), cg.lsum_at(row),
-                                                   cg.zeros_at(row))
-                                   : 1.f;
+            const float sc = GATED ? decay_k(ke, cg.kappa_at(row)) : 1.f;
             uint4 plain, scaled;
             phi_pack8x2(b.k.r[i], phi_mode, sc, plain, scaled);
             *reinterpret_cast<uint4 *>(sK + Tile<DK>::off(row, Units<DK>::col_of(tid, i))) = GATED ? scaled : plain;
@@ -518,9 +515,8 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd_out8_bf16(
     // the denominator tile reads (a broadcast), so that tile holds phi(q).z.
     __shared__ __attribute__((aligned(16))) uint16_t sS[DK * DV];
     __shared__ __attribute__((aligned(16))) uint16_t sZr[DK];
-    // gated: the chunk's inclusive gate prefix (log2 sum, zero count) per token
-    __shared__ __attribute__((aligned(16))) float sGl[GATED ? kChunk : 4];
-    __shared__ __attribute__((aligned(16))) int sGz[GATED ? kChunk : 4];
+    // gated: the chunk's inclusive gate prefix per token, as kappa (decay_k)
+    __shared__ __attribute__((aligned(16))) float sGk[GATED ? kChunk : 4];
 
     const int seg = blockIdx.x % P, bh = blockIdx.x / P;
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
@@ -584,24 +580,19 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd_out8_bf16(
         const int valid = rows_in(c);
         // ---- stage: phi(Q), phi(K) (and decayed phi(K)), V, all row-major
         ChunkGates cg;
-        float dC = 1.f, le = 0.f;
-        int ze = 0;
+        float dC = 1.f, ke = 0.f;
         if (GATED) {
             cg.build(b.a, lane < valid);
-            le = cg.lsum_at(valid - 1);
-            ze = cg.zeros_at(valid - 1);
-            dC = decay_between(le, ze, 0.f, 0);
-            if (w == 0) {
-                sGl[lane] = cg.lsum;
-                sGz[lane] = cg.zeros;
-            }
+            ke = cg.kappa_at(valid - 1);
+            dC = decay_k(ke, 0.f);
+            if (w == 0) sGk[lane] = cg.kappa();
         }
 #pragma unroll
         for (int i = 0; i < Units<DK>::N; ++i) {
             const int row = Units<DK>::row_of(tid, i), col = Units<DK>::col_of(tid, i);
             *reinterpret_cast<uint4 *>(sQ + TK::off(row, col)) = phi_pack8(qbuf.r[i], phi_mode);
             if (GATED) {
-                const float sc = decay_between(le, ze, cg.lsum_at(row), cg.zeros_at(row));
+                const float sc = decay_k(ke, cg.kappa_at(row));
                 uint4 plain, scaled;
                 phi_pack8x2(b.k.r[i], phi_mode, sc, plain, scaled);
                 *reinterpret_cast<uint4 *>(sK + TK::off(row, col)) = plain;
@@ -643,29 +634,21 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd_out8_bf16(
                 }
             }
             const int tq = 16 * qblk + l16;
-            float lq = 0.f;
-            int zq = 0;
-            if (GATED) {
-                lq = sGl[tq];
-                zq = sGz[tq];
-            }
+            const float kq = GATED ? sGk[tq] : 0.f;
     #pragma unroll
             for (int kb4 = 0; kb4 < 4; ++kb4) {
                 if (kb4 <= qblk) {
-                    float4 lk = make_float4(0.f, 0.f, 0.f, 0.f);
-                    int4 zk = make_int4(0, 0, 0, 0);
-                    if (GATED) {
-                        lk = *reinterpret_cast<const float4 *>(sGl + 16 * kb4 + 4 * g);
-                        zk = *reinterpret_cast<const int4 *>(sGz + 16 * kb4 + 4 * g);
-                    }
-                    const float lka[4] = {lk.x, lk.y, lk.z, lk.w};
-                    const int zka[4] = {zk.x, zk.y, zk.z, zk.w};
+                    float4 kk = make_float4(0.f, 0.f, 0.f, 0.f);
+                    if (GATED) kk = *reinterpret_cast<const float4 *>(sGk + 16 * kb4 + 4 * g);
+                    const float kka[4] = {kk.x, kk.y, kk.z, kk.w};
     #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int tk = 16 * kb4 + 4 * g + i;
                         float s = sc[kb4][i];
+                        // the decay first: above the diagonal it may be inf, and
+                        // the mask then replaces the product
+                        if (GATED) s *= decay_k(kq, kka[i]);
                         if (kb4 == qblk && tk > tq) s = 0.f;
-                        if (GATED) s *= decay_between(lq, zq, lka[i], zka[i]);
                         sc[kb4][i] = s;
                     }
                 }
@@ -693,7 +676,7 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd_out8_bf16(
                 dt = mfma16x16x32(a, qa[ks], dt);
             }
             if (GATED) {
-                const float dq = decay_between(lq, zq, 0.f, 0);
+                const float dq = decay_k(kq, 0.f);
                 dt *= dq;
     #pragma unroll
                 for (int j = 0; j < NTO; ++j) oacc[j] *= dq;

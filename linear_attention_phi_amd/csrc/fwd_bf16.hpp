@@ -178,6 +178,9 @@ struct ChunkGates {
     }
     __device__ __forceinline__ float lsum_at(int t) const { return __shfl(lsum, t, 64); }
     __device__ __forceinline__ int zeros_at(int t) const { return __shfl(zeros, t, 64); }
+    // this lane's token as one number (see decay_k)
+    __device__ __forceinline__ float kappa() const { return lsum - kZeroShift * (float)zeros; }
+    __device__ __forceinline__ float kappa_at(int t) const { return __shfl(kappa(), t, 64); }
 };
 
 // ------------------------------------------------------------------ state MFMA
