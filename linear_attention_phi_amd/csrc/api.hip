@@ -395,22 +395,17 @@ int run_mfma_backward(const Plan &pl, const void *q, const void *k, const void *
             sseg = (size_t)pl.R * pl.Eb;
             zbh = (size_t)pl.Ps * pl.Eb;
         }
+        // dQ and dd; for P > 1 also the reverse sums of every state sub-segment
+        // past the first segment (cell j: sub-segment R + j)
         LA_TRY(launch("bwd_dq_bf16", st, [&] {
             with_phi(phi, [&](auto PH) {
                 bwd_dq8_bf16<DK, DV, PH()><<<dim3(pl.P * BH), dim3(kThreads8), 0, st>>>(
                     q16, k16, v16, den, g16, (uint16_t *)dq, dd, start, sbh, sseg, start_z, zbh, start_vb, N, pl.P,
-                    pl.seg_len, eps);
+                    pl.seg_len, eps, rev, (size_t)pl.Ps * pl.E, pl.R, pl.sub_len / kChunk);
             });
         }));
         if (pl.P > 1) {
-            // cell j: state sub-segment R + j (the first segment's are never needed)
             const int cells = (pl.P - 1) * pl.R;
-            LA_TRY(launch("bwd_rstate_bf16", st, [&] {
-                with_phi(phi, [&](auto PH) {
-                    bwd_rstate8_bf16<DK, DV, PH()><<<dim3(cells * BH), dim3(kThreads8), 0, st>>>(
-                        q16, den, dd, g16, rev, N, cells, pl.Ps, pl.R, pl.sub_len);
-                });
-            }));
             LA_TRY(launch("seg_suffix", st, [&] {
                 seg_suffix<<<dim3((unsigned)((pl.E + 255) / 256), BH), dim3(256), 0, st>>>(rev, pl.Ps, cells,
                                                                                           (int)pl.E);

@@ -16,11 +16,13 @@
 //   dphi(K)_c = V_c R_{c+1}^T + 1 r_{c+1}^T + triu(V_c dY_c^T + 1 dd_c^T) phi(Q)_c
 //   dV_c      = phi(K)_c R_{c+1} + triu(phi(K)_c phi(Q)_c^T) dY_c
 // (tril / triu over (query, key) with the diagonal included).  Passes: the
-// state pass gives the forward state at segment starts; bwd_dq8_bf16 runs
-// each segment forward in time and also writes dd; bwd_rstate8_bf16 sums R
-// and r over state sub-segments for a suffix over segments; bwd_dkv8_bf16
-// runs each segment backward in time.  dY is dO over the forward's saved
-// denominator, rounded to bf16 once; every pass uses that same dY.
+// state pass gives the forward state at segment starts (or the training
+// forward's saved cells serve); bwd_dq8_bf16 runs each segment forward in
+// time, writes dd, and sums R and r over each state sub-segment from the
+// phi(Q), dY and dd it has staged (for a suffix over segments);
+// bwd_dkv8_bf16 runs each segment backward in time.  dY is dO over the
+// forward's saved denominator, rounded to bf16 once; every pass uses that
+// same dY.
 //
 // Precision of dq.  dphi(q_t) = sum_j phi(k_j) (v_j - o_t) . dY_t satisfies
 // phi(q_t) . dphi(q_t) = 0 up to eps: for elu + 1 its part along the all-ones
@@ -45,11 +47,6 @@
 #include "fwd8_bf16.hpp"
 
 namespace linattn {
-
-// 4-byte buffer load (bounds-checked: 0 past the range).
-__device__ __forceinline__ float buffer_load_f32(rsrc_t rs, int voff) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, voff, 0, 0));
-}
 
 // The lane index, hidden from loop-invariant code motion: the per-lane LDS
 // addresses of a chunk's many operand reads are then recomputed inside the
@@ -179,10 +176,12 @@ __device__ __forceinline__ float dphi_of(float f) {
 
 // Store 16 rows x (2 * NTW) permuted tiles of a gradient, scaled by phi'
 // (from the staged tile given, per MODE): lane (g, l16) holds, for tile pair
-// p, the 8 consecutive columns 32 p + 8 g .. + 7 of row l16.
+// p, the 8 consecutive columns 32 p + 8 g .. + 7 of row l16.  out: the
+// chunk's output rows (row tile_row of them is this lane's), bounded to the
+// chunk's valid rows (stores past them are dropped).
 template <int D, int NTW, int MODE, int PHI>
 __device__ __forceinline__ void store_grad_rows(const f32x4 (&acc)[NTW], int nt0, const uint16_t *phi_tile,
-                                                int tile_row, uint16_t *out_row, bool ok, int g) {
+                                                int tile_row, rsrc_t out, int g) {
     constexpr bool SCALE = MODE != kScaleNone && !PHI;
 #pragma unroll
     for (int pp = 0; pp < NTW / 2; ++pp) {
@@ -202,14 +201,12 @@ __device__ __forceinline__ void store_grad_rows(const f32x4 (&acc)[NTW], int nt0
                 x[2 * e + 1] *= dphi_of<PHI, MODE>(bf_hi(fw[e]));
             }
         }
-        if (ok) {
-            uint4 u;
-            u.x = pack_bf16x2(x[0], x[1]);
-            u.y = pack_bf16x2(x[2], x[3]);
-            u.z = pack_bf16x2(x[4], x[5]);
-            u.w = pack_bf16x2(x[6], x[7]);
-            *reinterpret_cast<uint4 *>(out_row + 32 * p + 8 * g) = u;
-        }
+        uint4 u;
+        u.x = pack_bf16x2(x[0], x[1]);
+        u.y = pack_bf16x2(x[2], x[3]);
+        u.z = pack_bf16x2(x[4], x[5]);
+        u.w = pack_bf16x2(x[6], x[7]);
+        buffer_store16(u, out, (tile_row * D + 32 * p + 8 * g) * 2);
     }
 }
 
@@ -230,14 +227,19 @@ __device__ __forceinline__ bf16x8 dd_operand(const float *sDD, int ks, int G) {
 // (start: E, zeta and Vbar of the segment's prefix cell; Vbar sits after zeta
 // and start_vb may be null for zero); for the identity map E, zeta are S, z.
 // The training forward keeps its cells in this same form, so they serve as
-// they are.  Writes dq and dd_out (dd of every token, for the reverse passes).
+// they are.  Writes dq and dd_out (dd of every token, for the dK, dV pass).
+// With rev given, a segment p > 0 also sums, over each of its R state
+// sub-segments j (sub_chunks chunks each), dR = phi(Q)^T dY and dr = phi(Q)^T dd
+// from the phi(Q), dY and dd it has just staged, into the reverse cell
+// (p - 1) R + j at rev + bh rev_stride_bh (cells of Dk Dv + Dk floats, in the
+// layout of the forward's segment states); the first segment's are never needed.
 template <int DK, int DV, int PHI>
 __global__ __launch_bounds__(kThreads8, 1) void bwd_dq8_bf16(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const float *__restrict__ den, const uint16_t *__restrict__ dout, uint16_t *__restrict__ dq,
     float *__restrict__ dd_out, const float *__restrict__ start, size_t start_stride_bh, size_t start_stride_seg,
     const float *__restrict__ start_z, size_t start_z_stride_bh, const float *__restrict__ start_vb, int N, int P,
-    int seg_len, float eps) {
+    int seg_len, float eps, float *__restrict__ rev, size_t rev_stride_bh, int R, int sub_chunks) {
     using TK = Tile<DK>;
     using TV = Tile<DV>;
     constexpr bool KAPPA = PHI == 0; // elu + 1: the constant part is carried apart
@@ -245,16 +247,20 @@ __global__ __launch_bounds__(kThreads8, 1) void bwd_dq8_bf16(
     constexpr int FEAT = KAPPA ? kFeatElu : PHI;
     constexpr int KSV = DV / 32;     // k-steps over value dims
     constexpr int NTK = DK / 16 / 2; // key-dim tiles per wave
-    __shared__ __attribute__((aligned(16))) uint16_t sQ[kChunk * TK::RS]; // phi(q), bf16
+    // phi(q) (bf16), dY and dd in two buffers, by chunk parity: the reverse
+    // sums of a chunk read them after its closing barrier while the next
+    // chunk is staged into the other buffer
+    __shared__ __attribute__((aligned(16))) uint16_t sQ2[2][kChunk * TK::RS];
     __shared__ __attribute__((aligned(16))) uint16_t sK[kChunk * TK::RS]; // features of k (elu for elu + 1)
     __shared__ __attribute__((aligned(16))) uint16_t sV[kChunk * TV::RS];
-    __shared__ __attribute__((aligned(16))) uint16_t sDY[kChunk * TV::RS];
+    __shared__ __attribute__((aligned(16))) uint16_t sDY2[2][kChunk * TV::RS];
     __shared__ __attribute__((aligned(16))) float sSq[kChunk];      // sum_i phi(q_i) per row
     __shared__ __attribute__((aligned(16))) float sRed[2 * 2 * kChunk]; // per key-dim half: phi(q).(S dY), phi(q).zeta
     __shared__ __attribute__((aligned(16))) uint16_t sS[DK * DV];
     __shared__ __attribute__((aligned(16))) float sZf[DK];
     __shared__ __attribute__((aligned(16))) float sVb[KAPPA ? DV : 4];     // Vbar before the chunk
     __shared__ __attribute__((aligned(16))) float sVp[KAPPA ? 8 * DV : 4]; // the chunk's per-wave column sums
+    __shared__ __attribute__((aligned(16))) float sDD2[2][kChunk];
 
     const int seg = blockIdx.x % P, bh = blockIdx.x / P;
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
@@ -281,6 +287,15 @@ __global__ __launch_bounds__(kThreads8, 1) void bwd_dq8_bf16(
         if (State8<DK, DV>::has_z(w) && lane < 16) sZf[State8<DK, DV>::z_dk(w, lane)] = st.z[0];
     };
     state_to_lds();
+    // the reverse sums of this segment's state sub-segments (segment 0 has none)
+    const bool do_rev = rev != nullptr && seg > 0;
+    State8<DK, DV> rt;
+    state8_load<DK, DV>(rt, nullptr, nullptr, w, lane);
+    auto rev_store = [&](int j) {
+        float *dst = rev + bh * rev_stride_bh + ((size_t)(seg - 1) * R + j) * (size_t)(DK * DV + DK);
+        state8_store<DK, DV>(rt, dst, w, lane);
+        state8_store_z<DK, DV>(rt, dst + DK * DV, w, lane);
+    };
 
     // never negative: a sub-segment may start past the end of a ragged sequence
     auto rows_in = [&](int c) { return max(0, min(kChunk, t_end - t_begin - c * kChunk)); };
@@ -288,22 +303,48 @@ __global__ __launch_bounds__(kThreads8, 1) void bwd_dq8_bf16(
         const size_t r = row0 + (size_t)c * kChunk;
         b.load(q + r * DK, k + r * DK, v + r * DV, dout + r * DV, den + r, nullptr, rows_in(c), tid);
     };
-    // two chunks in flight: the loads for chunk c + 2 are issued while chunk c
-    // is worked on (the loop runs two chunks per pass so that each buffer
-    // stays in its own registers)
+    // DEPTH chunks of loads in flight: the loads for chunk c + DEPTH are issued
+    // while chunk c is worked on (with two, the loop runs two chunks per pass
+    // so that each buffer stays in its own registers).  At Dk = Dv = 128 the
+    // reverse sums' accumulators leave registers for one.
+    constexpr int DEPTH = DK * DV > 64 * 128 ? 1 : 2;
     BwdBuf<DK, DV, false> buf0, buf1;
-    if (nch > 0) issue(buf0, 0);
-    if (nch > 1) issue(buf1, 1);
-    auto step = [&](BwdBuf<DK, DV, false> &buf, const int c) {
-        const int valid = rows_in(c);
-        float vsum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    // the column sums of V over the staged chunk (the constant part's Vbar)
+    float vsum[8];
+    // chunk c's tiles into LDS from its buffer, which then takes the loads of
+    // chunk c + DEPTH.  The loop stages chunk c + 1 at the end of chunk c's
+    // step, after that step's stores: every path into a staging has the same
+    // stores after the loads it waits for, so the wait need not cover them.
+    auto stage = [&](BwdBuf<DK, DV, false> &buf, const int c) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vsum[e] = 0.f;
         if (KAPPA) {
 #pragma unroll
             for (int i = 0; i < Units<DV>::N; ++i) add_bf16x8(vsum, buf.v.r[i]);
         }
-        stage_dq<DK, DV, PHI, FEAT>(buf, sQ, sK, sV, sSq, tid);
-        stage_dy<DV>(buf.g, buf.den, buf.dd, sDY, nullptr, tid);
-        if (c + 2 < nch) issue(buf, c + 2);
+        stage_dq<DK, DV, PHI, FEAT>(buf, sQ2[c & 1], sK, sV, sSq, tid);
+        stage_dy<DV>(buf.g, buf.den, buf.dd, sDY2[c & 1], nullptr, tid);
+        // every read of the buffer before its refill: the loads then land in
+        // the buffer's own registers (a load moved above a read would need
+        // other registers and a copy back, which waits for it at once).  The
+        // refill is not under a branch (past the last chunk its descriptors
+        // cover no bytes and the loads read nothing), which would let reads of
+        // the buffer sink below it.
+        __builtin_amdgcn_sched_barrier(0);
+        issue(buf, c + DEPTH);
+    };
+    issue(buf0, 0);
+    if (DEPTH == 2) issue(buf1, 1);
+    if (nch > 0) stage(buf0, 0);
+    // next: the buffer that holds chunk c + 1
+    auto step = [&](BwdBuf<DK, DV, false> &next, const int c) {
+        uint16_t *const sQ = sQ2[c & 1];
+        uint16_t *const sDY = sDY2[c & 1];
+        float *const sDD = sDD2[c & 1];
+        const int valid = rows_in(c);
+        // the chunk's dq rows and dd, bounded to its valid rows
+        const size_t crow = row0 + (size_t)c * kChunk;
+        const rsrc_t rdq = chunk_rsrc(dq + crow * DK, valid * DK * 2), rdd = chunk_rsrc(dd_out + crow, valid * 4);
         __syncthreads();
         // tokens before this chunk (the constant part's count)
         const float n_prev = (float)(t_begin + c * kChunk);
@@ -319,12 +360,11 @@ __global__ __launch_bounds__(kThreads8, 1) void bwd_dq8_bf16(
             for (int ks = 0; ks < KSV; ++ks)
                 dya[ks] = *reinterpret_cast<const bf16x8 *>(sDY + TV::off(tq, 32 * ks + 8 * g));
             // G^T[key][query] = v_key . dY_query for key blocks 0..qblk, zero
-            // above the diagonal; mk: the causal mask itself
-            f32x4 gt[4], mk[4];
+            // above the diagonal
+            f32x4 gt[4];
 #pragma unroll
             for (int kb4 = 0; kb4 < 4; ++kb4) {
                 gt[kb4] = f32x4{0.f, 0.f, 0.f, 0.f};
-                mk[kb4] = f32x4{0.f, 0.f, 0.f, 0.f};
                 if (kb4 <= qblk) {
 #pragma unroll
                     for (int ks = 0; ks < KSV; ++ks)
@@ -338,7 +378,6 @@ __global__ __launch_bounds__(kThreads8, 1) void bwd_dq8_bf16(
                     for (int i = 0; i < 4; ++i) {
                         const bool keep = kb4 < qblk || 4 * g + i <= l16;
                         gt[kb4][i] = keep ? bf16_round(gt[kb4][i]) : 0.f;
-                        mk[kb4][i] = keep ? 1.f : 0.f;
                     }
                 }
             }
@@ -359,6 +398,28 @@ __global__ __launch_bounds__(kThreads8, 1) void bwd_dq8_bf16(
                 }
             }
             vdy = sum_over_groups(vdy);
+            // the B operands of the in-chunk products over key steps of 32: G^T
+            // (its values are already bf16) and the causal mask itself (bf16
+            // ones on and below the diagonal), formed here so that G's fp32
+            // accumulators are free before the state product below
+            bf16x8 gop[2], mop[2];
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                uint4 u, m;
+                u.x = pack_bf16x2(gt[2 * s2][0], gt[2 * s2][1]);
+                u.y = pack_bf16x2(gt[2 * s2][2], gt[2 * s2][3]);
+                u.z = pack_bf16x2(gt[2 * s2 + 1][0], gt[2 * s2 + 1][1]);
+                u.w = pack_bf16x2(gt[2 * s2 + 1][2], gt[2 * s2 + 1][3]);
+                auto one = [&](int kb4, int i) -> uint32_t {
+                    return kb4 < qblk || (kb4 == qblk && 4 * g + i <= l16) ? 0x3f80u : 0u;
+                };
+                m.x = one(2 * s2, 0) | one(2 * s2, 1) << 16;
+                m.y = one(2 * s2, 2) | one(2 * s2, 3) << 16;
+                m.z = one(2 * s2 + 1, 0) | one(2 * s2 + 1, 1) << 16;
+                m.w = one(2 * s2 + 1, 2) | one(2 * s2 + 1, 3) << 16;
+                gop[s2] = as_bf16x8(u);
+                mop[s2] = as_bf16x8(m);
+            }
 
             // A = E_t dY_t and zeta_t over this wave's key dims (tiles permuted as perm_dv)
             f32x4 acc[NTK], zt[NTK];
@@ -373,27 +434,18 @@ __global__ __launch_bounds__(kThreads8, 1) void bwd_dq8_bf16(
                 const float4 zf = *reinterpret_cast<const float4 *>(sZf + 32 * (nt >> 1) + 8 * g + 4 * (nt & 1));
                 zt[j] = f32x4{zf.x, zf.y, zf.z, zf.w};
             }
-            auto pack_b = [&](const f32x4(&x)[4], int s2) {
-                uint4 u;
-                u.x = pack_bf16x2(x[2 * s2][0], x[2 * s2][1]);
-                u.y = pack_bf16x2(x[2 * s2][2], x[2 * s2][3]);
-                u.z = pack_bf16x2(x[2 * s2 + 1][0], x[2 * s2 + 1][1]);
-                u.w = pack_bf16x2(x[2 * s2 + 1][2], x[2 * s2 + 1][3]);
-                return as_bf16x8(u);
-            };
             // in-chunk: feat(K)^T Gm^T and feat(K)^T M over key steps of 32
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
                 if (2 * s2 <= qblk) {
-                    const bf16x8 bop = pack_b(gt, s2), mop = pack_b(mk, s2);
                     const int klo = 32 * s2 + 4 * g, khi = klo + 16;
 #pragma unroll
                     for (int j = 0; j < NTK; ++j) {
                         const int nt = dh * NTK + j;
                         const int colq = 32 * (nt >> 1) + 8 * qd + 4 * (nt & 1);
                         const bf16x8 ka = tr_operand<DK>(sK, klo, khi, colq, lane);
-                        acc[j] = mfma16x16x32(ka, bop, acc[j]);
-                        zt[j] = mfma16x16x32(ka, mop, zt[j]);
+                        acc[j] = mfma16x16x32(ka, gop[s2], acc[j]);
+                        zt[j] = mfma16x16x32(ka, mop[s2], zt[j]);
                     }
                 }
             }
@@ -443,9 +495,10 @@ __global__ __launch_bounds__(kThreads8, 1) void bwd_dq8_bf16(
                 for (int i = 0; i < 4; ++i) acc[j][i] = fmaf(ddq, zt[j][i], acc[j][i]) + cpart;
             }
             const bool ok = tq < valid;
-            if (ok && dh == 0 && g == 0) dd_out[row0 + (size_t)c * kChunk + tq] = ddq;
-            store_grad_rows<DK, NTK, kScalePhi, PHI>(acc, dh * NTK, sQ, tq,
-                                                     dq + (row0 + (size_t)c * kChunk + tq) * DK, ok, g);
+            const bool dd_lane = dh == 0 && g == 0;
+            if (dd_lane) sDD[tq] = ok ? ddq : 0.f;
+            buffer_store_f32(ddq, rdd, dd_lane ? tq * 4 : kDropOffset);
+            store_grad_rows<DK, NTK, kScalePhi, PHI>(acc, dh * NTK, sQ, tq, rdq, g);
         };
         // chunk_work holds one workgroup barrier (the dd exchange), reached by
         // each wave through its own case; as in the delta rule, gfx950's
@@ -462,82 +515,38 @@ __global__ __launch_bounds__(kThreads8, 1) void bwd_dq8_bf16(
         // carry the state across the chunk (elu(0) = 0: rows past the end add nothing)
         state8_update<DK, DV>(st, sK, sV, w, lane, ones, 0.f);
         __syncthreads();
+        if (do_rev) {
+            // dR += phi(Q)^T dY, dr += phi(Q)^T dd (rows past the end have dY = 0
+            // and dd = 0: nothing to take back out)
+            const bf16x8 wop[kChunk / 32] = {dd_operand(sDD, 0, lane >> 4), dd_operand(sDD, 1, lane >> 4)};
+            state8_update_w<DK, DV>(rt, sQ, sDY, w, lane, wop, 0.f);
+            if ((c + 1) % sub_chunks == 0 || c + 1 == nch) {
+                rev_store(c / sub_chunks);
+                state8_load<DK, DV>(rt, nullptr, nullptr, w, lane);
+            }
+        }
         if (c + 1 < nch) {
             state_to_lds();
             if (KAPPA && tid < DV) sVb[tid] += colsum_from_lds<DV>(sVp, tid);
+            stage(next, c + 1);
         }
     };
-    for (int c = 0; c < nch; c += 2) {
-        step(buf0, c);
-        if (c + 1 < nch) step(buf1, c + 1);
-    }
-}
-
-// ============================================================== reverse state pass
-// Per state sub-segment s (the first output segment's sub-segments are
-// skipped, cell j holds sub-segment R + j): dR = phi(Q)^T dY and
-// dr = phi(Q)^T dd, in the layout of the forward's segment states.
-template <int DK, int DV, int PHI>
-__global__ __launch_bounds__(kThreads8, 4) void bwd_rstate8_bf16(
-    const uint16_t *__restrict__ q, const float *__restrict__ den, const float *__restrict__ dd,
-    const uint16_t *__restrict__ dout, float *__restrict__ ws, int N, int cells_per_bh, int cell_stride,
-    int first_sub, int sub_len) {
-    __shared__ __attribute__((aligned(16))) uint16_t sQ[kChunk * Tile<DK>::RS];
-    __shared__ __attribute__((aligned(16))) uint16_t sDY[kChunk * Tile<DV>::RS];
-    __shared__ __attribute__((aligned(16))) float sDD[kChunk];
-
-    const int cell = blockIdx.x % cells_per_bh, bh = blockIdx.x / cells_per_bh;
-    const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
-    const int t_begin = (first_sub + cell) * sub_len;
-    const int t_end = min(N, t_begin + sub_len);
-    const int nch = (t_end - t_begin + kChunk - 1) / kChunk;
-    const size_t row0 = (size_t)bh * N + t_begin;
-
-    State8<DK, DV> st;
-    state8_load<DK, DV>(st, nullptr, nullptr, w, lane);
-    struct Buf {
-        Units<DK> q;
-        Units<DV> g;
-        float den[Units<DV>::N], dd[Units<DV>::N];
-    };
-    // never negative: a sub-segment may start past the end of a ragged sequence
-    auto rows_in = [&](int c) { return max(0, min(kChunk, t_end - t_begin - c * kChunk)); };
-    auto issue = [&](Buf &b, int c) {
-        const size_t r = row0 + (size_t)c * kChunk;
-        const int nv = rows_in(c);
-        b.q.load_stream(q + r * DK, nv, tid);
-        b.g.load_stream(dout + r * DV, nv, tid);
-        const rsrc_t rs = chunk_rsrc(den + r, nv * 4), rd = chunk_rsrc(dd + r, nv * 4);
-#pragma unroll
-        for (int i = 0; i < Units<DV>::N; ++i) {
-            b.den[i] = buffer_load_f32(rs, Units<DV>::row_of(tid, i) * 4);
-            b.dd[i] = buffer_load_f32(rd, Units<DV>::row_of(tid, i) * 4);
+    if constexpr (DEPTH == 2) {
+        // two steps per pass, both unconditional (an odd last chunk is peeled)
+        // so that each buffer keeps its registers
+        int c = 0;
+        for (; c + 1 < nch; c += 2) {
+            step(buf1, c);
+            step(buf0, c + 1);
         }
-    };
-    // two chunks in flight (one register buffer per chunk of a pair)
-    Buf b0, b1;
-    if (nch > 0) issue(b0, 0);
-    if (nch > 1) issue(b1, 1);
-    auto step = [&](Buf &b, const int c) {
-#pragma unroll
-        for (int i = 0; i < Units<DK>::N; ++i)
-            *reinterpret_cast<uint4 *>(sQ + Tile<DK>::off(Units<DK>::row_of(tid, i), Units<DK>::col_of(tid, i))) =
-                phi_pack8(b.q.r[i], PHI);
-        stage_dy<DV>(b.g, b.den, b.dd, sDY, sDD, tid);
-        if (c + 2 < nch) issue(b, c + 2);
-        __syncthreads();
-        const bf16x8 wop[kChunk / 32] = {dd_operand(sDD, 0, lane >> 4), dd_operand(sDD, 1, lane >> 4)};
-        // rows past the end have dY = 0 and dd = 0: nothing to take back out
-        state8_update_w<DK, DV>(st, sQ, sDY, w, lane, wop, 0.f);
-        __syncthreads();
-    };
-    for (int c = 0; c < nch; c += 2) {
-        step(b0, c);
-        if (c + 1 < nch) step(b1, c + 1);
+        if (c < nch) step(buf1, c);
+    } else {
+        for (int c = 0; c < nch; ++c) step(buf0, c);
     }
-    float *dst = ws + ((size_t)bh * cell_stride + cell) * (size_t)(DK * DV + DK);
-    state8_store<DK, DV>(st, dst, w, lane);
-    state8_store_z<DK, DV>(st, dst + DK * DV, w, lane);
+    // sub-segments past the end of a ragged sequence: zero cells
+    if (do_rev) {
+        for (int j = (nch + sub_chunks - 1) / sub_chunks; j < R; ++j) rev_store(j);
+    }
 }
 
 // ============================================================== dK, dV pass
@@ -596,6 +605,9 @@ __global__ __launch_bounds__(kThreads8, 1) void bwd_dkv8_bf16(
     if (nch > 1) issue(buf1, nch - 2);
     auto step = [&](BwdBuf<DK, DV> &buf, const int c) {
         const int valid = rows_in(c);
+        // the chunk's dk and dv rows, bounded to its valid rows
+        const size_t crow = row0 + (size_t)c * kChunk;
+        const rsrc_t rdk = chunk_rsrc(dk + crow * DK, valid * DK * 2), rdv = chunk_rsrc(dv + crow * DV, valid * DV * 2);
         stage_qkv<DK, DV, PHI, PHI>(buf, sQ, sK, sV, tid);
         stage_dy<DV>(buf.g, buf.den, buf.dd, sDY, sDD, tid);
         if (c > 1) issue(buf, c - 2);
@@ -606,7 +618,6 @@ __global__ __launch_bounds__(kThreads8, 1) void bwd_dkv8_bf16(
             const int lane = lane_in_loop(tid & 63);
             const int l16 = lane & 15, g = lane >> 4, qd = lane & 3;
             const int tk = 16 * kblk + l16;
-            const size_t orow = row0 + (size_t)c * kChunk + tk;
             auto pack_b = [&](const f32x4(&x)[4], int s2) {
                 uint4 u;
                 u.x = pack_bf16x2(x[2 * s2][0], x[2 * s2][1]);
@@ -672,7 +683,7 @@ __global__ __launch_bounds__(kThreads8, 1) void bwd_dkv8_bf16(
                         }
                     }
                 }
-                store_grad_rows<DK, NTK, kScalePhi, PHI>(ak, dh * NTK, sK, tk, dk + orow * DK, tk < valid, g);
+                store_grad_rows<DK, NTK, kScalePhi, PHI>(ak, dh * NTK, sK, tk, rdk, g);
             }
             // keep the dV phase's loads from being hoisted into the dK phase
             // (they would double the live registers)
@@ -726,7 +737,7 @@ __global__ __launch_bounds__(kThreads8, 1) void bwd_dkv8_bf16(
                         }
                     }
                 }
-                store_grad_rows<DV, NTV, kScaleNone, PHI>(av, dh * NTV, nullptr, tk, dv + orow * DV, tk < valid, g);
+                store_grad_rows<DV, NTV, kScaleNone, PHI>(av, dh * NTV, nullptr, tk, rdv, g);
             }
         };
         switch (kblk_w) {

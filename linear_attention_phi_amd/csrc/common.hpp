@@ -84,9 +84,17 @@ __device__ __forceinline__ uint4 as_u4(bf16x8 v) { return __builtin_bit_cast(uin
 // Buffer resource over [base, base + nbytes): raw (stride 0) buffer loads at a
 // byte offset at or past nbytes return zero instead of touching memory.  The
 // last descriptor word is the gfx9 default data format (32-bit, no swizzle).
+// Base and size are the same in every lane of a wave; they are taken from the
+// first lane so that the descriptor sits in scalar registers even where the
+// compiler formed them on the vector unit (a clamp lowers to v_med3, for one),
+// which would otherwise make it loop over the lanes' distinct descriptors.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 __device__ __forceinline__ rsrc_t chunk_rsrc(const void *base, int nbytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, nbytes, 0x00020000);
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    void *p = reinterpret_cast<void *>(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, __builtin_amdgcn_readfirstlane(nbytes), 0x00020000);
 }
 // 16-byte buffer load at byte offset voff (bounds-checked).  STREAM marks it
 // non-temporal (cache-policy bit 1).
@@ -94,6 +102,25 @@ template <bool STREAM>
 __device__ __forceinline__ uint4 buffer_load16(rsrc_t rs, int voff) {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, STREAM ? 2 : 0));
 }
+
+// 4-byte buffer load (bounds-checked: 0 past the range).
+__device__ __forceinline__ float buffer_load_f32(rsrc_t rs, int voff) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, voff, 0, 0));
+}
+
+// Buffer stores at byte offset voff: a store at or past the descriptor's size
+// is dropped by the hardware.  Rows past the end of a sequence are skipped
+// this way instead of under a branch, so that every store is an instruction
+// the compiler counts: waits for loads issued before a chunk's stores then
+// need not wait for the stores too.
+__device__ __forceinline__ void buffer_store16(uint4 v, rsrc_t rs, int voff) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, voff, 0, 0);
+}
+__device__ __forceinline__ void buffer_store_f32(float v, rsrc_t rs, int voff) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rs, voff, 0, 0);
+}
+// An offset that every chunk descriptor rejects (they cover at most a chunk).
+constexpr int kDropOffset = 1 << 30;
 
 // ---------------------------------------------------------------- cross-lane
 // Sum over the 16 lanes of a DPP row (lanes 16 r .. 16 r + 15), the same in

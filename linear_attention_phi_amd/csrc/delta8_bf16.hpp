@@ -138,6 +138,8 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8_bf16(
     if (nch > 0) issue(buf, 0);
     for (int c = 0; c < nch; ++c) {
         const int valid = rows_in(c);
+        // the chunk's output rows, bounded to its valid rows
+        const rsrc_t ro = chunk_rsrc(o + (row0 + (size_t)c * kChunk) * DV, valid * DV * 2);
         // ---- stage phi(Q), unit keys (zero past the end), V, beta
         {
             constexpr int CG = Units<DK>::CG;
@@ -443,8 +445,7 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8_bf16(
                     }
                 }
             }
-            store_grad_rows<DV, NTV, kScaleNone, PHI>(acc, dh * NTV, nullptr, tq,
-                                                      o + (row0 + (size_t)c * kChunk + tq) * DV, tq < valid, g);
+            store_grad_rows<DV, NTV, kScaleNone, PHI>(acc, dh * NTV, nullptr, tq, ro, g);
         };
         // chunk_rest holds the chunk's two workgroup barriers, and each wave
         // reaches them through its own case: different s_barrier instructions

@@ -52,9 +52,11 @@ def backward_kernel_bytes(kernel, B, H, N, Dk, Dv, in_bytes) -> int | None:
 
 def backward_kernel_flops(kernel, B, H, N, Dk, Dv) -> int | None:
     """Recurrence-level flops of a backward kernel (2 Dk Dv per token for each
-    state-sized product): dQ pass S dY and the forward state update; dK/dV
+    state-sized product): dQ pass S dY, the forward state update and the
+    reverse sums of the state sub-segments (these skip the first segment of a
+    sequence, so at P segments the figure is high by 2 Dk Dv N / P); dK/dV
     pass R v, R^T phi(k) and the reverse state update."""
-    per = {"bwd_dq_bf16": 4, "bwd_dkv_bf16": 6}.get(kernel)
+    per = {"bwd_dq_bf16": 6, "bwd_dkv_bf16": 6}.get(kernel)
     return None if per is None else per * B * H * N * Dk * Dv
 
 
