@@ -121,26 +121,28 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8_bf16(
         Units<DV> v;
         float beta, alpha; // token tid of the chunk (threads below kChunk)
     };
-    auto rows_in = [&](int c) { return min(kChunk, N - c * kChunk); };
+    // rows of chunk c (0 for chunks past the end, whose loads read nothing)
+    auto rows_in = [&](int c) { return max(0, min(kChunk, N - c * kChunk)); };
+    // every load bounded by a buffer descriptor (0 past the end), none under
+    // a branch: beta and alpha of token tid for the threads below kChunk (the
+    // others read past the descriptor's end)
     auto issue = [&](Buf &b, int c) {
         const size_t r = row0 + (size_t)c * kChunk;
         const int nv = rows_in(c);
         b.q.load(q + r * DK, nv, tid);
         b.k.load(k + r * DK, nv, tid);
         b.v.load(v + r * DV, nv, tid);
-        if (tid < kChunk) {
-            const bool in = tid < nv;
-            b.beta = BETA ? (in ? beta[r + tid] : 0.f) : (in ? 1.f : 0.f);
-            b.alpha = GATED && in ? alpha[r + tid] : 1.f;
-        }
+        b.beta = BETA ? buffer_load_f32(chunk_rsrc(beta + r, nv * 4), tid * 4) : (tid < nv ? 1.f : 0.f);
+        // (0 past the end: the staging reads no gate of a row past the end)
+        b.alpha = GATED ? buffer_load_f32(chunk_rsrc(alpha + r, nv * 4), tid * 4) : 1.f;
     };
     Buf buf;
-    if (nch > 0) issue(buf, 0);
-    for (int c = 0; c < nch; ++c) {
+    // ---- stage chunk c: phi(Q), unit keys (zero past the end), V, beta (and
+    // the gate prefix), then refill the buffer with chunk c + 1.  The loop
+    // stages chunk c + 1 at the end of chunk c, after that chunk's stores, so
+    // that the wait for its loads does not cover the stores.
+    auto stage = [&](int c) {
         const int valid = rows_in(c);
-        // the chunk's output rows, bounded to its valid rows
-        const rsrc_t ro = chunk_rsrc(o + (row0 + (size_t)c * kChunk) * DV, valid * DV * 2);
-        // ---- stage phi(Q), unit keys (zero past the end), V, beta
         {
             constexpr int CG = Units<DK>::CG;
 #pragma unroll
@@ -181,7 +183,17 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8_bf16(
                 }
             }
         }
-        if (c + 1 < nch) issue(buf, c + 1);
+        // every read of the buffer before its refill (a load moved above a
+        // read would need other registers and a copy that waits for it)
+        __builtin_amdgcn_sched_barrier(0);
+        issue(buf, c + 1);
+    };
+    issue(buf, 0);
+    if (nch > 0) stage(0);
+    for (int c = 0; c < nch; ++c) {
+        const int valid = rows_in(c);
+        // the chunk's output rows, bounded to its valid rows
+        const rsrc_t ro = chunk_rsrc(o + (row0 + (size_t)c * kChunk) * DV, valid * DV * 2);
         __syncthreads();
 
         // decay from after token j through token t (j < t), and through t from the chunk's start
@@ -469,7 +481,10 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8_bf16(
             state8_update<DK, DV>(st, sK, sV, w, lane, ones, 0.f);
         }
         __syncthreads();
-        if (c + 1 < nch) state8_to_lds<DK, DV>(st, sS, w, tid & 63);
+        if (c + 1 < nch) {
+            state8_to_lds<DK, DV>(st, sS, w, tid & 63);
+            stage(c + 1);
+        }
     }
     if (s_final) state8_store<DK, DV>(st, s_final + bh * DK * DV, w, tid & 63);
 }
