@@ -55,6 +55,11 @@ bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// The prefix and suffix kernels address one (b, h)'s state cells through a
+// buffer descriptor (32-bit byte offsets): a split may not give it more than
+// 2 GiB of cells.  Only a caller-chosen split can come near this.
+bool cells_fit(const Plan &p) { return (size_t)p.Ps * (p.Eb ? p.Eb : p.E) * sizeof(float) <= 0x7fffffffu; }
+
 // seg_req, sub_req > 0 replace the automatic choice of the number of output
 // segments and of state sub-segments per output segment (linattn_forward_planned):
 // the sequence is cut into segments of ceil(chunks / seg_req) chunks (so at most
@@ -537,6 +542,7 @@ int forward_impl(bool gated, const void *q, const void *k, const void *v, const 
     if (overlaps(o, nv, q, nq) || overlaps(o, nv, k, nq) || overlaps(o, nv, v, nv)) return LINATTN_EINVAL;
     if (kind < 0) kind = gated ? LINATTN_KIND_GATED : LINATTN_KIND_FORWARD;
     const Plan pl = make_plan(kind, B, H, N, Dk, Dv, dtype, seg_req, sub_req);
+    if (!cells_fit(pl)) return LINATTN_ESHAPE;
     if (pl.ws_bytes && (!workspace || workspace_bytes < pl.ws_bytes)) return LINATTN_EWORKSPACE;
     hipStream_t st = (hipStream_t)hip_stream;
     char *ws = (char *)workspace;
@@ -622,7 +628,8 @@ size_t linattn_workspace_size_planned(int kind, int B, int H, int N, int Dk, int
     if (kind != LINATTN_KIND_FORWARD && kind != LINATTN_KIND_GATED) return 0;
     if (segments < 1 || subsegments < 1) return 0;
     if (check_common(B, H, N, Dk, Dv, dtype, LINATTN_PHI_ELU1, 0.f) != LINATTN_OK) return 0;
-    return make_plan(kind, B, H, N, Dk, Dv, dtype, segments, subsegments).ws_bytes;
+    const Plan pl = make_plan(kind, B, H, N, Dk, Dv, dtype, segments, subsegments);
+    return cells_fit(pl) ? pl.ws_bytes : 0;
 }
 
 int linattn_forward_noalloc(const void *q, const void *k, const void *v, void *o, const float *s_init,

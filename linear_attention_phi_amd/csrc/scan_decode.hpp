@@ -6,6 +6,10 @@
 
 namespace linattn {
 
+// Cells whose loads the prefix and suffix kernels issue before their adds
+// (8 and 16 measured alike, 32 slower).
+constexpr int kCellBatch = 8;
+
 // Exclusive prefix over the segments of each (b, h), in place:
 //   ws[p] <- S_{<p} = a-decayed sum of the states of segments 0..p-1, seeded
 //   with the caller's initial state (or zero).
@@ -30,25 +34,30 @@ __global__ __launch_bounds__(256) void seg_prefix(float *__restrict__ ws, const 
     if (s_init && e < DK * DV + DK)
         run = e < DK * DV ? s_init[(size_t)bh * DK * DV + e] : z_init[(size_t)bh * DK + (e - DK * DV)];
     float *cell = ws + (size_t)bh * P * E + e;
-    const float *gb = gam ? gam + (size_t)bh * P : nullptr;
-    // Eight segments' loads are issued before their stores: the loop is a
-    // chain of dependent adds, and a load placed after a store to the same
-    // array would otherwise wait a full memory latency per segment.
-    constexpr int kBatch = 8;
+    // The loop is a chain of dependent adds: kBatch segments' loads are issued
+    // before any of their adds, so a chain of n cells waits ceil(n / kBatch)
+    // memory latencies.  Loads and stores go through buffer descriptors over
+    // this (b, h)'s cells, with no branch around them: a load past the
+    // segment states reads 0, a store that is not wanted takes an offset past
+    // the end and is dropped.
+    constexpr int kBatch = kCellBatch;
+    const rsrc_t rc = chunk_rsrc(ws + (size_t)bh * P * E, (cells - 1) * E * 4);
+    const rsrc_t rw = chunk_rsrc(ws + (size_t)bh * P * E, cells * E * 4);
+    const rsrc_t rg = chunk_rsrc(gam ? gam + (size_t)bh * P : ws, gam ? (cells - 1) * 4 : 0);
     for (int p0 = 0; p0 + 1 < cells; p0 += kBatch) {
-        const int nb = min(kBatch, cells - 1 - p0);
         float d[kBatch], gm[kBatch];
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
-            d[j] = j < nb ? cell[(size_t)(p0 + j) * E] : 0.f;
-            gm[j] = gb && j < nb ? gb[p0 + j] : 1.f;
+            d[j] = buffer_load_f32(rc, ((p0 + j) * E + e) * 4);
+            if (gam) gm[j] = buffer_load_f32(rg, (p0 + j) * 4);
         }
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
-            if (j < nb) {
-                if ((p0 + j) % every == 0) cell[(size_t)(p0 + j) * E] = run;
-                run = gb ? fmaf(gm[j], run, d[j]) : run + d[j];
-            }
+            const int p = p0 + j;
+            // cells past the last segment state: d = 0 and a gate of 1 leave run as it is
+            const bool in = p + 1 < cells;
+            buffer_store_f32(run, rw, in && p % every == 0 ? (p * E + e) * 4 : kDropOffset);
+            run = gam ? fmaf(in ? gm[j] : 1.f, run, d[j]) : run + d[j];
         }
     }
     cell[(size_t)(cells - 1) * E] = run;
@@ -61,20 +70,23 @@ __global__ __launch_bounds__(256) void seg_suffix(float *__restrict__ ws, int P,
     const int e = blockIdx.x * 256 + threadIdx.x;
     const int bh = blockIdx.y;
     if (e >= E) return;
-    float *cell = ws + (size_t)bh * P * E + e;
     float run = 0.f;
-    constexpr int kBatch = 8;
+    // as in seg_prefix: kBatch loads ahead of their adds, no branch around a
+    // load or a store (loads before the first cell read 0)
+    constexpr int kBatch = kCellBatch;
+    const rsrc_t rc = chunk_rsrc(ws + (size_t)bh * P * E, cells * E * 4);
     for (int j1 = cells; j1 > 0; j1 -= kBatch) {
-        const int nb = min(kBatch, j1);
         float d[kBatch];
 #pragma unroll
-        for (int i = 0; i < kBatch; ++i) d[i] = i < nb ? cell[(size_t)(j1 - 1 - i) * E] : 0.f;
+        for (int i = 0; i < kBatch; ++i) {
+            const int j = j1 - 1 - i;
+            d[i] = buffer_load_f32(rc, j >= 0 ? (j * E + e) * 4 : kDropOffset);
+        }
 #pragma unroll
         for (int i = 0; i < kBatch; ++i) {
-            if (i < nb) {
-                run += d[i];
-                cell[(size_t)(j1 - 1 - i) * E] = run;
-            }
+            run += d[i];
+            const int j = j1 - 1 - i;
+            buffer_store_f32(run, rc, j >= 0 ? (j * E + e) * 4 : kDropOffset);
         }
     }
 }
