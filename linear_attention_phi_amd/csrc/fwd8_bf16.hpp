@@ -560,20 +560,21 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd_out8_bf16(
 
     auto rows_in = [&](int c) { return min(kChunk, t_end - t_begin - c * kChunk); };
 
-    // K, V (and gates) are loaded two chunks ahead without gates and one with
-    // them (where the decay bookkeeping needs the registers), Q one chunk ahead;
-    // each buffer is refilled as soon as it is staged.
+    // Q, K, V (and gates) are loaded two chunks ahead without gates and one
+    // with them (where the decay bookkeeping needs the registers); each buffer
+    // is refilled as soon as it is staged.
     constexpr int DEPTH = GATED ? 1 : 2;
     struct Buf {
         Units<DK> k;
         Units<DV> v;
+        Units<DK> q;
         float a;
     };
-    Units<DK> qbuf;
     auto issue = [&](Buf &b, int c) {
         const int nv = rows_in(c);
         b.k.load(kbp + (size_t)c * kChunk * DK, nv, tid);
         b.v.load(vbp + (size_t)c * kChunk * DV, nv, tid);
+        b.q.load(qbp + (size_t)c * kChunk * DK, nv, tid);
         if (GATED) b.a = lane < nv ? ab[c * kChunk + lane] : 1.f;
     };
     auto step = [&](Buf &b, int c) {
@@ -590,7 +591,7 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd_out8_bf16(
 #pragma unroll
         for (int i = 0; i < Units<DK>::N; ++i) {
             const int row = Units<DK>::row_of(tid, i), col = Units<DK>::col_of(tid, i);
-            *reinterpret_cast<uint4 *>(sQ + TK::off(row, col)) = phi_pack8(qbuf.r[i], phi_mode);
+            *reinterpret_cast<uint4 *>(sQ + TK::off(row, col)) = phi_pack8(b.q.r[i], phi_mode);
             if (GATED) {
                 const float sc = decay_k(ke, cg.kappa_at(row));
                 uint4 plain, scaled;
@@ -605,7 +606,6 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd_out8_bf16(
         for (int i = 0; i < Units<DV>::N; ++i)
             *reinterpret_cast<uint4 *>(sV + TV::off(Units<DV>::row_of(tid, i), Units<DV>::col_of(tid, i))) =
                 b.v.r[i];
-        if (c + 1 < nch) qbuf.load(qbp + (size_t)(c + 1) * kChunk * DK, rows_in(c + 1), tid);
         if (c + DEPTH < nch) issue(b, c + DEPTH);
         __syncthreads();
         // The chunk's matrix work is specialized on the wave's query block, so
@@ -739,7 +739,6 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd_out8_bf16(
         }
     };
 
-    qbuf.load(qbp, rows_in(0), tid);
     if constexpr (DEPTH == 2) {
         Buf b0, b1;
         issue(b0, 0);
