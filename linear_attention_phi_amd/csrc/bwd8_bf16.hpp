@@ -41,7 +41,7 @@
 //      dd_t = -phi(q_t) . (S_t dY_t) / (phi(q_t) . z_t + eps),
 //    the same S_t, z_t that the gradient uses, so that the cancellation is
 //    exact in the arithmetic the pass carries out.  dd goes to the workspace
-//    for the reverse passes.
+//    for the dK, dV pass, and into the reverse sums.
 #pragma once
 
 #include "fwd8_bf16.hpp"
@@ -498,7 +498,13 @@ __global__ __launch_bounds__(kThreads8, 1) void bwd_dq8_bf16(
             const bool dd_lane = dh == 0 && g == 0;
             if (dd_lane) sDD[tq] = ok ? ddq : 0.f;
             buffer_store_f32(ddq, rdd, dd_lane ? tq * 4 : kDropOffset);
-            store_grad_rows<DK, NTK, kScalePhi, PHI>(acc, dh * NTK, sQ, tq, rdq, g);
+            // phi'(q) from the phi(q) values already unpacked for the dot products
+#pragma unroll
+            for (int j = 0; j < NTK; ++j) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[j][i] *= dphi_of<PHI, kScalePhi>(fq[j][i]);
+            }
+            store_grad_rows<DK, NTK, kScaleNone, PHI>(acc, dh * NTK, nullptr, tq, rdq, g);
         };
         // chunk_work holds one workgroup barrier (the dd exchange), reached by
         // each wave through its own case; as in the delta rule, gfx950's
