@@ -602,10 +602,12 @@ __global__ __launch_bounds__(kThreads, 2) void noncausal_apply_bf16(const uint16
     const int c1 = min((N + kChunk - 1) / kChunk, c0 + chunks_per_block);
     const int t = 16 * w + l16; // this lane's query row within a chunk
     const uint16_t *qh = q + (size_t)bh * N * DK;
-    // The next chunk's Q rows are loaded while this one is computed.  The loads
-    // are bounded to the chunk's valid rows (rows past the end read as zero and
-    // their outputs are not stored); past the block's last chunk the range is
-    // empty, so the loop needs no branch around them.
+    // The next chunk's Q rows are loaded while this one is computed.  Loads and
+    // stores are bounded to the chunk's valid rows (rows past the end read as
+    // zero, and their outputs are dropped by the store's bounds, with no branch
+    // around it: the compiler then counts every store, and the wait for the next
+    // chunk's loads does not cover them); past the block's last chunk the range
+    // is empty, so the loop needs no branch around the loads either.
     auto rows_in = [&](int c) { return c < c1 ? min(kChunk, N - c * kChunk) : 0; };
     auto qload = [&](uint4 (&r)[L::KS], int c) {
         const rsrc_t rs = chunk_rsrc(qh + (size_t)c * kChunk * DK, rows_in(c) * DK * 2);
@@ -646,9 +648,9 @@ __global__ __launch_bounds__(kThreads, 2) void noncausal_apply_bf16(const uint16
             den += bf_lo(u.z) * z1.x + bf_hi(u.z) * z1.y + bf_lo(u.w) * z1.z + bf_hi(u.w) * z1.w;
         }
         den = sum_over_groups(den);
-        if (t < valid) {
+        {
             const float inv = __builtin_amdgcn_rcpf(den + eps); // 1 ulp; the result is rounded to bf16
-            uint16_t *orow = o + ((size_t)bh * N + (size_t)c * kChunk + t) * DV;
+            const rsrc_t ro = chunk_rsrc(o + ((size_t)bh * N + (size_t)c * kChunk) * DV, valid * DV * 2);
 #pragma unroll
             for (int p = 0; p < DV / 32; ++p) {
                 uint4 u;
@@ -656,19 +658,20 @@ __global__ __launch_bounds__(kThreads, 2) void noncausal_apply_bf16(const uint16
                 u.y = pack_bf16x2(oacc[2 * p][2] * inv, oacc[2 * p][3] * inv);
                 u.z = pack_bf16x2(oacc[2 * p + 1][0] * inv, oacc[2 * p + 1][1] * inv);
                 u.w = pack_bf16x2(oacc[2 * p + 1][2] * inv, oacc[2 * p + 1][3] * inv);
-                *reinterpret_cast<uint4 *>(orow + 32 * p + 8 * g) = u;
+                buffer_store16(u, ro, (t * DV + 32 * p + 8 * g) * 2);
             }
         }
     };
     uint4 r0[L::KS], r1[L::KS];
     qload(r0, c0);
-    for (int c = c0; c < c1; c += 2) {
+    int c = c0;
+    for (; c + 1 < c1; c += 2) {
         qload(r1, c + 1);
         process(r0, c);
-        if (c + 1 >= c1) break;
         qload(r0, c + 2);
         process(r1, c + 1);
     }
+    if (c < c1) process(r0, c);
 }
 
 } // namespace linattn
