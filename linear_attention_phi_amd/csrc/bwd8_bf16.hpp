@@ -57,8 +57,10 @@ __device__ __forceinline__ int lane_in_loop(int lane) {
     return lane;
 }
 
-// 1 / den for dY = dO / den; rows past the end (den read as 0) get 0.
-__device__ __forceinline__ float dy_inv(float den) { return den != 0.f ? 1.f / den : 0.f; }
+// 1 / den for dY = dO / den; rows past the end (den read as 0) get 0.  The
+// hardware reciprocal (1 ulp) in place of a correctly rounded division: dY is
+// rounded to bf16 next, and every pass forms it with this same function.
+__device__ __forceinline__ float dy_inv(float den) { return den != 0.f ? __builtin_amdgcn_rcpf(den) : 0.f; }
 
 // Eight elements of dY = dO / den, rounded to bf16 as every pass uses them.
 __device__ __forceinline__ uint4 dy_pack8(uint4 g, float inv) {
@@ -486,7 +488,9 @@ __global__ __launch_bounds__(kThreads8, 1) void bwd_dq8_bf16(
             const float n_t = n_prev + (float)(tq + 1);
             const float num = (sRed[0 * kChunk + tq] + sRed[2 * kChunk + tq]) + kap * sq * vdy;
             const float dnm = (sRed[1 * kChunk + tq] + sRed[3 * kChunk + tq]) + kap * n_t * sq + eps;
-            const float ddq = dnm != 0.f ? -num / dnm : 0.f;
+            // (the hardware reciprocal, 1 ulp: dphi(q) . phi(q) = num + dd dnm
+            // still cancels to the rounding of the terms)
+            const float ddq = dnm != 0.f ? -num * __builtin_amdgcn_rcpf(dnm) : 0.f;
             // dphi(q) = A + dd zeta + (Vbar . dY + n dd) 1
             const float cpart = kap * fmaf(n_t, ddq, vdy);
 #pragma unroll

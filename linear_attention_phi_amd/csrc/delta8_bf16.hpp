@@ -163,8 +163,10 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8_bf16(
 #pragma unroll
                     for (int m = 1; m < CG; m <<= 1) nrm += __shfl_xor(nrm, m, 64);
                 }
-                // a zero key (or a row past the end) writes nothing
-                const float inv = (row < valid && nrm > 0.f) ? 1.f / sqrtf(nrm) : 0.f;
+                // a zero key (or a row past the end) writes nothing; the hardware
+                // reciprocal square root (about 1 ulp; the unit key is rounded to
+                // bf16 next) in place of a correctly rounded root and division
+                const float inv = (row < valid && nrm > 0.f) ? __builtin_amdgcn_rsqf(nrm) : 0.f;
                 *reinterpret_cast<uint4 *>(sK + TK::off(row, col)) =
                     make_uint4(pack_bf16x2(f[0] * inv, f[1] * inv), pack_bf16x2(f[2] * inv, f[3] * inv),
                                pack_bf16x2(f[4] * inv, f[5] * inv), pack_bf16x2(f[6] * inv, f[7] * inv));
