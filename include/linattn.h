@@ -176,8 +176,8 @@ int linattn_forward_noalloc(const void *q, const void *k, const void *v, void *o
  *                alpha is given, else LINATTN_KIND_FORWARD.
  * Other arguments as linattn_forward(_gated); LINATTN_EINVAL when segments
  * or subsegments is below 1, LINATTN_ESHAPE when the split's state cells of
- * one (b, h) (segments x parts, Dk Dv + Dk + Dv floats each) would exceed
- * 2 GiB (linattn_workspace_size_planned then returns 0).  linattn_forward
+ * one (b, h) (segments x parts, Dk Dv + Dk + Dv floats each) would reach
+ * 1 GiB (linattn_workspace_size_planned then returns 0).  linattn_forward
  * uses a split chosen to fill the GPU.
  */
 int linattn_forward_planned(const void *q, const void *k, const void *v,

@@ -56,9 +56,10 @@ bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // The prefix and suffix kernels address one (b, h)'s state cells through a
-// buffer descriptor (32-bit byte offsets): a split may not give it more than
-// 2 GiB of cells.  Only a caller-chosen split can come near this.
-bool cells_fit(const Plan &p) { return (size_t)p.Ps * (p.Eb ? p.Eb : p.E) * sizeof(float) <= 0x7fffffffu; }
+// buffer descriptor and drop unwanted stores by an offset of 1 GiB
+// (kDropOffset): a split may not give one (b, h) 1 GiB of cells.  Only a
+// caller-chosen split can come near this.
+bool cells_fit(const Plan &p) { return (size_t)p.Ps * (p.Eb ? p.Eb : p.E) * sizeof(float) < (size_t(1) << 30); }
 
 // seg_req, sub_req > 0 replace the automatic choice of the number of output
 // segments and of state sub-segments per output segment (linattn_forward_planned):

@@ -119,7 +119,8 @@ __device__ __forceinline__ void buffer_store16(uint4 v, rsrc_t rs, int voff) {
 __device__ __forceinline__ void buffer_store_f32(float v, rsrc_t rs, int voff) {
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rs, voff, 0, 0);
 }
-// An offset that every chunk descriptor rejects (they cover at most a chunk).
+// An offset past every descriptor the kernels form: each covers under 1 GiB
+// (a chunk's rows, or one (b, h)'s state cells, which the host keeps below it).
 constexpr int kDropOffset = 1 << 30;
 
 // ---------------------------------------------------------------- cross-lane

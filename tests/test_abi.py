@@ -243,13 +243,15 @@ def test_planned_forward_rejects_bad_arguments_and_sizes_its_workspace(L):
     assert wsp(0, 1, 1, 8192, 64, 64, 1, 0, 1) == 0
     need = wsp(0, 1, 1, 8192, 64, 64, 1, 4, 2)
     assert planned(L, segments=4, subsegments=2, ws=FAKE[6], wsb=need - 1) == EWORKSPACE
-    # a split whose state cells of one (b, h) pass 2 GiB (the prefix addresses them with 32-bit
-    # offsets): 2^21 tokens of 128-dim heads cut into one segment per chunk, 32768 cells of 66 KB
+    # a split whose state cells of one (b, h) reach 1 GiB (the prefix addresses them through one
+    # buffer descriptor): 2^21 tokens of 128-dim heads in one segment per chunk (32768 cells of 66 KB,
+    # 2.2 GB) or per two chunks (1.1 GB)
     big = 1 << 21
     assert wsp(0, 1, 1, big, 128, 128, 1, big // 64, 1) == 0
+    assert wsp(0, 1, 1, big, 128, 128, 1, big // 128, 1) == 0
     assert planned(L, segments=big // 64, N=big, Dk=128, Dv=128, ws=FAKE[6], wsb=1 << 40) == ESHAPE
-    # just inside the limit the call is sized normally
-    assert wsp(0, 1, 1, big, 128, 128, 1, big // 128, 1) > 0
+    # below the limit (4096 cells, 273 MB) the call is sized normally
+    assert wsp(0, 1, 1, big, 128, 128, 1, big // 512, 1) > 0
 
 
 def train(L, q=FAKE[0], k=FAKE[1], v=FAKE[2], o=FAKE[3], den=FAKE[4], B=1, H=1, N=64, Dk=64, Dv=64, dtype=1,
