@@ -23,7 +23,8 @@ root-sum-square of those products (parity.dk_term_size; a dropped or doubled
 chunk of 64 tokens is still about 15x above that floor at 2e-2).  dv rows have
 independent columns and are compared plainly.  Every gradient must also meet
 the tolerance head-normwise.  Shapes span several chunks and segments (the reverse segment
-sums), ragged tails, both head dims and their mix.  Sequences of one token get
+sums), ragged tails, both head dims and their mix, and inputs with and without the 1/sqrt(D)
+scale (features and denominators over a wider range).  Sequences of one token get
 their own test: there every row of dq and dk is eps-sized.
 """
 import numpy as np
@@ -39,8 +40,9 @@ pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 
 
-def make(B, H, N, Dk, Dv, seed, positive=False):
-    w = synth.Workload("t", B, H, N, Dk, Dv, torch.bfloat16, seed, q_scale=Dk ** -0.5, k_scale=Dk ** -0.5)
+def make(B, H, N, Dk, Dv, seed, positive=False, scale=None):
+    s = Dk ** -0.5 if scale is None else scale
+    w = synth.Workload("t", B, H, N, Dk, Dv, torch.bfloat16, seed, q_scale=s, k_scale=s)
     q, k, v = synth.qkv(w)
     if positive:
         q, k = ((x.float().abs() + 1.0 / 64).to(torch.bfloat16) for x in (q, k))
@@ -111,6 +113,13 @@ def test_backward_one_token(Dk, Dv):
         err = np.abs(got.double().numpy() - ref).max(-1)
         print(f"  {name}: max |err| / term size {float((err / terms).max()):.3e} (tol {tol:.0e})")
         assert (err <= tol * terms).all(), name
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 2000, 128, 128), (1, 2, 700, 64, 128)])
+def test_backward_unscaled_inputs(shape):
+    # q, k drawn N(0, 1) without the 1/sqrt(D) scale: features and denominators
+    # over a wider range (phi up to ~e^3, den in the thousands)
+    check(*make(*shape, seed=760 + sum(shape), scale=1.0))
 
 
 @pytest.mark.parametrize("use_saved", [True, False])

@@ -62,7 +62,8 @@ def test_delta_full_length():
     check(*synth.qkv(x))
 
 
-@pytest.mark.parametrize("shape", [(1, 2, 700, 128, 128), (2, 1, 130, 64, 64)])
+@pytest.mark.parametrize("shape", [(1, 2, 700, 128, 128), (2, 1, 130, 64, 64), (1, 2, 333, 128, 64),
+                                   (1, 1, 64, 64, 128)])
 def test_delta_with_beta(shape):
     check(*make(*shape, seed=1220 + sum(shape), with_beta=True))
 
