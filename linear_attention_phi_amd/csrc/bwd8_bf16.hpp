@@ -261,6 +261,8 @@ __global__ __launch_bounds__(kThreads8, 1) void bwd_dq8_bf16(
     __shared__ __attribute__((aligned(16))) uint16_t sS[DK * DV];
     __shared__ __attribute__((aligned(16))) float sZf[DK];
     __shared__ __attribute__((aligned(16))) float sVb[KAPPA ? DV : 4];     // Vbar before the chunk
+    // Vbar in bf16 high and low parts (rows 0 and 1 of an MFMA A operand)
+    __shared__ __attribute__((aligned(16))) uint16_t sVbh[KAPPA ? 2 * DV : 8];
     __shared__ __attribute__((aligned(16))) float sVp[KAPPA ? 8 * DV : 4]; // the chunk's per-wave column sums
     __shared__ __attribute__((aligned(16))) float sDD2[2][kChunk];
 
@@ -281,7 +283,11 @@ __global__ __launch_bounds__(kThreads8, 1) void bwd_dq8_bf16(
         state8_load<DK, DV>(st, s0, z0, w, lane);
         if (KAPPA && tid < DV) {
             const float *vb0 = start_vb ? start_vb + bh * start_z_stride_bh + seg * start_stride_seg : nullptr;
-            sVb[tid] = vb0 ? vb0[tid] : 0.f;
+            const float vb = vb0 ? vb0[tid] : 0.f;
+            sVb[tid] = vb;
+            const float hi = bf16_round(vb);
+            sVbh[tid] = (uint16_t)f32_to_bf16_bits(hi);
+            sVbh[DV + tid] = (uint16_t)f32_to_bf16_bits(vb - hi);
         }
     }
     auto state_to_lds = [&] {
@@ -383,21 +389,25 @@ __global__ __launch_bounds__(kThreads8, 1) void bwd_dq8_bf16(
                     }
                 }
             }
-            // Vbar_t . dY_t = Vbar_{c-1} . dY_t + sum_{j <= t} v_j . dY_t, in fp32
+            // Vbar_t . dY_t = Vbar_{c-1} . dY_t + sum_{j <= t} v_j . dY_t, summed in fp32
             float vdy = 0.f;
 #pragma unroll
             for (int kb4 = 0; kb4 < 4; ++kb4) {
                 if (kb4 <= qblk) vdy += (gt[kb4][0] + gt[kb4][1]) + (gt[kb4][2] + gt[kb4][3]);
             }
             if (KAPPA) {
+                // Vbar . dY on the matrix cores: rows 0 and 1 of the A operand hold
+                // Vbar's bf16 high and low parts (together Vbar to about 2^-17
+                // relative; the products accumulate in fp32), so lanes of group 0
+                // receive hi . dY and lo . dY (the other rows, and lanes, hold zeros)
+                f32x4 vbd = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < KSV; ++ks) {
-                    const float4 a = *reinterpret_cast<const float4 *>(sVb + 32 * ks + 8 * g);
-                    const float4 b = *reinterpret_cast<const float4 *>(sVb + 32 * ks + 8 * g + 4);
-                    const float vb[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) vdy = fmaf((float)dya[ks][e], vb[e], vdy);
+                    const bf16x8 z8 = as_bf16x8(make_uint4(0u, 0u, 0u, 0u));
+                    const bf16x8 a = l16 < 2 ? *reinterpret_cast<const bf16x8 *>(sVbh + l16 * DV + 32 * ks + 8 * g) : z8;
+                    vbd = mfma16x16x32(a, dya[ks], vbd);
                 }
+                vdy += vbd[0] + vbd[1];
             }
             vdy = sum_over_groups(vdy);
             // the B operands of the in-chunk products over key steps of 32: G^T
@@ -537,7 +547,13 @@ __global__ __launch_bounds__(kThreads8, 1) void bwd_dq8_bf16(
         }
         if (c + 1 < nch) {
             state_to_lds();
-            if (KAPPA && tid < DV) sVb[tid] += colsum_from_lds<DV>(sVp, tid);
+            if (KAPPA && tid < DV) {
+                const float vb = sVb[tid] + colsum_from_lds<DV>(sVp, tid);
+                sVb[tid] = vb;
+                const float hi = bf16_round(vb);
+                sVbh[tid] = (uint16_t)f32_to_bf16_bits(hi);
+                sVbh[DV + tid] = (uint16_t)f32_to_bf16_bits(vb - hi);
+            }
             stage(next, c + 1);
         }
     };
