@@ -221,6 +221,50 @@ __device__ __forceinline__ bf16x8 dd_operand(const float *sDD, int ks, int G) {
                                 pack_bf16x2(b.z, b.w)));
 }
 
+// The state update of state8_update with ones for z, which also sums the V
+// rows over the chunk (the column sums that carry Vbar) on the matrix cores:
+// V^T times a ones operand gives each column's sum in every output column.
+// The waves of the first key-dim block (which between them hold every
+// value-dim tile) do the extra products; lane 16 g of such a wave then holds
+// the sums of columns 16 (nt0 + ni) + 4 g + i and writes them to vd[Dv].
+template <int DK, int DV>
+__device__ __forceinline__ void state8_update_vcol(State8<DK, DV> &st, const uint16_t *kt, const uint16_t *vt, int w,
+                                                   int lane, bf16x8 ones, float *vd) {
+    using S = State8<DK, DV>;
+    const int G = lane >> 4, q = lane & 3, mt0 = (w >> 2) * S::MTW, nt0 = (w & 3) * S::NTW;
+    const int zmi = S::zmi(w);
+    const bool vcol = mt0 == 0;
+    f32x4 vc[S::NTW];
+#pragma unroll
+    for (int ni = 0; ni < S::NTW; ++ni) vc[ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < kChunk / 32; ++ks) {
+        const int klo = 32 * ks + 8 * G, khi = klo + 4;
+        bf16x8 a[S::MTW], b[S::NTW];
+#pragma unroll
+        for (int mi = 0; mi < S::MTW; ++mi) a[mi] = tr_operand<DK>(kt, klo, khi, 16 * (mt0 + mi) + 4 * q, lane);
+#pragma unroll
+        for (int ni = 0; ni < S::NTW; ++ni) b[ni] = tr_operand<DV>(vt, klo, khi, 16 * (nt0 + ni) + 4 * q, lane);
+#pragma unroll
+        for (int mi = 0; mi < S::MTW; ++mi) {
+#pragma unroll
+            for (int ni = 0; ni < S::NTW; ++ni) st.s[mi][ni] = mfma16x16x32(b[ni], a[mi], st.s[mi][ni]);
+            if (mi == zmi) st.z = mfma16x16x32(ones, a[mi], st.z);
+        }
+        if (vcol) {
+#pragma unroll
+            for (int ni = 0; ni < S::NTW; ++ni) vc[ni] = mfma16x16x32(b[ni], ones, vc[ni]);
+        }
+    }
+    if (vcol && (lane & 15) == 0) {
+#pragma unroll
+        for (int ni = 0; ni < S::NTW; ++ni) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) vd[16 * (nt0 + ni) + 4 * G + i] = vc[ni][i];
+        }
+    }
+}
+
 // ============================================================== dQ pass
 // Per output segment, forward in time from the segment's prefix state.  Wave
 // w serves query block qblk (light and heavy blocks paired per SIMD as in the
@@ -263,7 +307,7 @@ __global__ __launch_bounds__(kThreads8, 1) void bwd_dq8_bf16(
     __shared__ __attribute__((aligned(16))) float sVb[KAPPA ? DV : 4];     // Vbar before the chunk
     // Vbar in bf16 high and low parts (rows 0 and 1 of an MFMA A operand)
     __shared__ __attribute__((aligned(16))) uint16_t sVbh[KAPPA ? 2 * DV : 8];
-    __shared__ __attribute__((aligned(16))) float sVp[KAPPA ? 8 * DV : 4]; // the chunk's per-wave column sums
+    __shared__ __attribute__((aligned(16))) float sVd[KAPPA ? DV : 4]; // the chunk's column sums of V
     __shared__ __attribute__((aligned(16))) float sDD2[2][kChunk];
 
     const int seg = blockIdx.x % P, bh = blockIdx.x / P;
@@ -317,19 +361,11 @@ __global__ __launch_bounds__(kThreads8, 1) void bwd_dq8_bf16(
     // reverse sums' accumulators leave registers for one.
     constexpr int DEPTH = DK * DV > 64 * 128 ? 1 : 2;
     BwdBuf<DK, DV, false> buf0, buf1;
-    // the column sums of V over the staged chunk (the constant part's Vbar)
-    float vsum[8];
     // chunk c's tiles into LDS from its buffer, which then takes the loads of
     // chunk c + DEPTH.  The loop stages chunk c + 1 at the end of chunk c's
     // step, after that step's stores: every path into a staging has the same
     // stores after the loads it waits for, so the wait need not cover them.
     auto stage = [&](BwdBuf<DK, DV, false> &buf, const int c) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) vsum[e] = 0.f;
-        if (KAPPA) {
-#pragma unroll
-            for (int i = 0; i < Units<DV>::N; ++i) add_bf16x8(vsum, buf.v.r[i]);
-        }
         stage_dq<DK, DV, PHI, FEAT>(buf, sQ2[c & 1], sK, sV, sSq, tid);
         stage_dy<DV>(buf.g, buf.den, buf.dd, sDY2[c & 1], nullptr, tid);
         // every read of the buffer before its refill: the loads then land in
@@ -530,10 +566,14 @@ __global__ __launch_bounds__(kThreads8, 1) void bwd_dq8_bf16(
         case 2: chunk_work(std::integral_constant<int, 2>{}); break;
         default: chunk_work(std::integral_constant<int, 3>{}); break;
         }
-        if (KAPPA) colsum_to_lds<DV>(vsum, sVp, w, lane);
 
-        // carry the state across the chunk (elu(0) = 0: rows past the end add nothing)
-        state8_update<DK, DV>(st, sK, sV, w, lane, ones, 0.f);
+        // carry the state across the chunk (elu(0) = 0: rows past the end add
+        // nothing; their V rows are zeros)
+        if constexpr (KAPPA) {
+            state8_update_vcol<DK, DV>(st, sK, sV, w, lane, ones, sVd);
+        } else {
+            state8_update<DK, DV>(st, sK, sV, w, lane, ones, 0.f);
+        }
         __syncthreads();
         if (do_rev) {
             // dR += phi(Q)^T dY, dr += phi(Q)^T dd (rows past the end have dY = 0
@@ -548,7 +588,7 @@ __global__ __launch_bounds__(kThreads8, 1) void bwd_dq8_bf16(
         if (c + 1 < nch) {
             state_to_lds();
             if (KAPPA && tid < DV) {
-                const float vb = sVb[tid] + colsum_from_lds<DV>(sVp, tid);
+                const float vb = sVb[tid] + sVd[tid];
                 sVb[tid] = vb;
                 const float hi = bf16_round(vb);
                 sVbh[tid] = (uint16_t)f32_to_bf16_bits(hi);
