@@ -24,6 +24,8 @@ Prints ONE JSON line:
   the non-causal form, the forward with snapshots, the backward, the delta
   rule), each with the same fields and its own short oracle timing.
 
+Every oracle timing runs after every GPU timing.
+
 Also: ``--copy-calibration`` runs only a plain device copy of a known size
 (for scaling the FETCH_SIZE / WRITE_SIZE counters), ``--path`` runs a single
 workload (profiling runs), ``--sweep-plans`` times the headline forward under
@@ -113,8 +115,13 @@ def timed(fn, steps, warmup, stream):
 
 def kernel_times(fn, steps, stream):
     """Per library kernel: launches per step and average device ms per launch, from the library's
-    own HIP events; and the ms per step of that same loop (events add a little per launch)."""
+    own HIP events; and the ms per step of that same loop (events add a little per launch).  A few
+    launches with the events on come first, unrecorded."""
     la.linattn_profile_enable(True)
+    for _ in range(min(steps, 10)):
+        fn()
+    torch.cuda.synchronize()
+    la.linattn_profile_enable(True)  # (clears the record)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
@@ -469,6 +476,12 @@ def copy_calibration(dev, steps):
     print(json.dumps({"copy_bytes": n, "launches": steps}), flush=True)
 
 
+def loop_disturbed(prof_ms, ms):
+    """The profiled loop ran much slower than the timed one: more than the per-launch events explain
+    (a few microseconds a launch, which on the 64-dim forward's 30-microsecond step is over a quarter)."""
+    return prof_ms > 1.25 * ms and prof_ms - ms > 0.05
+
+
 def dominant_kernel(kt, w, any_kernel=False):
     """The kernel with the most time per step, among those whose algorithmic bytes are defined unless
     any_kernel (under a profiler's counter runs launches are serialized, and a small kernel such as the
@@ -482,6 +495,12 @@ def path_entry(w, fn, nbytes, stream, args, tokens, reset=None, flops=None, key=
     if reset:
         reset()
     kt, prof_ms = kernel_times(fn, args.steps, stream)
+    retried = loop_disturbed(prof_ms, ms)
+    if retried:
+        # a loop disturbed from outside (the clock, the host): measured once more
+        if reset:
+            reset()
+        kt, prof_ms = kernel_times(fn, args.steps, stream)
     if reset:
         reset()
     dom = dominant_kernel(kt, w, kernel_nbytes is not None)
@@ -492,7 +511,7 @@ def path_entry(w, fn, nbytes, stream, args, tokens, reset=None, flops=None, key=
             "roofline": roofline_entry(dom, kt[dom]["avg_ms"], kernel_nbytes or kernel_bytes(dom, w), key,
                                        kernel_flops(dom, w, flops)),
             "kernels_ms": {n: round(e["avg_ms"], 4) for n, e in kt.items()},
-            "profiled_ms_per_step": round(prof_ms, 4)}
+            "profiled_ms_per_step": round(prof_ms, 4), "profiled_loop_repeated": retried}
 
 
 def sweep_plans(dev, stream, steps, warmup):
@@ -557,7 +576,8 @@ def main():
 
     if args.path not in (None, "forward"):
         # single-path run (used for counter collection); prints its own line
-        print(json.dumps(single_path(args.path, args, dev, stream)), flush=True)
+        r, _ = single_path(args.path, args, dev, stream)
+        print(json.dumps(r), flush=True)
         return
 
     log(f"[bench] building inputs for {HEADLINE}")
@@ -565,6 +585,9 @@ def main():
     log(f"[bench] warmup {args.warmup}, timing {args.steps} steps")
     ms = timed(fn, args.steps, args.warmup, stream)
     kt, prof_ms = kernel_times(fn, args.steps, stream)
+    retried = loop_disturbed(prof_ms, ms)
+    if retried:
+        kt, prof_ms = kernel_times(fn, args.steps, stream)
     dom = dominant_kernel(kt, w)
     flops = rf.chunked_flops(w.B, w.H, w.N, w.Dk, w.Dv, 64)
     tokens = w.B * w.N
@@ -580,12 +603,17 @@ def main():
         "path_roofline": path_roofline_entry(ms, nbytes, kt, HEADLINE),
         "path_roofline_frac": round(rf.hbm_time_s(nbytes) / (ms * 1e-3), 4),
         "kernels_ms": {n: round(e["avg_ms"], 4) for n, e in kt.items()},
-        "profiled_ms_per_step": round(prof_ms, 4),
+        "profiled_ms_per_step": round(prof_ms, 4), "profiled_loop_repeated": retried,
         "counters_source_hash": kernel_source_hash(),
     }
     log(f"[bench] forward {ms:.3f} ms/step, {value:.1f} Mtok/s")
+    cpu_jobs = []
     if not args.no_paths:
-        result["paths"] = other_paths(args, dev, stream, (q, k, v))
+        result["paths"], cpu_jobs = other_paths(args, dev, stream, (q, k, v))
+    # the oracle timings run after every GPU timing: host work just before a timed loop (the oracle's
+    # OpenMP threads, large copies to the host) was seen to slow that loop's launches
+    for job in cpu_jobs:
+        job()
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on a sample of the same workload")
         result["cpu_baseline"] = cpu_baseline(w, *(x.cpu() for x in (q, k, v)))
@@ -595,7 +623,8 @@ def main():
 
 
 def single_path(name, args, dev, stream, headline_inputs=None, cpu=False):
-    """One path's entry (and, with cpu=True, a short oracle timing on its workload)."""
+    """One path's entry, and (with cpu=True, else None) a function that adds a short oracle timing on
+    its workload to the entry when called."""
     if name == "c2":
         w, fn, nbytes, first = forward_case("b4h8_n4096_d64", dev, sets=C2_INPUT_SETS)
         r = path_entry(w, fn, nbytes, stream, args, w.B * w.N,
@@ -639,22 +668,29 @@ def single_path(name, args, dev, stream, headline_inputs=None, cpu=False):
     else:
         raise ValueError(name)
     del fn
-    if cpu and cpu_in is not None:
+    if not (cpu and cpu_in is not None):
+        return r, None
+
+    def job():
+        log(f"[bench] timing the oracle on a sample of {r['workload']}")
         r["cpu_oracle"] = cpu_oracle_path(cpu_kind, w, cpu_in)
         r["gpu_over_oracle"] = round(r["Mtokens_per_s"] / r["cpu_oracle"]["value"], 1)
-    return r
+    return r, job
 
 
 def other_paths(args, dev, stream, headline_inputs):
-    out = {}
+    """Every other path's entry, and the oracle timings still to be run for them."""
+    out, jobs = {}, []
     cpu = not args.no_cpu_baseline
     for key, name in (("b4h8_n4096_d64", "c2"), ("gated", "gated"), ("decode", "decode"),
                       ("decode_bf16_state", "decode_bf16_state"), ("noncausal", "noncausal"),
                       ("snapshots", "snapshots"), ("backward", "backward"), ("delta", "delta")):
         log(f"[bench] {key}")
-        out[key] = single_path(name, args, dev, stream, headline_inputs, cpu=cpu)
+        out[key], job = single_path(name, args, dev, stream, headline_inputs, cpu=cpu)
+        if job:
+            jobs.append(job)
         torch.cuda.empty_cache()
-    return out
+    return out, jobs
 
 
 if __name__ == "__main__":
