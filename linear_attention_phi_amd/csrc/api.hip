@@ -691,9 +691,16 @@ int linattn_forward_delta(const void *q, const void *k, const void *v, const flo
         return launch("delta_bf16", st, [&] {
             with_phi(phi, [&](auto PH) {
                 auto go = [&](auto BT, auto GT) {
-                    delta8_bf16<DK, DV, PH(), BT(), GT()><<<dim3((unsigned)BH), dim3(kThreads8), 0, st>>>(
-                        (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, alpha, beta, (uint16_t *)o,
-                        s_init, s_final, N);
+                    // Dv = 128: one wave per 16 value columns, each carrying its
+                    // columns through the chunk in its own registers
+                    if constexpr (DV == 128)
+                        delta8c_bf16<DK, PH(), BT(), GT()><<<dim3((unsigned)BH), dim3(kThreads8), 0, st>>>(
+                            (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, alpha, beta,
+                            (uint16_t *)o, s_init, s_final, N);
+                    else
+                        delta8_bf16<DK, DV, PH(), BT(), GT()><<<dim3((unsigned)BH), dim3(kThreads8), 0, st>>>(
+                            (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, alpha, beta,
+                            (uint16_t *)o, s_init, s_final, N);
                 };
                 using T = std::true_type;
                 using F = std::false_type;

@@ -76,6 +76,7 @@ __device__ __forceinline__ bf16x8 bf16_ones8() { return as_bf16x8(make_uint4(0x3
 // Streaming (non-temporal) 16-byte global load: every input row is read once,
 // so it should not displace cache lines that are reused.
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint4 load_stream16(const void *p) {
     return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p)));
 }
@@ -115,6 +116,9 @@ __device__ __forceinline__ float buffer_load_f32(rsrc_t rs, int voff) {
 // need not wait for the stores too.
 __device__ __forceinline__ void buffer_store16(uint4 v, rsrc_t rs, int voff) {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, voff, 0, 0);
+}
+__device__ __forceinline__ void buffer_store8(uint2 v, rsrc_t rs, int voff) {
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), rs, voff, 0, 0);
 }
 __device__ __forceinline__ void buffer_store_f32(float v, rsrc_t rs, int voff) {
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rs, voff, 0, 0);

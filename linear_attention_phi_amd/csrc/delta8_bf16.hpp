@@ -491,4 +491,417 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8_bf16(
     if (s_final) state8_store<DK, DV>(st, s_final + bh * DK * DV, w, tid & 63);
 }
 
+// The same chunked delta rule at Dv = 128 with the value columns owned by the
+// waves: wave w keeps S[:, 16 w .. 16 w + 15] in its own registers (lane
+// (g, l16) holds S[16 t + 4 g + i][16 w + l16], i = 0..3, for every key-dim
+// tile t) and carries its columns through the chunk -- the right-hand side,
+// the blocked solve, the outputs and the state update -- with operands taken
+// from its registers.  The waves share only the staged tiles, the coupling
+// blocks with their inverses, and the masked scores (as bf16 high and low
+// parts), so each chunk has three barriers (staged, shared parts formed,
+// tiles free) and no LDS round trip of S, of the right-hand side or of D.
+//
+// Operand layouts.  A 16 x 16 x 32 product takes its 32 k values per lane
+// group g in two halves: keys (or key components) 32 s + 4 g .. + 3 and
+// 32 s + 16 + 4 g .. + 3.  With that order an accumulator fragment (lane
+// (g, l16): rows 4 g + i of a 16-row tile, column l16) of two consecutive
+// tiles is at once an A operand (rows = its columns) and a B operand
+// (columns = its columns) over those 32 values: S_0 serves as the B operand
+// of Kh S_0 and the A operand of S_0^T phi(Q)^T, D as the B operand of the
+// state update Kh^T D and the A operand of D^T P^T, all straight from the
+// registers that hold them.
+template <int DK, int PHI, bool BETA, bool GATED>
+__global__ __launch_bounds__(kThreads8, 1) void delta8c_bf16(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    const float *__restrict__ alpha, const float *__restrict__ beta, uint16_t *__restrict__ o,
+    const float *__restrict__ s_init, float *__restrict__ s_final, int N) {
+    constexpr int DV = 128;
+    using TK = Tile<DK>;
+    using TV = Tile<DV>;
+    constexpr int KSK = DK / 32; // 32-component steps over the key dims
+    constexpr int NT = DK / 16;  // key-dim tiles of the state
+    constexpr int AS = kChunk + 4;
+    __shared__ __attribute__((aligned(16))) uint16_t sQ[kChunk * TK::RS]; // phi(Q)
+    __shared__ __attribute__((aligned(16))) uint16_t sK[kChunk * TK::RS]; // unit keys
+    __shared__ __attribute__((aligned(16))) uint16_t sV[kChunk * TV::RS];
+    // diag(beta) tril(Kh Kh^T, -1): the diagonal blocks in fp32; below them the
+    // negated blocks as bf16 high and low parts, 4 + 4 per 16-byte group
+    __shared__ __attribute__((aligned(16))) float sA[kChunk * AS];
+    __shared__ __attribute__((aligned(16))) float sB[kChunk]; // beta (0 past the end)
+    __shared__ __attribute__((aligned(16))) uint16_t sTh[4 * 16 * 16];
+    __shared__ __attribute__((aligned(16))) uint16_t sTl[4 * 16 * 16];
+    // the masked scores P[query][key] of tile (qb, kb <= qb), number
+    // qb (qb + 1) / 2 + kb, as lane (g, l16) of its product holds them: keys
+    // 16 kb + 4 g .. + 3 of query 16 qb + l16, high parts then low parts
+    __shared__ __attribute__((aligned(16))) uint4 sP[10 * 64];
+    __shared__ __attribute__((aligned(16))) float sGl[GATED ? kChunk : 4];
+    __shared__ __attribute__((aligned(16))) int sGz[GATED ? kChunk : 4];
+
+    const size_t bh = blockIdx.x;
+    const int tid = threadIdx.x, w = wave_id();
+    const int nch = (N + kChunk - 1) / kChunk;
+    const size_t row0 = bh * N;
+
+    // this wave's columns of the state
+    f32x4 st[NT];
+    {
+        const int lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+        const float *s0 = s_init ? s_init + bh * DK * DV : nullptr;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) st[t][i] = s0 ? s0[(16 * t + 4 * g + i) * DV + 16 * w + l16] : 0.f;
+        }
+    }
+
+    struct Buf {
+        Units<DK> q, k;
+        Units<DV> v;
+        float beta, alpha;
+    };
+    auto rows_in = [&](int c) { return max(0, min(kChunk, N - c * kChunk)); };
+    auto issue = [&](Buf &b, int c) {
+        const size_t r = row0 + (size_t)c * kChunk;
+        const int nv = rows_in(c);
+        b.q.load(q + r * DK, nv, tid);
+        b.k.load(k + r * DK, nv, tid);
+        b.v.load(v + r * DV, nv, tid);
+        b.beta = BETA ? buffer_load_f32(chunk_rsrc(beta + r, nv * 4), tid * 4) : (tid < nv ? 1.f : 0.f);
+        b.alpha = GATED ? buffer_load_f32(chunk_rsrc(alpha + r, nv * 4), tid * 4) : 1.f;
+    };
+    Buf buf;
+    // ---- stage chunk c (phi(Q), unit keys, V, beta, the gate prefix), then
+    // refill the buffer with chunk c + 1
+    auto stage = [&](int c) {
+        const int valid = rows_in(c);
+        constexpr int CG = Units<DK>::CG;
+#pragma unroll
+        for (int i = 0; i < Units<DK>::N; ++i) {
+            const int row = Units<DK>::row_of(tid, i), col = Units<DK>::col_of(tid, i);
+            *reinterpret_cast<uint4 *>(sQ + TK::off(row, col)) = phi_pack8(buf.q.r[i], PHI);
+            const uint32_t kw[4] = {buf.k.r[i].x, buf.k.r[i].y, buf.k.r[i].z, buf.k.r[i].w};
+            float f[8], nrm = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                f[2 * e] = phi_fast(bf_lo(kw[e]), PHI);
+                f[2 * e + 1] = phi_fast(bf_hi(kw[e]), PHI);
+                nrm = fmaf(f[2 * e], f[2 * e], fmaf(f[2 * e + 1], f[2 * e + 1], nrm));
+            }
+            if constexpr (CG == 16) {
+                nrm = row16_sum(nrm);
+            } else {
+#pragma unroll
+                for (int m = 1; m < CG; m <<= 1) nrm += __shfl_xor(nrm, m, 64);
+            }
+            const float inv = (row < valid && nrm > 0.f) ? __builtin_amdgcn_rsqf(nrm) : 0.f;
+            *reinterpret_cast<uint4 *>(sK + TK::off(row, col)) =
+                make_uint4(pack_bf16x2(f[0] * inv, f[1] * inv), pack_bf16x2(f[2] * inv, f[3] * inv),
+                           pack_bf16x2(f[4] * inv, f[5] * inv), pack_bf16x2(f[6] * inv, f[7] * inv));
+        }
+#pragma unroll
+        for (int i = 0; i < Units<DV>::N; ++i)
+            *reinterpret_cast<uint4 *>(sV + TV::off(Units<DV>::row_of(tid, i), Units<DV>::col_of(tid, i))) =
+                buf.v.r[i];
+        if (tid < kChunk) {
+            sB[tid] = buf.beta;
+            if (GATED) {
+                ChunkGates cg;
+                cg.build(buf.alpha, tid < valid);
+                sGl[tid] = cg.lsum;
+                sGz[tid] = cg.zeros;
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        issue(buf, c + 1);
+    };
+    issue(buf, 0);
+    if (nch > 0) stage(0);
+    for (int c = 0; c < nch; ++c) {
+        const int valid = rows_in(c);
+        const rsrc_t ro = chunk_rsrc(o + (row0 + (size_t)c * kChunk) * DV, valid * DV * 2);
+        __syncthreads();
+        const int lane = lane_in_loop(tid & 63);
+        const int l16 = lane & 15, g = lane >> 4, qd = lane & 3;
+        auto dec = [&](int t, int j) { return decay_between(sGl[t], sGz[t], sGl[j], sGz[j]); };
+        auto gam = [&](int t) { return decay_between(sGl[t], sGz[t], 0.f, 0); };
+
+        // ---- shared parts: coupling blocks (waves 0..3 a diagonal block each,
+        // inverted at once; waves 4..7 the six below the diagonal) and the ten
+        // score tiles (waves 4..7)
+        {
+            auto krow = [&](int blk, bf16x8(&kr)[KSK]) {
+#pragma unroll
+                for (int ks = 0; ks < KSK; ++ks)
+                    kr[ks] = *reinterpret_cast<const bf16x8 *>(sK + TK::off(16 * blk + l16, 32 * ks + 8 * g));
+            };
+            auto gram = [&](int rb, int cb, const bf16x8(&kr)[KSK]) {
+                const int tr = 16 * rb + l16;
+                f32x4 gr = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KSK; ++ks)
+                    gr = mfma16x16x32(*reinterpret_cast<const bf16x8 *>(sK + TK::off(16 * cb + l16, 32 * ks + 8 * g)),
+                                      kr[ks], gr);
+                const float b = sB[tr];
+                if (GATED) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int j = 16 * cb + 4 * g + i;
+                        gr[i] *= j < tr ? dec(tr, j) : 0.f;
+                    }
+                }
+                float4 a4;
+                a4.x = 16 * cb + 4 * g + 0 < tr ? b * gr[0] : 0.f;
+                a4.y = 16 * cb + 4 * g + 1 < tr ? b * gr[1] : 0.f;
+                a4.z = 16 * cb + 4 * g + 2 < tr ? b * gr[2] : 0.f;
+                a4.w = 16 * cb + 4 * g + 3 < tr ? b * gr[3] : 0.f;
+                if (cb == rb) {
+                    *reinterpret_cast<float4 *>(sA + tr * AS + 16 * cb + 4 * g) = a4;
+                } else {
+                    s16x4 hi, lo;
+                    split_bf16x4(-a4.x, -a4.y, -a4.z, -a4.w, hi, lo);
+                    const uint2 h2 = __builtin_bit_cast(uint2, hi), l2 = __builtin_bit_cast(uint2, lo);
+                    *reinterpret_cast<uint4 *>(sA + tr * AS + 16 * cb + 4 * g) = make_uint4(h2.x, h2.y, l2.x, l2.y);
+                }
+            };
+            // score tile (qb, kb): P^T[key][query] = Kh . phi(q), masked above
+            // the diagonal, decayed between the two tokens when gated
+            auto score = [&](int qb, int kb) {
+                f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KSK; ++ks)
+                    sc = mfma16x16x32(*reinterpret_cast<const bf16x8 *>(sK + TK::off(16 * kb + l16, 32 * ks + 8 * g)),
+                                      *reinterpret_cast<const bf16x8 *>(sQ + TK::off(16 * qb + l16, 32 * ks + 8 * g)),
+                                      sc);
+                const int tq = 16 * qb + l16;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int tk = 16 * kb + 4 * g + i;
+                    float x = sc[i];
+                    if (GATED) x *= dec(tq, tk);
+                    if (kb == qb && tk > tq) x = 0.f;
+                    sc[i] = x;
+                }
+                s16x4 hi, lo;
+                split_bf16x4(sc[0], sc[1], sc[2], sc[3], hi, lo);
+                const uint2 h2 = __builtin_bit_cast(uint2, hi), l2 = __builtin_bit_cast(uint2, lo);
+                sP[(qb * (qb + 1) / 2 + kb) * 64 + lane] = make_uint4(h2.x, h2.y, l2.x, l2.y);
+            };
+            if (w < 4) {
+                const int b = w;
+                bf16x8 kd[KSK];
+                krow(b, kd);
+                gram(b, b, kd);
+                // I + A_bb inverted in the wave by forward substitution on unit
+                // vectors (lane = column; all four lane groups alike, group g
+                // then writes rows 4 g .. 4 g + 3)
+                const float *ab = sA + 16 * b * AS + 16 * b;
+                const int cc = l16;
+                float t[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float x[4] = {r == cc ? 1.f : 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int j4 = 0; j4 < r; j4 += 4) {
+                        const float4 a = *reinterpret_cast<const float4 *>(ab + r * AS + j4);
+                        const float av[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (j4 + e < r) x[e] = fmaf(-av[e], t[j4 + e], x[e]);
+                    }
+                    t[r] = (x[0] + x[1]) + (x[2] + x[3]);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 4 * g + i;
+                    float tr = t[0];
+#pragma unroll
+                    for (int rr = 1; rr < 16; ++rr) tr = r == rr ? t[rr] : tr;
+                    split_bf16x1(tr, sTh[(16 * b + r) * 16 + cc], sTl[(16 * b + r) * 16 + cc]);
+                }
+            } else if (w == 4) {
+                bf16x8 k3[KSK];
+                krow(3, k3);
+                gram(3, 0, k3);
+                gram(3, 1, k3);
+                score(0, 0);
+                score(1, 1);
+            } else if (w == 5) {
+                bf16x8 k3[KSK];
+                krow(3, k3);
+                gram(3, 2, k3);
+                score(1, 0);
+                score(2, 0);
+                score(2, 1);
+            } else if (w == 6) {
+                bf16x8 k2[KSK];
+                krow(2, k2);
+                gram(2, 0, k2);
+                score(2, 2);
+                score(3, 0);
+                score(3, 1);
+            } else {
+                bf16x8 k2[KSK], k1[KSK];
+                krow(2, k2);
+                gram(2, 1, k2);
+                krow(1, k1);
+                gram(1, 0, k1);
+                score(3, 2);
+                score(3, 3);
+            }
+        }
+
+        // ---- this wave's columns before the solve: the right-hand side
+        // X = diag(beta)(V - Kh S_0) and the outputs' part O^T = S_0^T phi(Q)^T
+        // (S_0 in bf16, as one operand fragment per 32 key components)
+        f32x4 x[4], oacc[4];
+        {
+            bf16x8 sb[KSK];
+#pragma unroll
+            for (int s = 0; s < KSK; ++s)
+                sb[s] = as_bf16x8(make_uint4(pack_bf16x2(st[2 * s][0], st[2 * s][1]),
+                                             pack_bf16x2(st[2 * s][2], st[2 * s][3]),
+                                             pack_bf16x2(st[2 * s + 1][0], st[2 * s + 1][1]),
+                                             pack_bf16x2(st[2 * s + 1][2], st[2 * s + 1][3])));
+            // a row of a row-major tile in the split k order: components
+            // 32 s + 4 g .. + 3, then 32 s + 16 + 4 g .. + 3
+            auto split_row = [&](const uint16_t *tile, int row, int s) {
+                const uint2 a = *reinterpret_cast<const uint2 *>(tile + TK::off(row, 32 * s + 4 * g));
+                const uint2 b = *reinterpret_cast<const uint2 *>(tile + TK::off(row, 32 * s + 16 + 4 * g));
+                return as_bf16x8(make_uint4(a.x, a.y, b.x, b.y));
+            };
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                f32x4 r = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < KSK; ++s) r = mfma16x16x32(split_row(sK, 16 * b + l16, s), sb[s], r);
+                x[b] = r;
+            }
+#pragma unroll
+            for (int b2 = 0; b2 < 2; ++b2) {
+                // V[16 b + 4 g + i][16 w + l16] for blocks b = 2 b2, 2 b2 + 1
+                const bf16x8 vv = tr_operand<DV>(sV, 32 * b2 + 4 * g, 32 * b2 + 16 + 4 * g, 16 * w + 4 * qd, lane);
+                const uint4 vu = __builtin_bit_cast(uint4, vv);
+                const uint32_t vw[4] = {vu.x, vu.y, vu.z, vu.w};
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int b = 2 * b2 + h;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int tk = 16 * b + 4 * g + i;
+                        const float vi = (i & 1) ? bf_hi(vw[2 * h + (i >> 1)]) : bf_lo(vw[2 * h + (i >> 1)]);
+                        float r = x[b][i];
+                        if (GATED) r *= gam(tk);
+                        x[b][i] = sB[tk] * (vi - r);
+                    }
+                }
+            }
+#pragma unroll
+            for (int qb = 0; qb < 4; ++qb) {
+                f32x4 r = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < KSK; ++s) r = mfma16x16x32(sb[s], split_row(sQ, 16 * qb + l16, s), r);
+                if (GATED) r *= gam(16 * qb + l16);
+                oacc[qb] = r;
+            }
+        }
+        __syncthreads();
+
+        // ---- solve (I + A) D = X for this wave's columns, block by block:
+        // Y_b = X_b - sum_{kb < b} A_b,kb D_kb and D_b = (I + A_bb)^-1 Y_b, as
+        // 16 x 16 x 16 products on bf16 high and low parts
+        f32x4 dblk[4];
+        s16x4 dh4[4], dl4[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            f32x4 y = x[b], y1 = f32x4{0.f, 0.f, 0.f, 0.f}, y2 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < b; ++kb) {
+                const uint4 a = *reinterpret_cast<const uint4 *>(sA + (16 * b + l16) * AS + 16 * kb + 4 * g);
+                const s16x4 ah = __builtin_bit_cast(s16x4, make_uint2(a.x, a.y));
+                const s16x4 al = __builtin_bit_cast(s16x4, make_uint2(a.z, a.w));
+                y = mfma16x16x16(ah, dh4[kb], y);
+                y1 = mfma16x16x16(al, dh4[kb], y1);
+                y2 = mfma16x16x16(ah, dl4[kb], y2);
+            }
+            if (b > 0) y += y1 + y2;
+            const uint2 th = *reinterpret_cast<const uint2 *>(sTh + (16 * b + l16) * 16 + 4 * g);
+            const uint2 tl = *reinterpret_cast<const uint2 *>(sTl + (16 * b + l16) * 16 + 4 * g);
+            s16x4 yh, yl;
+            split_bf16x4(y[0], y[1], y[2], y[3], yh, yl);
+            const s16x4 t_h = __builtin_bit_cast(s16x4, th), t_l = __builtin_bit_cast(s16x4, tl);
+            const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
+            dblk[b] = mfma16x16x16(t_h, yh, zero) + (mfma16x16x16(t_l, yh, zero) + mfma16x16x16(t_h, yl, zero));
+            split_bf16x4(dblk[b][0], dblk[b][1], dblk[b][2], dblk[b][3], dh4[b], dl4[b]);
+        }
+
+        // ---- outputs: O^T += D^T P^T, both factors in high and low parts
+        // (three products: the new writes largely cancel the old summary)
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb) {
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                if (2 * s2 <= qb) {
+                    const uint4 p0 = sP[(qb * (qb + 1) / 2 + 2 * s2) * 64 + lane];
+                    const uint4 p1 = 2 * s2 + 1 <= qb ? sP[(qb * (qb + 1) / 2 + 2 * s2 + 1) * 64 + lane]
+                                                      : make_uint4(0u, 0u, 0u, 0u);
+                    const bf16x8 phi8 = as_bf16x8(make_uint4(p0.x, p0.y, p1.x, p1.y));
+                    const bf16x8 plo8 = as_bf16x8(make_uint4(p0.z, p0.w, p1.z, p1.w));
+                    const uint2 d0 = __builtin_bit_cast(uint2, dh4[2 * s2]), d1 = __builtin_bit_cast(uint2, dh4[2 * s2 + 1]);
+                    const uint2 e0 = __builtin_bit_cast(uint2, dl4[2 * s2]), e1 = __builtin_bit_cast(uint2, dl4[2 * s2 + 1]);
+                    const bf16x8 dhi = as_bf16x8(make_uint4(d0.x, d0.y, d1.x, d1.y));
+                    const bf16x8 dlo = as_bf16x8(make_uint4(e0.x, e0.y, e1.x, e1.y));
+                    oacc[qb] = mfma16x16x32(dhi, phi8, oacc[qb]);
+                    oacc[qb] = mfma16x16x32(dlo, phi8, oacc[qb]);
+                    oacc[qb] = mfma16x16x32(dhi, plo8, oacc[qb]);
+                }
+            }
+            // lane (g, l16): O[16 qb + l16][16 w + 4 g .. + 3]
+            const uint2 u = make_uint2(pack_bf16x2(oacc[qb][0], oacc[qb][1]), pack_bf16x2(oacc[qb][2], oacc[qb][3]));
+            buffer_store8(u, ro, ((16 * qb + l16) * DV + 16 * w + 4 * g) * 2);
+        }
+
+        // ---- S <- g_C S + Kh^T D for this wave's columns (rows of D decayed to
+        // the chunk's end when gated; rows past the end have zero keys)
+        {
+            s16x4 du[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                if (GATED) {
+                    const int tk0 = 16 * b + 4 * g;
+                    const float e0 = dblk[b][0] * dec(valid - 1, tk0), e1 = dblk[b][1] * dec(valid - 1, tk0 + 1);
+                    const float e2 = dblk[b][2] * dec(valid - 1, tk0 + 2), e3 = dblk[b][3] * dec(valid - 1, tk0 + 3);
+                    du[b] = __builtin_bit_cast(s16x4, make_uint2(pack_bf16x2(e0, e1), pack_bf16x2(e2, e3)));
+                } else {
+                    du[b] = dh4[b];
+                }
+            }
+            if (GATED) {
+                const float gc = gam(valid - 1);
+#pragma unroll
+                for (int t = 0; t < NT; ++t) st[t] *= gc;
+            }
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const uint2 d0 = __builtin_bit_cast(uint2, du[2 * s2]), d1 = __builtin_bit_cast(uint2, du[2 * s2 + 1]);
+                const bf16x8 db = as_bf16x8(make_uint4(d0.x, d0.y, d1.x, d1.y));
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+                    st[t] = mfma16x16x32(tr_operand<DK>(sK, 32 * s2 + 4 * g, 32 * s2 + 16 + 4 * g, 16 * t + 4 * qd, lane),
+                                         db, st[t]);
+            }
+        }
+        __syncthreads();
+        if (c + 1 < nch) stage(c + 1);
+    }
+    if (s_final) {
+        const int lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+        float *sf = s_final + bh * DK * DV;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sf[(16 * t + 4 * g + i) * DV + 16 * w + l16] = st[t][i];
+        }
+    }
+}
+
 } // namespace linattn
