@@ -498,8 +498,9 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8_bf16(
 // the blocked solve, the outputs and the state update -- with operands taken
 // from its registers.  The waves share only the staged tiles, the coupling
 // blocks with their inverses, and the masked scores (as bf16 high and low
-// parts), so each chunk has three barriers (staged, shared parts formed,
-// tiles free) and no LDS round trip of S, of the right-hand side or of D.
+// parts), so each chunk has two barriers (staged, shared parts formed; the
+// staged tiles are double buffered) and no LDS round trip of S, of the
+// right-hand side or of D.
 //
 // Operand layouts.  A 16 x 16 x 32 product takes its 32 k values per lane
 // group g in two halves: keys (or key components) 32 s + 4 g .. + 3 and
@@ -521,21 +522,23 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8c_bf16(
     constexpr int KSK = DK / 32; // 32-component steps over the key dims
     constexpr int NT = DK / 16;  // key-dim tiles of the state
     constexpr int AS = kChunk + 4;
-    __shared__ __attribute__((aligned(16))) uint16_t sQ[kChunk * TK::RS]; // phi(Q)
-    __shared__ __attribute__((aligned(16))) uint16_t sK[kChunk * TK::RS]; // unit keys
-    __shared__ __attribute__((aligned(16))) uint16_t sV[kChunk * TV::RS];
+    // the staged tiles in two buffers, by chunk parity: chunk c + 1 is staged
+    // while chunk c is still being read
+    __shared__ __attribute__((aligned(16))) uint16_t sQb[2][kChunk * TK::RS]; // phi(Q)
+    __shared__ __attribute__((aligned(16))) uint16_t sKb[2][kChunk * TK::RS]; // unit keys
+    __shared__ __attribute__((aligned(16))) uint16_t sVb[2][kChunk * TV::RS];
     // diag(beta) tril(Kh Kh^T, -1): the diagonal blocks in fp32; below them the
     // negated blocks as bf16 high and low parts, 4 + 4 per 16-byte group
     __shared__ __attribute__((aligned(16))) float sA[kChunk * AS];
-    __shared__ __attribute__((aligned(16))) float sB[kChunk]; // beta (0 past the end)
+    __shared__ __attribute__((aligned(16))) float sBb[2][kChunk]; // beta (0 past the end)
     __shared__ __attribute__((aligned(16))) uint16_t sTh[4 * 16 * 16];
     __shared__ __attribute__((aligned(16))) uint16_t sTl[4 * 16 * 16];
     // the masked scores P[query][key] of tile (qb, kb <= qb), number
     // qb (qb + 1) / 2 + kb, as lane (g, l16) of its product holds them: keys
     // 16 kb + 4 g .. + 3 of query 16 qb + l16, high parts then low parts
     __shared__ __attribute__((aligned(16))) uint4 sP[10 * 64];
-    __shared__ __attribute__((aligned(16))) float sGl[GATED ? kChunk : 4];
-    __shared__ __attribute__((aligned(16))) int sGz[GATED ? kChunk : 4];
+    __shared__ __attribute__((aligned(16))) float sGlb[2][GATED ? kChunk : 4];
+    __shared__ __attribute__((aligned(16))) int sGzb[2][GATED ? kChunk : 4];
 
     const size_t bh = blockIdx.x;
     const int tid = threadIdx.x, w = wave_id();
@@ -574,6 +577,9 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8c_bf16(
     // refill the buffer with chunk c + 1
     auto stage = [&](int c) {
         const int valid = rows_in(c);
+        uint16_t *sQ = sQb[c & 1], *sK = sKb[c & 1], *sV = sVb[c & 1];
+        float *sB = sBb[c & 1], *sGl = sGlb[c & 1];
+        int *sGz = sGzb[c & 1];
         constexpr int CG = Units<DK>::CG;
 #pragma unroll
         for (int i = 0; i < Units<DK>::N; ++i) {
@@ -619,7 +625,11 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8c_bf16(
     for (int c = 0; c < nch; ++c) {
         const int valid = rows_in(c);
         const rsrc_t ro = chunk_rsrc(o + (row0 + (size_t)c * kChunk) * DV, valid * DV * 2);
+        // chunk c staged; chunk c - 1 done with the coupling, inverse and score tiles
         __syncthreads();
+        const uint16_t *sQ = sQb[c & 1], *sK = sKb[c & 1], *sV = sVb[c & 1];
+        const float *sB = sBb[c & 1], *sGl = sGlb[c & 1];
+        const int *sGz = sGzb[c & 1];
         const int lane = lane_in_loop(tid & 63);
         const int l16 = lane & 15, g = lane >> 4, qd = lane & 3;
         auto dec = [&](int t, int j) { return decay_between(sGl[t], sGz[t], sGl[j], sGz[j]); };
@@ -805,6 +815,8 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8c_bf16(
             }
         }
         __syncthreads();
+        // the next chunk into the other buffers (last read by chunk c - 1)
+        if (c + 1 < nch) stage(c + 1);
 
         // ---- solve (I + A) D = X for this wave's columns, block by block:
         // Y_b = X_b - sum_{kb < b} A_b,kb D_kb and D_b = (I + A_bb)^-1 Y_b, as
@@ -890,8 +902,6 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8c_bf16(
                                          db, st[t]);
             }
         }
-        __syncthreads();
-        if (c + 1 < nch) stage(c + 1);
     }
     if (s_final) {
         const int lane = tid & 63, l16 = lane & 15, g = lane >> 4;
