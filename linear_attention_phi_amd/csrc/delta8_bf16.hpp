@@ -502,15 +502,17 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8_bf16(
 // staged tiles are double buffered) and no LDS round trip of S, of the
 // right-hand side or of D.
 //
-// Operand layouts.  A 16 x 16 x 32 product takes its 32 k values per lane
-// group g in two halves: keys (or key components) 32 s + 4 g .. + 3 and
-// 32 s + 16 + 4 g .. + 3.  With that order an accumulator fragment (lane
-// (g, l16): rows 4 g + i of a 16-row tile, column l16) of two consecutive
-// tiles is at once an A operand (rows = its columns) and a B operand
-// (columns = its columns) over those 32 values: S_0 serves as the B operand
-// of Kh S_0 and the A operand of S_0^T phi(Q)^T, D as the B operand of the
-// state update Kh^T D and the A operand of D^T P^T, all straight from the
-// registers that hold them.
+// Operand layouts.  An accumulator fragment of two consecutive 16-row tiles
+// (lane (g, l16): rows 4 g + i of each, column l16) supplies 8 k values per
+// lane group, so it is at once an A operand (rows = its columns) and a B
+// operand (columns = its columns) of a 16 x 16 x 32 product, once the other
+// operand takes its k values in the same order.  D's rows are keys, taken
+// as keys 32 s + 4 g .. + 3, then 32 s + 16 + 4 g .. + 3 (the score tiles
+// are stored in that order); the state's rows are key components, kept in an
+// order (sdk) that makes them components 32 s + 8 g .. + 7, one 16-byte read
+// of a staged row.  S_0 is thus the B operand of Kh S_0 and the A operand of
+// S_0^T phi(Q)^T, D the B operand of the state update Kh^T D and the A
+// operand of D^T P^T, all straight from the registers that hold them.
 template <int DK, int PHI, bool BETA, bool GATED>
 __global__ __launch_bounds__(kThreads8, 1) void delta8c_bf16(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
@@ -545,7 +547,11 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8c_bf16(
     const int nch = (N + kChunk - 1) / kChunk;
     const size_t row0 = bh * N;
 
-    // this wave's columns of the state
+    // this wave's columns of the state; the key components of tile t in the
+    // order that makes two consecutive tiles' fragments (t = 2 s, 2 s + 1) hold
+    // components 32 s + 8 g .. + 7 in lane group g: element i of tile t in
+    // group g is component sdk(t, g, i)
+    auto sdk = [](int t, int g, int i) { return 32 * (t >> 1) + 8 * g + 4 * (t & 1) + i; };
     f32x4 st[NT];
     {
         const int lane = tid & 63, l16 = lane & 15, g = lane >> 4;
@@ -553,7 +559,7 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8c_bf16(
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) st[t][i] = s0 ? s0[(16 * t + 4 * g + i) * DV + 16 * w + l16] : 0.f;
+            for (int i = 0; i < 4; ++i) st[t][i] = s0 ? s0[sdk(t, g, i) * DV + 16 * w + l16] : 0.f;
         }
     }
 
@@ -772,18 +778,15 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8c_bf16(
                                              pack_bf16x2(st[2 * s][2], st[2 * s][3]),
                                              pack_bf16x2(st[2 * s + 1][0], st[2 * s + 1][1]),
                                              pack_bf16x2(st[2 * s + 1][2], st[2 * s + 1][3])));
-            // a row of a row-major tile in the split k order: components
-            // 32 s + 4 g .. + 3, then 32 s + 16 + 4 g .. + 3
-            auto split_row = [&](const uint16_t *tile, int row, int s) {
-                const uint2 a = *reinterpret_cast<const uint2 *>(tile + TK::off(row, 32 * s + 4 * g));
-                const uint2 b = *reinterpret_cast<const uint2 *>(tile + TK::off(row, 32 * s + 16 + 4 * g));
-                return as_bf16x8(make_uint4(a.x, a.y, b.x, b.y));
+            // components 32 s + 8 g .. + 7 of a row (the fragment's key components)
+            auto row8 = [&](const uint16_t *tile, int row, int s) {
+                return *reinterpret_cast<const bf16x8 *>(tile + TK::off(row, 32 * s + 8 * g));
             };
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
                 f32x4 r = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int s = 0; s < KSK; ++s) r = mfma16x16x32(split_row(sK, 16 * b + l16, s), sb[s], r);
+                for (int s = 0; s < KSK; ++s) r = mfma16x16x32(row8(sK, 16 * b + l16, s), sb[s], r);
                 x[b] = r;
             }
 #pragma unroll
@@ -809,7 +812,7 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8c_bf16(
             for (int qb = 0; qb < 4; ++qb) {
                 f32x4 r = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int s = 0; s < KSK; ++s) r = mfma16x16x32(sb[s], split_row(sQ, 16 * qb + l16, s), r);
+                for (int s = 0; s < KSK; ++s) r = mfma16x16x32(sb[s], row8(sQ, 16 * qb + l16, s), r);
                 if (GATED) r *= gam(16 * qb + l16);
                 oacc[qb] = r;
             }
@@ -898,7 +901,8 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8c_bf16(
                 const bf16x8 db = as_bf16x8(make_uint4(d0.x, d0.y, d1.x, d1.y));
 #pragma unroll
                 for (int t = 0; t < NT; ++t)
-                    st[t] = mfma16x16x32(tr_operand<DK>(sK, 32 * s2 + 4 * g, 32 * s2 + 16 + 4 * g, 16 * t + 4 * qd, lane),
+                    st[t] = mfma16x16x32(tr_operand<DK>(sK, 32 * s2 + 4 * g, 32 * s2 + 16 + 4 * g,
+                                                        32 * (t >> 1) + 8 * qd + 4 * (t & 1), lane),
                                          db, st[t]);
             }
         }
@@ -909,7 +913,7 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8c_bf16(
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sf[(16 * t + 4 * g + i) * DV + 16 * w + l16] = st[t][i];
+            for (int i = 0; i < 4; ++i) sf[sdk(t, g, i) * DV + 16 * w + l16] = st[t][i];
         }
     }
 }
