@@ -798,13 +798,15 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8c_bf16(
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int b = 2 * b2 + h;
+                    const float4 bt = *reinterpret_cast<const float4 *>(sB + 16 * b + 4 * g);
+                    const float bv[4] = {bt.x, bt.y, bt.z, bt.w};
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int tk = 16 * b + 4 * g + i;
                         const float vi = (i & 1) ? bf_hi(vw[2 * h + (i >> 1)]) : bf_lo(vw[2 * h + (i >> 1)]);
                         float r = x[b][i];
                         if (GATED) r *= gam(tk);
-                        x[b][i] = sB[tk] * (vi - r);
+                        x[b][i] = bv[i] * (vi - r);
                     }
                 }
             }
