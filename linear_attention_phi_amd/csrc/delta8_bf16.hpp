@@ -16,9 +16,12 @@
 // the diagonal blocks by forward substitution in fp32 (one block per wave of
 // the light query blocks, as soon as the wave has formed it), the rest as MFMA
 // products on bf16 high/low parts; everything else is bf16 MFMA with fp32
-// accumulation, in the tile layouts and wave pairing of fwd8_bf16.hpp.  One
-// workgroup carries one (b, h) through its chunks in order; four barriers per
-// chunk (staged, coupled, solved, carried).
+// accumulation.  One workgroup carries one (b, h) through its chunks in
+// order.  Two kernels: delta8_bf16 (any Dv of 64 and 128; tile layouts and wave
+// pairing of fwd8_bf16.hpp, four barriers per chunk: staged, coupled, solved,
+// carried) and delta8c_bf16 (Dv = 128: each wave owns 16 value columns of S
+// and of every per-column quantity, two barriers per chunk), which the
+// library runs at Dv = 128.
 #pragma once
 
 #include "bwd8_bf16.hpp"
