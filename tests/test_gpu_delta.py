@@ -101,6 +101,16 @@ def test_gate_of_one_equals_ungated_on_the_gpu():
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
 
 
+@pytest.mark.parametrize("shape", [(1, 2, 300, 128, 128), (1, 1, 200, 64, 128), (1, 2, 150, 64, 64)])
+def test_delta_identity_map(shape):
+    # the identity feature map (keys normalized as they are, negative entries
+    # included) through both kernels and both gate forms
+    q, k, v, beta = make(*shape, seed=1260 + sum(shape), with_beta=True)
+    check(q, k, v, beta, phi=la.PHI_IDENTITY)
+    a = synth.gate_heads(1260 + sum(shape), *shape[:3])
+    check(q, k, v, beta, phi=la.PHI_IDENTITY, alpha=a)
+
+
 def test_worked_example_on_the_gpu():
     g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "summary_scalar_values.json")))
     D = 64
