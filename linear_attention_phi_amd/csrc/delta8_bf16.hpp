@@ -538,16 +538,21 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8c_bf16(
     __shared__ __attribute__((aligned(16))) float sBb[2][kChunk]; // beta (0 past the end)
     __shared__ __attribute__((aligned(16))) uint16_t sTh[4 * 16 * 16];
     __shared__ __attribute__((aligned(16))) uint16_t sTl[4 * 16 * 16];
-    // the masked scores P[query][key] of tile (qb, kb <= qb), number
-    // qb (qb + 1) / 2 + kb, as lane (g, l16) of its product holds them: keys
-    // 16 kb + 4 g .. + 3 of query 16 qb + l16, high parts then low parts
-    __shared__ __attribute__((aligned(16))) uint4 sP[10 * 64];
+    // the masked scores P[query][key] as bf16 high (sPh) and low (sPl) parts:
+    // per query block qb and key-block pair (2 p, 2 p + 1), p <= qb / 2, the
+    // 16 bytes of lane (g, l16) hold keys 16 (2 p) + 4 g .. + 3 then
+    // 16 (2 p + 1) + 4 g .. + 3 of query 16 qb + l16 (zeros for the key block
+    // past the diagonal): one operand of the outputs' product
+    __shared__ __attribute__((aligned(16))) uint4 sPh[6 * 64];
+    __shared__ __attribute__((aligned(16))) uint4 sPl[6 * 64];
     __shared__ __attribute__((aligned(16))) float sGlb[2][GATED ? kChunk : 4];
     __shared__ __attribute__((aligned(16))) int sGzb[2][GATED ? kChunk : 4];
 
     const size_t bh = blockIdx.x;
     const int tid = threadIdx.x, w = wave_id();
     const int nch = (N + kChunk - 1) / kChunk;
+    // first key-block pair of query block qb among the six (1, 1, 2, 2 per qb)
+    auto pair_base = [](int qb) { return qb == 3 ? 4 : qb; };
     const size_t row0 = bh * N;
 
     // this wave's columns of the state; the key components of tile t in the
@@ -702,8 +707,15 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8c_bf16(
                 }
                 s16x4 hi, lo;
                 split_bf16x4(sc[0], sc[1], sc[2], sc[3], hi, lo);
-                const uint2 h2 = __builtin_bit_cast(uint2, hi), l2 = __builtin_bit_cast(uint2, lo);
-                sP[(qb * (qb + 1) / 2 + kb) * 64 + lane] = make_uint4(h2.x, h2.y, l2.x, l2.y);
+                const int slot = (pair_base(qb) + (kb >> 1)) * 64 + lane;
+                uint2 *ph = reinterpret_cast<uint2 *>(sPh + slot) + (kb & 1);
+                uint2 *pl = reinterpret_cast<uint2 *>(sPl + slot) + (kb & 1);
+                *ph = __builtin_bit_cast(uint2, hi);
+                *pl = __builtin_bit_cast(uint2, lo);
+                if (kb == qb && !(kb & 1)) {
+                    ph[1] = make_uint2(0u, 0u);
+                    pl[1] = make_uint2(0u, 0u);
+                }
             };
             if (w < 4) {
                 const int b = w;
@@ -829,8 +841,13 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8c_bf16(
         // ---- solve (I + A) D = X for this wave's columns, block by block:
         // Y_b = X_b - sum_{kb < b} A_b,kb D_kb and D_b = (I + A_bb)^-1 Y_b, as
         // 16 x 16 x 16 products on bf16 high and low parts
+        // D's high and low parts, blocks 2 p and 2 p + 1 as the two halves of
+        // pair p (the 8 k values of a 16 x 16 x 32 operand)
         f32x4 dblk[4];
-        s16x4 dh4[4], dl4[4];
+        uint4 dH[2], dL[2];
+        auto half = [](const uint4 &u, int h) {
+            return __builtin_bit_cast(s16x4, h ? make_uint2(u.z, u.w) : make_uint2(u.x, u.y));
+        };
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             f32x4 y = x[b], y1 = f32x4{0.f, 0.f, 0.f, 0.f}, y2 = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -839,9 +856,9 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8c_bf16(
                 const uint4 a = *reinterpret_cast<const uint4 *>(sA + (16 * b + l16) * AS + 16 * kb + 4 * g);
                 const s16x4 ah = __builtin_bit_cast(s16x4, make_uint2(a.x, a.y));
                 const s16x4 al = __builtin_bit_cast(s16x4, make_uint2(a.z, a.w));
-                y = mfma16x16x16(ah, dh4[kb], y);
-                y1 = mfma16x16x16(al, dh4[kb], y1);
-                y2 = mfma16x16x16(ah, dl4[kb], y2);
+                y = mfma16x16x16(ah, half(dH[kb >> 1], kb & 1), y);
+                y1 = mfma16x16x16(al, half(dH[kb >> 1], kb & 1), y1);
+                y2 = mfma16x16x16(ah, half(dL[kb >> 1], kb & 1), y2);
             }
             if (b > 0) y += y1 + y2;
             const uint2 th = *reinterpret_cast<const uint2 *>(sTh + (16 * b + l16) * 16 + 4 * g);
@@ -851,7 +868,14 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8c_bf16(
             const s16x4 t_h = __builtin_bit_cast(s16x4, th), t_l = __builtin_bit_cast(s16x4, tl);
             const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
             dblk[b] = mfma16x16x16(t_h, yh, zero) + (mfma16x16x16(t_l, yh, zero) + mfma16x16x16(t_h, yl, zero));
-            split_bf16x4(dblk[b][0], dblk[b][1], dblk[b][2], dblk[b][3], dh4[b], dl4[b]);
+            s16x4 dh, dl;
+            split_bf16x4(dblk[b][0], dblk[b][1], dblk[b][2], dblk[b][3], dh, dl);
+            const uint2 hb = __builtin_bit_cast(uint2, dh), lb = __builtin_bit_cast(uint2, dl);
+            if (b & 1) {
+                dH[b >> 1].z = hb.x, dH[b >> 1].w = hb.y, dL[b >> 1].z = lb.x, dL[b >> 1].w = lb.y;
+            } else {
+                dH[b >> 1].x = hb.x, dH[b >> 1].y = hb.y, dL[b >> 1].x = lb.x, dL[b >> 1].y = lb.y;
+            }
         }
 
         // ---- outputs: O^T += D^T P^T, both factors in high and low parts
@@ -861,15 +885,9 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8c_bf16(
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
                 if (2 * s2 <= qb) {
-                    const uint4 p0 = sP[(qb * (qb + 1) / 2 + 2 * s2) * 64 + lane];
-                    const uint4 p1 = 2 * s2 + 1 <= qb ? sP[(qb * (qb + 1) / 2 + 2 * s2 + 1) * 64 + lane]
-                                                      : make_uint4(0u, 0u, 0u, 0u);
-                    const bf16x8 phi8 = as_bf16x8(make_uint4(p0.x, p0.y, p1.x, p1.y));
-                    const bf16x8 plo8 = as_bf16x8(make_uint4(p0.z, p0.w, p1.z, p1.w));
-                    const uint2 d0 = __builtin_bit_cast(uint2, dh4[2 * s2]), d1 = __builtin_bit_cast(uint2, dh4[2 * s2 + 1]);
-                    const uint2 e0 = __builtin_bit_cast(uint2, dl4[2 * s2]), e1 = __builtin_bit_cast(uint2, dl4[2 * s2 + 1]);
-                    const bf16x8 dhi = as_bf16x8(make_uint4(d0.x, d0.y, d1.x, d1.y));
-                    const bf16x8 dlo = as_bf16x8(make_uint4(e0.x, e0.y, e1.x, e1.y));
+                    const int slot = (pair_base(qb) + s2) * 64 + lane;
+                    const bf16x8 phi8 = as_bf16x8(sPh[slot]), plo8 = as_bf16x8(sPl[slot]);
+                    const bf16x8 dhi = as_bf16x8(dH[s2]), dlo = as_bf16x8(dL[s2]);
                     oacc[qb] = mfma16x16x32(dhi, phi8, oacc[qb]);
                     oacc[qb] = mfma16x16x32(dlo, phi8, oacc[qb]);
                     oacc[qb] = mfma16x16x32(dhi, plo8, oacc[qb]);
@@ -883,16 +901,17 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8c_bf16(
         // ---- S <- g_C S + Kh^T D for this wave's columns (rows of D decayed to
         // the chunk's end when gated; rows past the end have zero keys)
         {
-            s16x4 du[4];
+            uint4 du[2] = {dH[0], dH[1]};
+            if (GATED) {
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                if (GATED) {
+                for (int b = 0; b < 4; ++b) {
                     const int tk0 = 16 * b + 4 * g;
                     const float e0 = dblk[b][0] * dec(valid - 1, tk0), e1 = dblk[b][1] * dec(valid - 1, tk0 + 1);
                     const float e2 = dblk[b][2] * dec(valid - 1, tk0 + 2), e3 = dblk[b][3] * dec(valid - 1, tk0 + 3);
-                    du[b] = __builtin_bit_cast(s16x4, make_uint2(pack_bf16x2(e0, e1), pack_bf16x2(e2, e3)));
-                } else {
-                    du[b] = dh4[b];
+                    if (b & 1)
+                        du[b >> 1].z = pack_bf16x2(e0, e1), du[b >> 1].w = pack_bf16x2(e2, e3);
+                    else
+                        du[b >> 1].x = pack_bf16x2(e0, e1), du[b >> 1].y = pack_bf16x2(e2, e3);
                 }
             }
             if (GATED) {
@@ -902,8 +921,7 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8c_bf16(
             }
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
-                const uint2 d0 = __builtin_bit_cast(uint2, du[2 * s2]), d1 = __builtin_bit_cast(uint2, du[2 * s2 + 1]);
-                const bf16x8 db = as_bf16x8(make_uint4(d0.x, d0.y, d1.x, d1.y));
+                const bf16x8 db = as_bf16x8(du[s2]);
 #pragma unroll
                 for (int t = 0; t < NT; ++t)
                     st[t] = mfma16x16x32(tr_operand<DK>(sK, 32 * s2 + 4 * g, 32 * s2 + 16 + 4 * g,
