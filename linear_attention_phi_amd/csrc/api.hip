@@ -401,29 +401,30 @@ int run_mfma_backward(const Plan &pl, const void *q, const void *k, const void *
             sseg = (size_t)pl.R * pl.Eb;
             zbh = (size_t)pl.Ps * pl.Eb;
         }
-        // dQ and dd; for P > 1 also the reverse sums of every state sub-segment
-        // past the first segment (cell j: sub-segment R + j)
+        // dQ and dd; for P > 1 also the reverse sums of every output segment
+        // past the first (cell j: segment j + 1), the granularity the dK/dV
+        // pass starts from
         LA_TRY(launch("bwd_dq_bf16", st, [&] {
             with_phi(phi, [&](auto PH) {
                 bwd_dq8_bf16<DK, DV, PH()><<<dim3(pl.P * BH), dim3(kThreads8), 0, st>>>(
                     q16, k16, v16, den, g16, (uint16_t *)dq, dd, start, sbh, sseg, start_z, zbh, start_vb, N, pl.P,
-                    pl.seg_len, eps, rev, (size_t)pl.Ps * pl.E, pl.R, pl.sub_len / kChunk);
+                    pl.seg_len, eps, rev, (size_t)pl.Ps * pl.E, 1, pl.seg_len / kChunk);
             });
         }));
         if (pl.P > 1) {
-            const int cells = (pl.P - 1) * pl.R;
+            const int cells = pl.P - 1;
             LA_TRY(launch("seg_suffix", st, [&] {
                 seg_suffix<<<dim3((unsigned)((pl.E + 255) / 256), BH), dim3(256), 0, st>>>(rev, pl.Ps, cells,
                                                                                           (int)pl.E);
             }));
         }
         // output segment p < P - 1 starts (going backward) from the sum over
-        // cells j >= p * R; the last segment starts from zero
+        // cells j >= p; the last segment starts from zero
         return launch("bwd_dkv_bf16", st, [&] {
             with_phi(phi, [&](auto PH) {
                 bwd_dkv8_bf16<DK, DV, PH()><<<dim3(pl.P * BH), dim3(kThreads8), 0, st>>>(
                     q16, k16, v16, den, dd, g16, (uint16_t *)dk, (uint16_t *)dv, rev, (size_t)pl.Ps * pl.E,
-                    (size_t)pl.R * pl.E, N, pl.P, pl.seg_len);
+                    pl.E, N, pl.P, pl.seg_len);
             });
         });
     }

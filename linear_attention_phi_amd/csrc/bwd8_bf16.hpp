@@ -18,8 +18,8 @@
 // (tril / triu over (query, key) with the diagonal included).  Passes: the
 // state pass gives the forward state at segment starts (or the training
 // forward's saved cells serve); bwd_dq8_bf16 runs each segment forward in
-// time, writes dd, and sums R and r over each state sub-segment from the
-// phi(Q), dY and dd it has staged (for a suffix over segments);
+// time, writes dd, and sums R and r over the segment from the phi(Q), dY and
+// dd it has staged (for a suffix over segments);
 // bwd_dkv8_bf16 runs each segment backward in time.  dY is dO over the
 // forward's saved denominator, rounded to bf16 once; every pass uses that
 // same dY.
@@ -274,8 +274,9 @@ __device__ __forceinline__ void state8_update_vcol(State8<DK, DV> &st, const uin
 // and start_vb may be null for zero); for the identity map E, zeta are S, z.
 // The training forward keeps its cells in this same form, so they serve as
 // they are.  Writes dq and dd_out (dd of every token, for the dK, dV pass).
-// With rev given, a segment p > 0 also sums, over each of its R state
-// sub-segments j (sub_chunks chunks each), dR = phi(Q)^T dY and dr = phi(Q)^T dd
+// With rev given, a segment p > 0 also sums, over each of R parts j of it
+// (sub_chunks chunks each; the library takes the whole segment as one part,
+// the granularity the dK, dV pass starts from), dR = phi(Q)^T dY and dr = phi(Q)^T dd
 // from the phi(Q), dY and dd it has just staged, into the reverse cell
 // (p - 1) R + j at rev + bh rev_stride_bh (cells of Dk Dv + Dk floats, in the
 // layout of the forward's segment states); the first segment's are never needed.
