@@ -111,6 +111,25 @@ def test_delta_identity_map(shape):
     check(q, k, v, beta, phi=la.PHI_IDENTITY, alpha=a)
 
 
+@pytest.mark.parametrize("shape", [(1, 2, 300, 128, 128), (2, 1, 200, 128, 64)])
+def test_delta_final_state_in_place(shape):
+    # through the C ABI with s_final at s_init's address (the header allows it):
+    # the same outputs and state as with separate buffers, both kernels
+    q, k, v, beta = make(*shape, seed=1270 + sum(shape), with_beta=True)
+    B, H, N, Dk, Dv = shape
+    d = [x.to(DEV) for x in (q, k, v, beta)]
+    s0 = (torch.randn(B, H, Dk, Dv, generator=torch.Generator().manual_seed(11)) * 0.1).to(DEV)
+    o1, s1 = la.linattn_forward_delta(d[0], d[1], d[2], d[3], s0.clone())
+    s = s0.clone()
+    o2 = torch.empty_like(o1)
+    rc = la.lib().linattn_forward_delta(la._ptr(d[0]), la._ptr(d[1]), la._ptr(d[2]), None, la._ptr(d[3]),
+                                        la._ptr(o2), la._ptr(s), la._ptr(s), B, H, N, Dk, Dv, la.BF16,
+                                        la.PHI_ELU1, la._stream(d[0]))
+    assert rc == 0
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s)
+
+
 def test_worked_example_on_the_gpu():
     g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "summary_scalar_values.json")))
     D = 64
