@@ -321,8 +321,8 @@ def decode_prefix_gpu(w, b, dev):
 
 # ------------------------------------------------------------------ CPU baseline
 def host_cores():
-    """Threads the oracle may use here: OMP_NUM_THREADS if set (the GPU machine sets it to its per-GPU CPU
-    share), else the CPUs this process is allowed to run on."""
+    """Threads the oracle may use here: OMP_NUM_THREADS if set (a shared host may set it to the CPU share
+    of one GPU), else the CPUs this process is allowed to run on."""
     try:
         allowed = len(os.sched_getaffinity(0))
     except (AttributeError, OSError):
