@@ -496,14 +496,14 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8_bf16(
 
 // The same chunked delta rule at Dv = 128 with the value columns owned by the
 // waves: wave w keeps S[:, 16 w .. 16 w + 15] in its own registers (lane
-// (g, l16) holds S[16 t + 4 g + i][16 w + l16], i = 0..3, for every key-dim
-// tile t) and carries its columns through the chunk -- the right-hand side,
-// the blocked solve, the outputs and the state update -- with operands taken
-// from its registers.  The waves share only the staged tiles, the coupling
-// blocks with their inverses, and the masked scores (as bf16 high and low
-// parts), so each chunk has two barriers (staged, shared parts formed; the
-// staged tiles are double buffered) and no LDS round trip of S, of the
-// right-hand side or of D.
+// (g, l16) holds four key components of column 16 w + l16 for every key-dim
+// tile t, in the order sdk below) and carries its columns through the chunk --
+// the right-hand side, the blocked solve, the outputs and the state update --
+// with operands taken from its registers.  The waves share only the staged
+// tiles, the coupling blocks with their inverses, and the masked scores (as
+// bf16 high and low parts), so each chunk has two barriers (staged, shared
+// parts formed; the staged tiles are double buffered) and no LDS round trip of
+// S, of the right-hand side or of D.
 //
 // Operand layouts.  An accumulator fragment of two consecutive 16-row tiles
 // (lane (g, l16): rows 4 g + i of each, column l16) supplies 8 k values per
