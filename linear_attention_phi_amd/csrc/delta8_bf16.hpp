@@ -536,6 +536,8 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8c_bf16(
     // negated blocks as bf16 high and low parts, 4 + 4 per 16-byte group
     __shared__ __attribute__((aligned(16))) float sA[kChunk * AS];
     __shared__ __attribute__((aligned(16))) float sBb[2][kChunk]; // beta (0 past the end)
+    // inverses of A's diagonal blocks, bf16 high and low parts, each block
+    // column-major ([column][row]: a lane writes its column in 16-byte stores)
     __shared__ __attribute__((aligned(16))) uint16_t sTh[4 * 16 * 16];
     __shared__ __attribute__((aligned(16))) uint16_t sTl[4 * 16 * 16];
     // the masked scores P[query][key] as bf16 high (sPh) and low (sPl) parts:
@@ -649,9 +651,10 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8c_bf16(
         auto dec = [&](int t, int j) { return decay_between(sGl[t], sGz[t], sGl[j], sGz[j]); };
         auto gam = [&](int t) { return decay_between(sGl[t], sGz[t], 0.f, 0); };
 
-        // ---- shared parts: coupling blocks (waves 0..3 a diagonal block each,
-        // inverted at once; waves 4..7 the six below the diagonal) and the ten
-        // score tiles (waves 4..7)
+        // ---- shared parts: the coupling blocks and the inverses of the diagonal
+        // ones (wave 0: the four diagonal blocks, then lane group g inverts
+        // block g), the six blocks below the diagonal and the ten score tiles
+        // (waves 1..7, fewest on wave 4, which shares wave 0's SIMD)
         {
             auto krow = [&](int blk, bf16x8(&kr)[KSK]) {
 #pragma unroll
@@ -717,19 +720,22 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8c_bf16(
                     pl[1] = make_uint2(0u, 0u);
                 }
             };
-            if (w < 4) {
-                const int b = w;
-                bf16x8 kd[KSK];
-                krow(b, kd);
-                gram(b, b, kd);
-                // I + A_bb inverted in the wave by forward substitution on unit
-                // vectors (lane = column; all four lane groups alike, group g
-                // then writes rows 4 g .. 4 g + 3)
+            if (w == 0) {
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    bf16x8 kd[KSK];
+                    krow(b, kd);
+                    gram(b, b, kd);
+                }
+                // I + A_bb inverted by forward substitution on unit vectors:
+                // lane group g takes block g, lane l16 its column l16 (this
+                // wave wrote the four blocks; its LDS accesses stay in order)
+                const int b = g, cc = l16;
                 const float *ab = sA + 16 * b * AS + 16 * b;
-                const int cc = l16;
                 float t[16];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
+                    // four partial sums: a short dependency chain per row
                     float x[4] = {r == cc ? 1.f : 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int j4 = 0; j4 < r; j4 += 4) {
@@ -741,43 +747,53 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8c_bf16(
                     }
                     t[r] = (x[0] + x[1]) + (x[2] + x[3]);
                 }
+                uint32_t h[8], lo[8];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 4 * g + i;
-                    float tr = t[0];
-#pragma unroll
-                    for (int rr = 1; rr < 16; ++rr) tr = r == rr ? t[rr] : tr;
-                    split_bf16x1(tr, sTh[(16 * b + r) * 16 + cc], sTl[(16 * b + r) * 16 + cc]);
+                for (int e = 0; e < 8; ++e) {
+                    h[e] = pack_bf16x2(t[2 * e], t[2 * e + 1]);
+                    lo[e] = pack_bf16x2(t[2 * e] - bf_lo(h[e]), t[2 * e + 1] - bf_hi(h[e]));
                 }
-            } else if (w == 4) {
-                bf16x8 k3[KSK];
-                krow(3, k3);
-                gram(3, 0, k3);
-                gram(3, 1, k3);
+                uint4 *th = reinterpret_cast<uint4 *>(sTh + (16 * b + cc) * 16);
+                uint4 *tl = reinterpret_cast<uint4 *>(sTl + (16 * b + cc) * 16);
+                th[0] = make_uint4(h[0], h[1], h[2], h[3]);
+                th[1] = make_uint4(h[4], h[5], h[6], h[7]);
+                tl[0] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+                tl[1] = make_uint4(lo[4], lo[5], lo[6], lo[7]);
+            } else if (w == 1) {
+                bf16x8 kr[KSK];
+                krow(1, kr);
+                gram(1, 0, kr);
                 score(0, 0);
                 score(1, 1);
-            } else if (w == 5) {
-                bf16x8 k3[KSK];
-                krow(3, k3);
-                gram(3, 2, k3);
+            } else if (w == 2) {
+                bf16x8 kr[KSK];
+                krow(2, kr);
+                gram(2, 0, kr);
                 score(1, 0);
-                score(2, 0);
-                score(2, 1);
-            } else if (w == 6) {
-                bf16x8 k2[KSK];
-                krow(2, k2);
-                gram(2, 0, k2);
                 score(2, 2);
+            } else if (w == 3) {
+                bf16x8 kr[KSK];
+                krow(2, kr);
+                gram(2, 1, kr);
+                score(2, 0);
+                score(3, 3);
+            } else if (w == 4) {
+                bf16x8 kr[KSK];
+                krow(3, kr);
+                gram(3, 0, kr);
+            } else if (w == 5) {
+                bf16x8 kr[KSK];
+                krow(3, kr);
+                gram(3, 1, kr);
+                score(2, 1);
                 score(3, 0);
+            } else if (w == 6) {
+                bf16x8 kr[KSK];
+                krow(3, kr);
+                gram(3, 2, kr);
                 score(3, 1);
             } else {
-                bf16x8 k2[KSK], k1[KSK];
-                krow(2, k2);
-                gram(2, 1, k2);
-                krow(1, k1);
-                gram(1, 0, k1);
                 score(3, 2);
-                score(3, 3);
             }
         }
 
@@ -861,8 +877,10 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8c_bf16(
                 y2 = mfma16x16x16(ah, half(dL[kb >> 1], kb & 1), y2);
             }
             if (b > 0) y += y1 + y2;
-            const uint2 th = *reinterpret_cast<const uint2 *>(sTh + (16 * b + l16) * 16 + 4 * g);
-            const uint2 tl = *reinterpret_cast<const uint2 *>(sTl + (16 * b + l16) * 16 + 4 * g);
+            // T[16 b + l16][4 g .. + 3] from the column-major block (a
+            // transposing read: lane i of a group receives column 4 g + j of row i)
+            const int toff = (16 * b + 4 * g + ((lane & 15) >> 2)) * 16 + 4 * qd;
+            const uint2 th = lds_tr16(sTh + toff), tl = lds_tr16(sTl + toff);
             s16x4 yh, yl;
             split_bf16x4(y[0], y[1], y[2], y[3], yh, yl);
             const s16x4 t_h = __builtin_bit_cast(s16x4, th), t_l = __builtin_bit_cast(s16x4, tl);
