@@ -850,9 +850,11 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8c_bf16(
                 oacc[qb] = r;
             }
         }
-        __syncthreads();
-        // the next chunk into the other buffers (last read by chunk c - 1)
+        // the next chunk into the other buffers (last read by chunk c - 1), before
+        // the barrier: the waves that wait there for wave 0's block inverses
+        // stage meanwhile
         if (c + 1 < nch) stage(c + 1);
+        __syncthreads();
 
         // ---- solve (I + A) D = X for this wave's columns, block by block:
         // Y_b = X_b - sum_{kb < b} A_b,kb D_kb and D_b = (I + A_bb)^-1 Y_b, as
