@@ -733,19 +733,34 @@ __global__ __launch_bounds__(kThreads8, 1) void delta8c_bf16(
                 const int b = g, cc = l16;
                 const float *ab = sA + 16 * b * AS + 16 * b;
                 float t[16];
+                // four rows at a time: their reads all issued before the
+                // substitution steps that use them (so that a step waits for
+                // at most one batch of reads, not for each read in turn)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    // four partial sums: a short dependency chain per row
-                    float x[4] = {r == cc ? 1.f : 0.f, 0.f, 0.f, 0.f};
+                for (int r0 = 0; r0 < 16; r0 += 4) {
+                    float4 arow[4][4];
 #pragma unroll
-                    for (int j4 = 0; j4 < r; j4 += 4) {
-                        const float4 a = *reinterpret_cast<const float4 *>(ab + r * AS + j4);
-                        const float av[4] = {a.x, a.y, a.z, a.w};
+                    for (int rr = 0; rr < 4; ++rr) {
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (j4 + e < r) x[e] = fmaf(-av[e], t[j4 + e], x[e]);
+                        for (int j4 = 0; j4 < 4; ++j4)
+                            if (4 * j4 < r0 + rr)
+                                arow[rr][j4] = *reinterpret_cast<const float4 *>(ab + (r0 + rr) * AS + 4 * j4);
                     }
-                    t[r] = (x[0] + x[1]) + (x[2] + x[3]);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) {
+                        const int r = r0 + rr;
+                        // four partial sums: a short dependency chain per row
+                        float x[4] = {r == cc ? 1.f : 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int j4 = 0; 4 * j4 < r; ++j4) {
+                            const float av[4] = {arow[rr][j4].x, arow[rr][j4].y, arow[rr][j4].z, arow[rr][j4].w};
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                if (4 * j4 + e < r) x[e] = fmaf(-av[e], t[4 * j4 + e], x[e]);
+                        }
+                        t[r] = (x[0] + x[1]) + (x[2] + x[3]);
+                    }
                 }
                 uint32_t h[8], lo[8];
 #pragma unroll
