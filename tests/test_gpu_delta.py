@@ -62,6 +62,16 @@ def test_delta_full_length():
     check(*synth.qkv(x))
 
 
+def test_gated_delta_full_length():
+    # the workload's length (64 chunks) with gates a = sigmoid(N(4, 1)), beta and
+    # an initial state: the gated chain over every chunk
+    w = synth.WORKLOADS["delta_b16h16_n4096_d128"]
+    q, k, v, beta = make(1, 2, w.N, w.Dk, w.Dv, seed=w.seed + 1, with_beta=True)
+    a = synth.gate_heads(1280, 1, 2, w.N)
+    s0 = torch.randn(1, 2, w.Dk, w.Dv, generator=torch.Generator().manual_seed(14)) * 0.1
+    check(q, k, v, beta, s0, alpha=a)
+
+
 @pytest.mark.parametrize("shape", [(1, 2, 700, 128, 128), (2, 1, 130, 64, 64), (1, 2, 333, 128, 64),
                                    (1, 1, 64, 64, 128)])
 def test_delta_with_beta(shape):
